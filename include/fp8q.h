@@ -1,0 +1,165 @@
+/*
+ * fp8q.h -- C ABI of the MI355X (gfx950) FP8 delayed-scaling library libfp8q.so.
+ *
+ * The library implements the memory-bound hot path of FP8 training with delayed
+ * scaling:
+ *   - quantize: each element of a wide (bf16 or fp32) tensor is divided by the
+ *     scale of the previous step, saturated to the FP8 range and cast to E4M3 or
+ *     E5M2, while max|x| of the same tensor is reduced in the same pass
+ *     ("Fusion of Fp8 quantization and amax reduction kernels", openxla/xla issue
+ *     7432: the quantize and the amax passes read the same tensor and are fused);
+ *   - the amax-history scale update for many tensors in one launch ("Implement
+ *     fused kernel for FP8 scale update", TransformerEngine PR 593: roll the amax
+ *     history in place, take the amax from it, compute the new scale);
+ *   - dequantize (FP8 code times scale).
+ * The formulas are those of "User Guide on Native XLA-FP8" (NVIDIA JAX-Toolbox),
+ * section "JAX": quantize A_fp8 = cast(A / A_scale); dequantize cast_up(a_fp8) *
+ * a_scale; delayed scaling A_scale = max|A| / E4M3_MAX.
+ *
+ * Conventions shared by every entry point
+ *   Pointers.   Every pointer except `tensors` of fp8_multi_quantize_amax is a
+ *               DEVICE pointer on the current HIP device.  The caller owns all
+ *               memory; the library allocates nothing, frees nothing and keeps no
+ *               per-call state, so calls are reentrant and thread-safe.
+ *   Streams.    `stream` is a hipStream_t (NULL = the null stream).  Every call only
+ *               enqueues work on it and returns; nothing synchronises and nothing is
+ *               copied device-to-host.
+ *   Errors.     Arguments are validated on the host before anything is enqueued; a
+ *               negative status is returned and nothing is enqueued.  A failed
+ *               launch returns FP8Q_EHIP.  Faults during kernel execution surface at
+ *               the caller's next synchronisation, as in HIP.
+ *   Layout.     Tensors are dense and contiguous, element i at byte offset
+ *               i * sizeof(element).  Any alignment is accepted: when source and
+ *               destination are aligned alike the body runs with 16-byte vector
+ *               loads, otherwise (or for the few head/tail elements) element-wise.
+ *   Aliasing.   Sources and destinations of one call must not overlap.
+ *   Numerics.   Binary32 throughout: the quotient x/scale is one IEEE division
+ *               rounded to nearest even, then saturated to +-FP8_MAX (448 for E4M3,
+ *               57344 for E5M2), then rounded to nearest even into the FP8 format,
+ *               FP8 subnormals and the sign of zero kept.  A NaN quotient becomes
+ *               0x7F (E4M3 and E5M2 NaN) with the sign bit of x.  +-inf saturates.
+ */
+#ifndef FP8Q_H
+#define FP8Q_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* FP8 formats ("User Guide on Native XLA-FP8", opening paragraphs: E4M3 for the
+ * forward pass, E5M2 for gradients).  OCP encodings: E4M3 = float8_e4m3fn (bias 7,
+ * no inf, max 448), E5M2 = float8_e5m2 (bias 15, inf, max 57344). */
+enum { FP8Q_E4M3 = 0, FP8Q_E5M2 = 1 };
+
+/* Wide element types (quantize source, dequantize destination). */
+enum { FP8Q_BF16 = 0, FP8Q_F32 = 1 };
+
+/* How the scale update picks the amax ("Implement fused kernel for FP8 scale
+ * update": the amax comes from the history).  MAX: the largest entry of the rolled
+ * history window; MOST_RECENT: the amax just inserted. */
+enum { FP8Q_AMAX_MAX = 0, FP8Q_AMAX_MOST_RECENT = 1 };
+
+/* Status codes. */
+enum {
+  FP8Q_OK = 0,
+  FP8Q_EINVAL = -1,       /* invalid argument; nothing was enqueued            */
+  FP8Q_EUNSUPPORTED = -2, /* valid request this build cannot serve              */
+  FP8Q_EHIP = -3          /* a HIP runtime call or kernel launch failed          */
+};
+
+/* One entry of a multi-tensor quantize call. */
+typedef struct fp8q_tensor {
+  const void* src;    /* device; numel elements of src_dtype                          */
+  uint8_t* dst;       /* device; numel FP8 codes                                      */
+  int64_t numel;      /* >= 0; 0 is a no-op for this entry (amax left unchanged)      */
+  int32_t src_dtype;  /* FP8Q_BF16 | FP8Q_F32                                         */
+  int32_t format;     /* FP8Q_E4M3 | FP8Q_E5M2                                        */
+  const float* scale; /* device, 1 float: the previous step's scale (the divisor)    */
+  float* amax;        /* device, 1 float: max-accumulated with max|src|; entries may
+                         share one amax                                               */
+} fp8q_tensor;
+
+/*
+ * fp8_quantize_amax -- fused quantize + amax of one tensor.
+ *   dst[i]  = FP8(saturate(RN32(src[i] / *scale)))            for i in [0, numel)
+ *   *amax   = max(*amax, max_i |src[i]|)
+ * ("User Guide on Native XLA-FP8", section "JAX": quantization divides by the scale
+ * of the previous step and casts; the amax is max|A| of the unscaled tensor.
+ * "Fusion of Fp8 quantization and amax reduction kernels": both in one pass.)
+ * The amax is max-accumulated ("Gradient accumulation of FP8 params": FP8 meta
+ * combines with max): it is compared by bit pattern with the sign cleared, so a NaN
+ * input propagates into amax, and the caller zeroes *amax before the first call of a
+ * step (or lets fp8_amax_and_scale_update with reset_amax do it).  *amax must hold a
+ * non-negative value or NaN.
+ *   src_dtype  FP8Q_BF16 or FP8Q_F32.   format  FP8Q_E4M3 or FP8Q_E5M2.
+ *   numel      >= 0; 0 enqueues nothing.  src, dst non-NULL when numel > 0; scale and
+ *              amax non-NULL always.
+ * Returns FP8Q_OK, FP8Q_EINVAL or FP8Q_EHIP.
+ */
+int fp8_quantize_amax(const void* src, int src_dtype, uint8_t* dst, int64_t numel,
+                      int format, const float* scale, float* amax, void* stream);
+
+/*
+ * fp8_multi_quantize_amax -- fp8_quantize_amax over a list of tensors in one
+ * kernel launch per 32 entries (the per-op launch overhead of many small GPU ops is
+ * what "Implement fused kernel for FP8 scale update" profiles; batching across
+ * layers is the remedy it names).  Each entry follows fp8_quantize_amax exactly;
+ * entries may mix dtypes and formats and may share an amax.
+ *   tensors    HOST array of n entries, read during the call only.
+ *   n          >= 0; 0 enqueues nothing.
+ * Every entry is validated before anything is enqueued.
+ * Returns FP8Q_OK, FP8Q_EINVAL or FP8Q_EHIP.
+ */
+int fp8_multi_quantize_amax(const fp8q_tensor* tensors, int n, void* stream);
+
+/*
+ * fp8_dequantize -- y[i] = RN32(decode(src[i]) * *scale), written as fp32, or
+ * rounded to nearest even into bf16 ("User Guide on Native XLA-FP8", section "JAX":
+ * dequantization casts up and multiplies by the scale).  A NaN result is written as
+ * the quiet NaN 0x7FC00000 (bf16 0x7FC0) carrying the sign bit of the code.
+ *   format     FP8Q_E4M3 or FP8Q_E5M2.   dst_dtype  FP8Q_BF16 or FP8Q_F32.
+ *   numel      >= 0; src, dst non-NULL when numel > 0; scale non-NULL.
+ * Returns FP8Q_OK, FP8Q_EINVAL or FP8Q_EHIP.
+ */
+int fp8_dequantize(const uint8_t* src, int format, void* dst, int dst_dtype, int64_t numel,
+                   const float* scale, void* stream);
+
+/*
+ * fp8_amax_and_scale_update -- the delayed-scaling update of n tensors, in place,
+ * in one launch ("Implement fused kernel for FP8 scale update": history roll,
+ * amax selection and scale computation fused, in place; "User Guide on Native
+ * XLA-FP8", section "JAX": scale = amax / FP8_MAX).  For every tensor t:
+ *   roll      amax_history[h][t] = old amax_history[h-1][t] for h = H-1 .. 1 (the
+ *             oldest row H-1 is dropped), amax_history[0][t] = amax[t];
+ *   select    sel = max over h of amax_history[h][t] (algo MAX, compared by bit
+ *             pattern) or amax[t] (algo MOST_RECENT);
+ *   scale     c = RN32(sel / FP8_MAX(formats[t])) * 2^margin (exact power-of-two
+ *             scaling); scale[t] = c if sel and c are finite and > 0, otherwise
+ *             scale[t] keeps its previous value;
+ *   inverse   scale_inv[t] = RN32(1 / scale[t]);
+ *   reset     if reset_amax != 0: amax[t] = 0 after it has been read.
+ *   amax           device float[n]   (written only when reset_amax != 0)
+ *   amax_history   device float[H][n], row-major, row 0 newest; updated in place
+ *   scale          device float[n], in: previous scale, out: new scale
+ *   scale_inv      device float[n], out
+ *   formats        device uint8[n]: 0 = E4M3 (max 448), any other value = E5M2
+ *                  (max 57344)
+ *   n >= 0 (0 enqueues nothing); history_len >= 1; algo FP8Q_AMAX_MAX or
+ *   FP8Q_AMAX_MOST_RECENT; margin in [-126, 126].  The five arrays must not overlap.
+ * Returns FP8Q_OK, FP8Q_EINVAL or FP8Q_EHIP.
+ */
+int fp8_amax_and_scale_update(float* amax, float* amax_history, float* scale,
+                              float* scale_inv, const uint8_t* formats, int64_t n,
+                              int64_t history_len, int algo, int margin, int reset_amax,
+                              void* stream);
+
+/* Static, human-readable text for a status code. */
+const char* fp8_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP8Q_H */

@@ -1,0 +1,168 @@
+"""CPU oracle for FP8 delayed scaling (quantize + amax, amax-history scale update,
+dequantize).
+
+TEST INFRASTRUCTURE ONLY: imported by ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py``.  The GPU library (``delayed_scaling_amax_amd``)
+never imports, links or calls anything here, and this package never imports it.
+
+The arithmetic lives in ``fp8_oracle.c`` (plain serial C, one IEEE binary32 operation
+per step).  This module compiles it with gcc and marshals numpy arrays into it.  The
+only parallelism added here is splitting an element range into contiguous chunks run
+by threads; the chunk amaxes are combined with the same bit-pattern max the oracle
+uses, which is exact and order-independent.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "fp8_oracle.c")
+LIB_PATH = os.path.join(_HERE, "liboracle.so")
+
+E4M3, E5M2 = 0, 1
+BF16, F32 = 0, 1
+AMAX_MAX, AMAX_MOST_RECENT = 0, 1
+
+_lib = None
+
+
+def build(lib_path: str = LIB_PATH, src: str = _SRC, extra_flags=()) -> str:
+    """Compile the oracle with gcc (no fast-math, no FMA contraction)."""
+    tmp = lib_path + ".tmp%d" % os.getpid()
+    cmd = ["gcc", "-O2", "-ffp-contract=off", "-fno-fast-math", "-std=c11", "-Wall",
+           "-fPIC", "-shared", "-o", tmp, src, "-lm", *extra_flags]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, lib_path)
+    return lib_path
+
+
+def _declare(lib):
+    c = ctypes
+    vp, i64, i32, f32p = c.c_void_p, c.c_int64, c.c_int, c.POINTER(c.c_float)
+    lib.oracle_fp8_max.argtypes = [i32]
+    lib.oracle_fp8_max.restype = c.c_float
+    lib.oracle_fp8_decode.argtypes = [i32, c.c_uint8]
+    lib.oracle_fp8_decode.restype = c.c_float
+    lib.oracle_fp8_encode.argtypes = [i32, c.c_float]
+    lib.oracle_fp8_encode.restype = c.c_uint8
+    lib.oracle_quantize_element.argtypes = [i32, c.c_float, c.c_float]
+    lib.oracle_quantize_element.restype = c.c_uint8
+    lib.oracle_quantize_amax.argtypes = [vp, i32, vp, i64, i32, c.c_float, f32p]
+    lib.oracle_quantize_amax.restype = None
+    lib.oracle_amax.argtypes = [vp, i32, i64, f32p]
+    lib.oracle_amax.restype = None
+    lib.oracle_amax_and_scale_update.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i64, i64,
+                                                 i32, i32, i32]
+    lib.oracle_amax_and_scale_update.restype = None
+    lib.oracle_dequantize.argtypes = [vp, i32, vp, i32, i64, c.c_float]
+    lib.oracle_dequantize.restype = None
+    lib.oracle_count_saturated.argtypes = [vp, i32, i64, i32, c.c_float]
+    lib.oracle_count_saturated.restype = i64
+    return lib
+
+
+class Oracle:
+    """ctypes view of one compiled oracle library (the real one, or a test mutant)."""
+
+    def __init__(self, lib_path: str):
+        self.path = lib_path
+        self.lib = _declare(ctypes.CDLL(lib_path))
+
+    # -- scalar entry points -------------------------------------------------
+    def fp8_max(self, fmt: int) -> float:
+        return float(self.lib.oracle_fp8_max(fmt))
+
+    def decode(self, fmt: int, code: int) -> float:
+        return float(self.lib.oracle_fp8_decode(fmt, code))
+
+    def encode(self, fmt: int, v: float) -> int:
+        return int(self.lib.oracle_fp8_encode(fmt, v))
+
+    def quantize_element(self, fmt: int, x: float, scale: float) -> int:
+        return int(self.lib.oracle_quantize_element(fmt, x, scale))
+
+    # -- array entry points --------------------------------------------------
+    @staticmethod
+    def _src(x: np.ndarray):
+        x = np.ascontiguousarray(x)
+        if x.dtype == np.uint16:
+            return x, BF16
+        if x.dtype == np.float32:
+            return x, F32
+        raise TypeError("src must be uint16 (bf16 bits) or float32, got %s" % x.dtype)
+
+    def quantize_amax(self, x: np.ndarray, fmt: int, scale: float, amax_in: float = 0.0,
+                      threads: int = 1, out: np.ndarray | None = None):
+        """Returns (codes uint8[n], amax float32).  x: uint16 bf16 bits or float32."""
+        x, dt = self._src(x)
+        flat = x.reshape(-1)
+        n = flat.size
+        dst = np.empty(n, np.uint8) if out is None else out.reshape(-1)
+        threads = max(1, min(int(threads), max(1, n // (1 << 16))))
+        bounds = [n * k // threads for k in range(threads + 1)]
+        amaxes = np.zeros(threads, np.float32)
+
+        def run(k):
+            lo, hi = bounds[k], bounds[k + 1]
+            a = ctypes.c_float(amax_in)      # every chunk max-accumulates into amax_in
+            self.lib.oracle_quantize_amax(flat[lo:].ctypes.data if hi > lo else None, dt,
+                                          dst[lo:].ctypes.data if hi > lo else None,
+                                          hi - lo, fmt, float(scale), ctypes.byref(a))
+            amaxes[k] = a.value
+
+        if threads == 1:
+            run(0)
+        else:
+            with ThreadPoolExecutor(threads) as ex:
+                list(ex.map(run, range(threads)))
+        return dst.reshape(x.shape), np.uint32(amaxes.view(np.uint32).max()).view(np.float32)
+
+    def amax(self, x: np.ndarray, amax_in: float = 0.0) -> np.float32:
+        x, dt = self._src(x)
+        a = ctypes.c_float(amax_in)
+        self.lib.oracle_amax(x.ctypes.data, dt, x.size, ctypes.byref(a))
+        return np.float32(a.value)
+
+    def amax_and_scale_update(self, amax, hist, scale, formats, algo=AMAX_MAX, margin=0,
+                              reset_amax=False):
+        """Out-of-place update.  hist: float32[H, n].  Returns dict of new arrays."""
+        amax = np.ascontiguousarray(amax, np.float32)
+        hist = np.ascontiguousarray(hist, np.float32)
+        scale = np.ascontiguousarray(scale, np.float32)
+        formats = np.ascontiguousarray(formats, np.uint8)
+        H, n = hist.shape
+        assert amax.shape == (n,) and scale.shape == (n,) and formats.shape == (n,)
+        out = dict(hist=np.empty_like(hist), scale=np.empty_like(scale),
+                   scale_inv=np.empty_like(scale), amax=np.empty_like(amax))
+        self.lib.oracle_amax_and_scale_update(
+            amax.ctypes.data, hist.ctypes.data, out["hist"].ctypes.data, scale.ctypes.data,
+            out["scale"].ctypes.data, out["scale_inv"].ctypes.data, out["amax"].ctypes.data,
+            formats.ctypes.data, n, H, int(algo), int(margin), int(bool(reset_amax)))
+        return out
+
+    def dequantize(self, codes: np.ndarray, fmt: int, scale: float, out_dtype: int = F32):
+        codes = np.ascontiguousarray(codes, np.uint8)
+        dst = np.empty(codes.shape, np.float32 if out_dtype == F32 else np.uint16)
+        self.lib.oracle_dequantize(codes.ctypes.data, fmt, dst.ctypes.data, out_dtype,
+                                   codes.size, float(scale))
+        return dst
+
+    def count_saturated(self, x: np.ndarray, fmt: int, scale: float) -> int:
+        x, dt = self._src(x)
+        return int(self.lib.oracle_count_saturated(x.ctypes.data, dt, x.size, fmt,
+                                                   float(scale)))
+
+
+def load(build_if_missing: bool = True) -> Oracle:
+    """The oracle library built from fp8_oracle.c (compiled here if not built yet)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH) and build_if_missing:
+            build()
+        _lib = Oracle(LIB_PATH)
+    return _lib

@@ -1,0 +1,227 @@
+/*
+ * fp8_oracle.c -- plain CPU oracle for FP8 delayed scaling.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This file is compiled into liboracle.so, which only
+ * tests/, the smoke check and the CPU-baseline leg of bench.py load.  The GPU
+ * library shares no code, header, table or constant with it and never calls it.
+ *
+ * Everything here is the plain definition, element by element, in IEEE binary32
+ * where the method fixes binary32 (the scales and the quotient x/scale) and in
+ * exact double arithmetic where only exact values are manipulated (decoding FP8
+ * codes, locating the nearest FP8 value).  Build: gcc -O2 -ffp-contract=off, no
+ * fast-math, so every binary32 operation below is one correctly rounded IEEE op.
+ *
+ * Sources (the pages):
+ *  [NG-intro]  "User Guide on Native XLA-FP8" (NVIDIA JAX-Toolbox), opening
+ *              paragraphs: the two FP8 formats E4M3 (float8_e4m3fn) and E5M2
+ *              (float8_e5m2); E4M3 for forward tensors, E5M2 for gradients;
+ *              quantization scales wide data into the FP8 range, dequantization
+ *              scales it back.
+ *  [NG-JAX]    same page, section "JAX", second example: quantize divides by the
+ *              scale of the previous step then casts to E4M3; dequantize casts up
+ *              and multiplies by the scale; the delayed-scaling update sets
+ *              scale = max|A| / E4M3_MAX; scales are held in wider types.
+ *  [NG-grad]   same page, section "Gradient accumulation of FP8 params": FP8 meta
+ *              (amax history, scale) accumulates with max, not with addition.
+ *  [XLA-7432]  "Fusion of Fp8 quantization and amax reduction kernels" (openxla/xla
+ *              issue 7432): the quantize pass and the amax reduction read the same
+ *              tensor and are the two passes being fused.
+ *  [TE-593]    "Implement fused kernel for FP8 scale update" (TransformerEngine
+ *              PR 593): one update per call that rolls the amax history in place,
+ *              takes the amax from the history and computes the new scale.
+ *
+ * Readings where the pages are silent (each also listed in the design notes):
+ *  R1 x/scale is one binary32 IEEE round-to-nearest-even division.
+ *  R2 the quotient saturates to +-FP8_MAX before the cast (no NaN/inf on overflow).
+ *  R3 the cast rounds to nearest, ties to even, keeps FP8 subnormals and the sign
+ *     of zero.
+ *  R4 a NaN quotient encodes as 0x7F with the sign bit of x.
+ *  R5 amax is the max of the unscaled |x|, taken as an unsigned max over the
+ *     binary32 bit patterns with the sign cleared, and max-accumulated into the
+ *     caller's amax (also by bit pattern).
+ *  R6 history layout hist[H][N] row-major, row 0 newest: the roll moves row h-1 to
+ *     row h, drops row H-1 and writes the new amax into row 0; the selection then
+ *     runs over the rolled window.
+ *  R7 scale = RN32(sel / FP8_MAX) * 2^margin; if sel is not finite or not > 0, or
+ *     the result is not finite or not > 0, the previous scale is kept.
+ *  R8 scale_inv = RN32(1 / scale).
+ *  R9 dequantize y = RN32(decode(q) * scale); a NaN result is the quiet NaN
+ *     0x7FC00000 carrying the sign bit of the code; bf16 output rounds y to
+ *     nearest even.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+enum { ORC_E4M3 = 0, ORC_E5M2 = 1 };
+enum { ORC_BF16 = 0, ORC_F32 = 1 };
+enum { ORC_AMAX_MAX = 0, ORC_AMAX_MOST_RECENT = 1 };
+
+static uint32_t f2u(float f) { uint32_t u; memcpy(&u, &f, 4); return u; }
+static float u2f(uint32_t u) { float f; memcpy(&f, &u, 4); return f; }
+
+/* Format parameters of the two OCP formats named in [NG-intro]:
+ *   E4M3 (e4m3fn): 4 exponent bits, bias 7, 3 mantissa bits, no infinity,
+ *                  S.1111.111 is NaN, so the largest finite is 1.75 * 2^8 = 448.
+ *   E5M2:          5 exponent bits, bias 15, 2 mantissa bits, exponent 31 holds
+ *                  inf (mantissa 0) and NaN, largest finite 1.75 * 2^15 = 57344. */
+static int fmt_mbits(int fmt) { return fmt == ORC_E4M3 ? 3 : 2; }
+static int fmt_bias(int fmt) { return fmt == ORC_E4M3 ? 7 : 15; }
+float oracle_fp8_max(int fmt) { return fmt == ORC_E4M3 ? 448.0f : 57344.0f; }
+
+/* Decode one FP8 code to its exact value (closed form of the format). */
+float oracle_fp8_decode(int fmt, uint8_t code) {
+  int sign = code >> 7;
+  int mbits = fmt_mbits(fmt), bias = fmt_bias(fmt);
+  int efield = (code & 0x7F) >> mbits;
+  int m = code & ((1 << mbits) - 1);
+  double v;
+  if (fmt == ORC_E4M3 && efield == 15 && m == 7) {
+    v = NAN;
+  } else if (fmt == ORC_E5M2 && efield == 31) {
+    v = (m == 0) ? INFINITY : NAN;
+  } else if (efield == 0) {
+    v = ldexp((double)m, 1 - bias - mbits);                 /* subnormal */
+  } else {
+    v = ldexp(1.0 + (double)m / (double)(1 << mbits), efield - bias);
+  }
+  return (float)(sign ? -v : v);
+}
+
+/* Encode v (finite with |v| <= FP8_MAX, or NaN) to the nearest FP8 code, ties to
+ * the code with an even mantissa, subnormals kept, sign of zero kept (R3). */
+uint8_t oracle_fp8_encode(int fmt, float v) {
+  uint8_t sign = signbit(v) ? 0x80 : 0x00;
+  if (isnan(v)) return (uint8_t)(0x7F | sign);
+  int mbits = fmt_mbits(fmt), bias = fmt_bias(fmt), emin = 1 - bias;
+  double a = fabs((double)v);
+  if (a == 0.0) return sign;
+  int e;
+  frexp(a, &e);            /* a = f * 2^e with f in [0.5, 1): binade exponent is e-1 */
+  e -= 1;
+  if (e < emin) e = emin;  /* below the normal range the spacing stays 2^(emin-mbits) */
+  double n = nearbyint(ldexp(a, mbits - e));   /* exact scaling, then RNE to integer */
+  int code;
+  if (n < (double)(1 << mbits)) {
+    code = (int)n;                              /* subnormal (or zero) */
+  } else {
+    if (n == (double)(2 << mbits)) { n /= 2; e += 1; }  /* rounded up into next binade */
+    code = ((e + bias) << mbits) | ((int)n - (1 << mbits));
+  }
+  return (uint8_t)(code | sign);
+}
+
+/* One element of the quantize pass [NG-JAX]: (x / scale) cast to FP8 with R1-R4. */
+uint8_t oracle_quantize_element(int fmt, float x, float scale) {
+  float v = x / scale;
+  if (isnan(v)) return (uint8_t)(0x7F | (signbit(x) ? 0x80 : 0x00));
+  float mx = oracle_fp8_max(fmt);
+  if (v > mx) v = mx;
+  if (v < -mx) v = -mx;
+  return oracle_fp8_encode(fmt, v);
+}
+
+static float load_wide(const void* src, int src_dtype, int64_t i) {
+  if (src_dtype == ORC_BF16) return u2f((uint32_t)((const uint16_t*)src)[i] << 16);
+  return ((const float*)src)[i];
+}
+
+/* Quantize n elements and max-accumulate amax over the same elements
+ * ([XLA-7432] pass pair, [NG-JAX] formulas, R5). */
+void oracle_quantize_amax(const void* src, int src_dtype, uint8_t* dst, int64_t n,
+                          int fmt, float scale, float* amax) {
+  uint32_t acc = f2u(*amax);
+  for (int64_t i = 0; i < n; ++i) {
+    float x = load_wide(src, src_dtype, i);
+    dst[i] = oracle_quantize_element(fmt, x, scale);
+    uint32_t mag = f2u(x) & 0x7FFFFFFFu;
+    if (mag > acc) acc = mag;
+  }
+  *amax = u2f(acc);
+}
+
+/* Amax only (same R5 reduction), for checks that do not need the codes. */
+void oracle_amax(const void* src, int src_dtype, int64_t n, float* amax) {
+  uint32_t acc = f2u(*amax);
+  for (int64_t i = 0; i < n; ++i) {
+    uint32_t mag = f2u(load_wide(src, src_dtype, i)) & 0x7FFFFFFFu;
+    if (mag > acc) acc = mag;
+  }
+  *amax = u2f(acc);
+}
+
+/* The amax-history scale update of [TE-593] for n tensors, out of place
+ * (hist_in/hist_out are [H][n] row-major; R6-R8; scale formula [NG-JAX]). */
+void oracle_amax_and_scale_update(const float* amax, const float* hist_in, float* hist_out,
+                                  const float* scale_in, float* scale_out,
+                                  float* scale_inv_out, float* amax_out,
+                                  const uint8_t* formats, int64_t n, int64_t H,
+                                  int algo, int margin, int reset_amax) {
+  for (int64_t t = 0; t < n; ++t) {
+    hist_out[t] = amax[t];
+    for (int64_t h = 1; h < H; ++h) hist_out[h * n + t] = hist_in[(h - 1) * n + t];
+
+    uint32_t sel_bits;
+    if (algo == ORC_AMAX_MOST_RECENT) {
+      sel_bits = f2u(amax[t]);
+    } else {
+      sel_bits = 0;
+      for (int64_t h = 0; h < H; ++h) {
+        uint32_t b = f2u(hist_out[h * n + t]);
+        if (b > sel_bits) sel_bits = b;
+      }
+    }
+    float sel = u2f(sel_bits);
+    float mx = oracle_fp8_max(formats[t] ? ORC_E5M2 : ORC_E4M3);
+    float s = scale_in[t];
+    if (isfinite(sel) && sel > 0.0f) {
+      float c = sel / mx;
+      c = ldexpf(c, margin);
+      if (isfinite(c) && c > 0.0f) s = c;
+    }
+    scale_out[t] = s;
+    scale_inv_out[t] = 1.0f / s;
+    amax_out[t] = reset_amax ? 0.0f : amax[t];
+  }
+}
+
+/* Round a binary32 value to bfloat16 (8 significant bits), nearest-even, with
+ * overflow to infinity; returns the bf16 bit pattern.  NaN handled by caller. */
+static uint16_t round_to_bf16(float y) {
+  uint32_t sign = f2u(y) & 0x80000000u;
+  double a = fabs((double)y);
+  if (isinf(y) || a == 0.0) return (uint16_t)(f2u(y) >> 16);
+  int e;
+  frexp(a, &e);
+  e -= 1;
+  if (e < -126) e = -126;
+  double r = ldexp(nearbyint(ldexp(a, 7 - e)), e - 7);   /* nearest multiple of 2^(e-7) */
+  if (r >= ldexp(1.0, 128)) return (uint16_t)((sign | 0x7F800000u) >> 16);
+  return (uint16_t)((sign | f2u((float)r)) >> 16);       /* r has <= 8 significant bits */
+}
+
+/* Dequantize [NG-JAX]: decode, multiply by the scale in binary32 (R9). */
+void oracle_dequantize(const uint8_t* src, int fmt, void* dst, int dst_dtype, int64_t n,
+                       float scale) {
+  for (int64_t i = 0; i < n; ++i) {
+    float y = oracle_fp8_decode(fmt, src[i]) * scale;
+    uint32_t nan_bits = 0x7FC00000u | ((uint32_t)(src[i] & 0x80) << 24);
+    if (dst_dtype == ORC_F32) {
+      ((float*)dst)[i] = isnan(y) ? u2f(nan_bits) : y;
+    } else {
+      ((uint16_t*)dst)[i] = isnan(y) ? (uint16_t)(nan_bits >> 16) : round_to_bf16(y);
+    }
+  }
+}
+
+/* Count of elements whose quotient lands beyond +-FP8_MAX (saturated by R2). */
+int64_t oracle_count_saturated(const void* src, int src_dtype, int64_t n, int fmt,
+                               float scale) {
+  int64_t c = 0;
+  float mx = oracle_fp8_max(fmt);
+  for (int64_t i = 0; i < n; ++i) {
+    float v = load_wide(src, src_dtype, i) / scale;
+    if (v > mx || v < -mx) ++c;
+  }
+  return c;
+}

@@ -1,0 +1,476 @@
+"""Pins of the CPU oracle against facts that do not come from the oracle itself.
+
+Each ``pin_*`` function takes an ``oracle.Oracle`` and raises AssertionError when it
+disagrees with:
+  * values worked by hand from the format definitions (tests/golden/*.txt, cited there);
+  * torch's CPU float8_e4m3fn / float8_e5m2 decode and cast, and its bfloat16 cast
+    (an independent library; the oracle does not use torch);
+  * exact rational arithmetic (``fractions.Fraction``) with round-half-even done here,
+    independent of the host's IEEE hardware;
+  * brute-force nearest-code search over the decoded code table;
+  * invariants (monotonicity, power-of-two margin, roll bookkeeping, error bound).
+
+test_oracle_pins.py runs them on the real oracle; test_oracle_mutants.py runs them on
+oracle copies with planted mistakes and requires each mistake to fail at least one pin.
+"""
+from __future__ import annotations
+
+import os
+from fractions import Fraction
+
+import numpy as np
+import torch
+
+E4M3, E5M2 = 0, 1
+BF16, F32 = 0, 1
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+TORCH_FP8 = {E4M3: torch.float8_e4m3fn, E5M2: torch.float8_e5m2}
+FMT_NAME = {"e4m3": E4M3, "e5m2": E5M2}
+
+
+# ------------------------------------------------------------------ helpers
+def u2f(u: int) -> float:
+    return float(np.uint32(u).view(np.float32))
+
+
+def f2u(f) -> int:
+    return int(np.float32(f).view(np.uint32))
+
+
+def bf16_to_f32(bits: np.ndarray) -> np.ndarray:
+    return (bits.astype(np.uint32) << 16).view(np.float32)
+
+
+def rn_binary(fr: Fraction, mant_bits: int, emin: int, emax_bound: int) -> Fraction | None:
+    """Exact round-to-nearest-even of a non-negative rational to a binary format with
+    `mant_bits` fraction bits and minimum normal exponent `emin`; None on overflow
+    (result >= 2^emax_bound)."""
+    if fr == 0:
+        return Fraction(0)
+    p, q = fr.numerator, fr.denominator
+    e = p.bit_length() - q.bit_length()
+    if Fraction(2) ** e > fr:
+        e -= 1
+    e = max(e, emin)
+    quantum = Fraction(2) ** (e - mant_bits)
+    r = round(fr / quantum) * quantum          # Fraction.__round__ is half-to-even
+    if r >= Fraction(2) ** emax_bound:
+        return None
+    return r
+
+
+def rn32(fr: Fraction) -> float:
+    """Exact RN-even of a rational to binary32 (sign handled, overflow -> inf)."""
+    sgn = -1.0 if fr < 0 else 1.0
+    r = rn_binary(abs(fr), 23, -126, 128)
+    return sgn * (float("inf") if r is None else float(r))
+
+
+def code_table(fmt: int) -> np.ndarray:
+    """Decoded values of all 256 codes from torch (independent library)."""
+    return torch.arange(256, dtype=torch.uint8).view(TORCH_FP8[fmt]).float().numpy()
+
+
+def brute_encode(fmt: int, v: np.ndarray) -> np.ndarray:
+    """Nearest finite code by exhaustive search over the code table; ties go to the
+    code with an even mantissa (LSB 0); zero keeps its sign.  |v| <= max assumed."""
+    tab = code_table(fmt).astype(np.float64)
+    pos = [c for c in range(128) if np.isfinite(tab[c])]
+    vals = tab[pos]
+    codes = np.array(pos)
+    v = np.asarray(v, np.float64)
+    a = np.abs(v)
+    d = np.abs(vals[None, :] - a[:, None])
+    best = d.min(axis=1, keepdims=True)
+    cand = d == best
+    # among candidates prefer even LSB
+    even = (codes[None, :] & 1) == 0
+    pick = np.where((cand & even).any(axis=1), np.argmax(cand & even, axis=1),
+                    np.argmax(cand, axis=1))
+    out = codes[pick].astype(np.uint8)
+    out |= (np.signbit(v).astype(np.uint8) << 7)
+    return out
+
+
+def read_golden(name: str):
+    rows = []
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.split("#", 1)[0].strip()
+            if line:
+                rows.append(line)
+    return rows
+
+
+def golden_kv(name: str) -> dict:
+    kv = {}
+    for r in read_golden(name):
+        if ":" in r:
+            k, v = r.split(":", 1)
+            kv[k.strip()] = v.split()
+    return kv
+
+
+# ------------------------------------------------------------------ pins: formats
+def pin_format_constants(o):
+    for row in read_golden("fp8_formats.txt"):
+        f = row.split()
+        if f[0] not in FMT_NAME:
+            continue
+        fmt = FMT_NAME[f[0]]
+        mx = float(f[1])
+        mn = 2.0 ** int(f[2].split("^")[1])
+        ms = 2.0 ** int(f[3].split("^")[1])
+        assert o.fp8_max(fmt) == mx
+        assert o.decode(fmt, int(f[4], 16)) == mx
+        assert o.decode(fmt, int(f[5], 16)) == mn
+        assert o.decode(fmt, int(f[6], 16)) == ms
+        vals = np.array([o.decode(fmt, c) for c in range(256)])
+        assert np.isfinite(vals).sum() == int(f[7])
+        assert np.isnan(vals).sum() == int(f[8])
+        assert np.isinf(vals).sum() == int(f[9])
+        assert torch.finfo(TORCH_FP8[fmt]).max == mx
+
+
+def pin_decode_matches_torch(o):
+    for fmt in (E4M3, E5M2):
+        ref = code_table(fmt)
+        got = np.array([o.decode(fmt, c) for c in range(256)], np.float32)
+        same = (got.view(np.uint32) == ref.view(np.uint32)) | (np.isnan(got) & np.isnan(ref))
+        assert same.all(), np.nonzero(~same)[0][:8]
+
+
+def pin_decode_monotone(o):
+    for fmt in (E4M3, E5M2):
+        pos = np.array([o.decode(fmt, c) for c in range(128)])
+        fin = pos[np.isfinite(pos)]
+        assert (np.diff(fin) > 0).all()
+        neg = np.array([o.decode(fmt, c | 0x80) for c in range(128)])
+        assert (np.signbit(neg)).all()
+
+
+def pin_encode_roundtrip(o):
+    for fmt in (E4M3, E5M2):
+        for c in range(256):
+            v = o.decode(fmt, c)
+            if np.isfinite(v):
+                assert o.encode(fmt, v) == c, (fmt, hex(c))
+
+
+def pin_encode_bruteforce_all_bf16(o):
+    """Every finite bf16 value, clamped to +-max, vs exhaustive nearest search and
+    vs torch's CPU cast (which agrees once the value is in range)."""
+    allb = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    x = bf16_to_f32(allb)
+    x = x[np.isfinite(x)]
+    for fmt in (E4M3, E5M2):
+        mx = np.float32(o.fp8_max(fmt))
+        v = np.clip(x, -mx, mx)
+        got = np.array([o.encode(fmt, float(t)) for t in v], np.uint8)
+        tor = torch.from_numpy(v.copy()).to(TORCH_FP8[fmt]).view(torch.uint8).numpy()
+        assert (got == tor).all(), np.nonzero(got != tor)[0][:8]
+        # brute force on a strided subset (the full set is covered by torch above)
+        sub = v[::7]
+        assert (brute_encode(fmt, sub) == got[::7]).all()
+
+
+def pin_encode_random_f32(o):
+    g = np.random.Generator(np.random.PCG64(7))
+    for fmt in (E4M3, E5M2):
+        mx = o.fp8_max(fmt)
+        v = (np.exp2(g.uniform(-20, np.log2(mx), 4000)) *
+             np.where(g.random(4000) < 0.5, -1, 1)).astype(np.float32)
+        got = np.array([o.encode(fmt, float(t)) for t in v], np.uint8)
+        assert (got == brute_encode(fmt, v)).all()
+
+
+def pin_encode_worked_ties(o):
+    """Ties and underflow by hand: E4M3 2^-10 is half the smallest subnormal (tie ->
+    0x00), 1.5*2^-10 -> 0x01 (2^-9 nearer), -1e-9 -> 0x80 (signed zero); E5M2
+    480 = midpoint of 448 (0x5f) and 512 (0x60) -> 0x60 (even), 2^-17 -> 0x00 (tie),
+    3*2^-18 -> 0x01."""
+    assert o.encode(E4M3, 2.0 ** -10) == 0x00
+    assert o.encode(E4M3, 1.5 * 2.0 ** -10) == 0x01
+    assert o.encode(E4M3, -1e-9) == 0x80
+    assert o.encode(E4M3, 440.0) == 0x7E            # between 416 and 448, nearer 448
+    assert o.encode(E4M3, 432.0) == 0x7E            # midpoint 416|448 -> even 448 (0x7e)
+    assert o.encode(E4M3, 400.0) == 0x7C            # midpoint 384|416 -> even 384 (0x7c)
+    assert o.encode(E5M2, 448.0) == 0x5F
+    assert o.encode(E5M2, 480.0) == 0x60
+    assert o.encode(E5M2, 2.0 ** -17) == 0x00
+    assert o.encode(E5M2, 3 * 2.0 ** -18) == 0x01
+    assert o.encode(E5M2, -1e-9) == 0x80
+
+
+# ------------------------------------------------------------------ pins: quantize
+def pin_quantize_worked_tensor(o):
+    kv = golden_kv("quantize_worked.txt")
+    x = np.array([int(h, 16) for h in kv["x_bf16"]], np.uint16)
+    for key, fmt in (("e4m3_scale_3f800000", E4M3), ("e5m2_scale_3f800000", E5M2),
+                     ("e4m3_scale_400edb6e", E4M3)):
+        scale = u2f(int(key.rsplit("_", 1)[1], 16))
+        want = bytes(int(h, 16) for h in kv[key])
+        codes, amax = o.quantize_amax(x, fmt, scale)
+        assert codes.tobytes() == want, (key, codes.tobytes().hex())
+        assert f2u(amax) == int(kv["amax"][0], 16)
+
+
+def _exact_quantize(o, fmt, x: float, s: float) -> int:
+    """RN32 of the exact quotient (rational), saturation, brute-force encode."""
+    if np.isnan(x):
+        return 0x7F | (0x80 if np.signbit(x) else 0)
+    q = rn32(Fraction(x) / Fraction(s))
+    mx = o.fp8_max(fmt)
+    q = min(max(q, -mx), mx)
+    if q == 0.0:
+        return 0x80 if (np.signbit(x) != np.signbit(s)) else 0x00
+    return int(brute_encode(fmt, np.array([q]))[0])
+
+
+def pin_quantize_exact_quotient(o):
+    """Random (x, s) and near-midpoint quotients: the oracle's element result equals
+    exact-rational RN32(x/s) -> clamp -> nearest code.  Near-midpoint pairs make the
+    double rounding (binary32, then FP8) decide the byte."""
+    g = np.random.Generator(np.random.PCG64(11))
+    cases = []
+    for _ in range(1500):
+        s = float(np.float32(np.exp2(g.uniform(-30, 30))))
+        x = float(bf16_to_f32(np.array([g.integers(0, 1 << 16)], np.uint16))[0])
+        if np.isfinite(x):
+            cases.append((x, s))
+    for fmt in (E4M3, E5M2):
+        tab = code_table(fmt)
+        fin = np.sort(tab[np.isfinite(tab) & (tab >= 0)])
+        mids = (fin[1:] + fin[:-1]) / 2
+        for _ in range(600):
+            m = float(mids[g.integers(0, len(mids))])
+            s = float(np.float32(np.exp2(g.uniform(-20, 20))))
+            x = np.float32(m * s)
+            for k in (-2, -1, 0, 1, 2):
+                xx = float(np.nextafter(x, np.float32(np.inf) if k > 0 else np.float32(0)))
+                xx = float(x) if k == 0 else xx
+                cases.append((xx, s))
+    for fmt in (E4M3, E5M2):
+        for x, s in cases:
+            want = _exact_quantize(o, fmt, x, s)
+            got = o.quantize_element(fmt, x, s)
+            assert got == want, (fmt, x, s, hex(got), hex(want))
+
+
+def pin_quantize_f32_matches_encode_at_scale_one(o):
+    g = np.random.Generator(np.random.PCG64(3))
+    v = (np.exp2(g.uniform(-30, 20, 3000)) * np.where(g.random(3000) < .5, -1, 1)).astype(
+        np.float32)
+    for fmt in (E4M3, E5M2):
+        codes, _ = o.quantize_amax(v, fmt, 1.0)
+        mx = np.float32(o.fp8_max(fmt))
+        want = torch.from_numpy(np.clip(v, -mx, mx)).to(TORCH_FP8[fmt]).view(
+            torch.uint8).numpy()
+        assert (codes == want).all()
+
+
+def pin_quantize_specials(o):
+    # +-inf saturate, NaN -> 0x7f with the sign of x, huge quotients saturate.
+    for fmt in (E4M3, E5M2):
+        mxc = 0x7E if fmt == E4M3 else 0x7B
+        assert o.quantize_element(fmt, float("inf"), 1.0) == mxc
+        assert o.quantize_element(fmt, float("-inf"), 1.0) == mxc | 0x80
+        assert o.quantize_element(fmt, float("nan"), 1.0) == 0x7F
+        assert o.quantize_element(fmt, -float("nan"), 1.0) == 0xFF
+        assert o.quantize_element(fmt, 1e30, 1e-6) == mxc
+        assert o.quantize_element(fmt, -0.0, 3.0) == 0x80
+
+
+def pin_quantize_monotone(o):
+    allb = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    x = bf16_to_f32(allb)
+    x = np.sort(x[np.isfinite(x)])
+    for fmt, s in ((E4M3, 0.37), (E5M2, 1e-5)):
+        codes, _ = o.quantize_amax(x, fmt, s)
+        dec = code_table(fmt)[codes]
+        assert (np.diff(dec) >= 0).all()
+
+
+def pin_amax(o):
+    g = np.random.Generator(np.random.PCG64(5))
+    x = (g.standard_normal(10001) * 3).astype(np.float32)
+    xb = (x.view(np.uint32) >> 16).astype(np.uint16)        # bf16 by truncation
+    _, a = o.quantize_amax(xb, E4M3, 1.0)
+    assert a == np.abs(bf16_to_f32(xb)).max()
+    _, a = o.quantize_amax(x, E5M2, 2.0)
+    assert a == np.abs(x).max()
+    # max-accumulation: a larger incoming amax survives, a smaller one is replaced
+    _, a = o.quantize_amax(x, E4M3, 1.0, amax_in=1e6)
+    assert a == np.float32(1e6)
+    _, a = o.quantize_amax(x, E4M3, 1.0, amax_in=1e-6)
+    assert a == np.abs(x).max()
+    # negative values count by magnitude
+    _, a = o.quantize_amax(np.array([-5.0, 2.0], np.float32), E4M3, 1.0)
+    assert a == 5.0
+    # NaN propagates (largest bit pattern)
+    y = x.copy()
+    y[17] = np.nan
+    _, a = o.quantize_amax(y, E4M3, 1.0)
+    assert np.isnan(a)
+
+
+def pin_saturation_count(o):
+    x = np.array([447.0, 448.0, 463.9, 464.0, 470.0, -500.0, 1e9, np.inf], np.float32)
+    assert o.count_saturated(x, E4M3, 1.0) == 6
+    assert o.count_saturated(x, E5M2, 1.0) == 2
+
+
+def pin_dequant_error_bound(o):
+    """|dq(q(x)) - x| <= half an FP8 ulp of x/s, times s (plus binary32 rounding)."""
+    g = np.random.Generator(np.random.PCG64(9))
+    for fmt, s in ((E4M3, 0.013), (E5M2, 3.1e-4)):
+        mx = o.fp8_max(fmt)
+        xs = (g.uniform(-mx, mx, 3000) * s).astype(np.float32)
+        codes, _ = o.quantize_amax(xs, fmt, s)
+        y = o.dequantize(codes, fmt, s)
+        tab = code_table(fmt)
+        fin = np.sort(np.unique(np.abs(tab[np.isfinite(tab)])))
+        q = np.abs(xs.astype(np.float64) / s)
+        i = np.clip(np.searchsorted(fin, q), 1, len(fin) - 1)
+        gap = fin[i] - fin[i - 1]
+        err = np.abs(y.astype(np.float64) - xs)
+        assert (err <= 0.5 * gap * s * (1 + 2e-6) + np.abs(xs) * 2e-7).all()
+
+
+# ------------------------------------------------------------------ pins: scale update
+def pin_scale_update_worked(o):
+    for row in read_golden("scale_update_worked.txt"):
+        f = row.split()
+        if f[0].startswith("h4") or len(f) != 5:
+            continue
+        amax = u2f(int(f[0], 16))
+        fmt = FMT_NAME[f[1]]
+        r = o.amax_and_scale_update(np.array([amax], np.float32),
+                                    np.zeros((4, 1), np.float32),
+                                    np.ones(1, np.float32), np.array([fmt], np.uint8),
+                                    margin=int(f[2]))
+        assert f2u(r["scale"][0]) == int(f[3], 16), row
+        assert f2u(r["scale_inv"][0]) == int(f[4], 16), row
+
+
+def pin_history_worked(o):
+    hist = np.zeros((4, 1), np.float32)
+    scale = np.ones(1, np.float32)
+    for row in read_golden("scale_update_worked.txt"):
+        f = row.split()
+        if f[0] != "h4":
+            continue
+        a = np.array([float(f[1])], np.float32)
+        r = o.amax_and_scale_update(a, hist, scale, np.zeros(1, np.uint8))
+        hist, scale = r["hist"], r["scale"]
+        assert list(hist[:, 0]) == [float(v) for v in f[2:6]], row
+        sel = float(f[6])
+        assert f2u(scale[0]) == f2u(np.float32(rn32(Fraction(sel) / 448))), row
+    want = int(golden_kv("scale_update_worked.txt")["h4_last_scale"][0], 16)
+    assert f2u(scale[0]) == want
+
+
+def pin_scale_update_exact(o):
+    """Scale and scale_inv equal exact-rational RN32 of sel/MAX * 2^margin and of
+    1/scale, for random amaxes across the binary32 range, both formats, margins."""
+    g = np.random.Generator(np.random.PCG64(21))
+    n = 400
+    amax = np.exp2(g.uniform(-60, 60, n)).astype(np.float32)
+    fmts = (g.random(n) < 0.5).astype(np.uint8)
+    for margin in (0, 1, 3, -2):
+        r = o.amax_and_scale_update(amax, np.zeros((1, n), np.float32),
+                                    np.ones(n, np.float32), fmts, margin=margin)
+        for t in range(n):
+            mx = 448 if fmts[t] == 0 else 57344
+            c = rn32(Fraction(float(amax[t])) / mx)
+            c = rn32(Fraction(c) * Fraction(2) ** margin)
+            assert f2u(r["scale"][t]) == f2u(np.float32(c)), (t, margin)
+            inv = rn32(1 / Fraction(c))
+            assert f2u(r["scale_inv"][t]) == f2u(np.float32(inv)), (t, margin)
+
+
+def pin_scale_update_invariants(o):
+    g = np.random.Generator(np.random.PCG64(23))
+    H, n = 6, 50
+    hist = np.exp2(g.uniform(-10, 10, (H, n))).astype(np.float32)
+    amax = np.exp2(g.uniform(-10, 10, n)).astype(np.float32)
+    scale = np.exp2(g.uniform(-3, 3, n)).astype(np.float32)
+    fmts = np.tile(np.array([0, 0, 1], np.uint8), n)[:n]
+    r0 = o.amax_and_scale_update(amax, hist, scale, fmts, margin=0)
+    r1 = o.amax_and_scale_update(amax, hist, scale, fmts, margin=1)
+    # roll: row 0 = new amax, row h = old row h-1, old last row dropped
+    assert (r0["hist"][0] == amax).all()
+    assert (r0["hist"][1:] == hist[:-1]).all()
+    # margin 1 doubles the scale exactly
+    assert (r1["scale"] == 2 * r0["scale"]).all()
+    # algo max selects the max of the rolled window
+    sel = np.maximum(amax, hist[:-1].max(axis=0))
+    mx = np.where(fmts == 0, np.float32(448), np.float32(57344))
+    assert (r0["scale"] == (sel / mx).astype(np.float32)).all()
+    # most recent: selection is the new amax
+    rm = o.amax_and_scale_update(amax, hist, scale, fmts, algo=1)
+    assert (rm["scale"] == (amax / mx).astype(np.float32)).all()
+    assert (rm["hist"] == r0["hist"]).all()
+    # amax output: untouched without reset, zero with reset
+    assert (r0["amax"] == amax).all()
+    rr = o.amax_and_scale_update(amax, hist, scale, fmts, reset_amax=True)
+    assert (rr["amax"] == 0).all() and (rr["scale"] == r0["scale"]).all()
+    # k <= H steps from zero history: rows 0..k-1 hold the last k amaxes, newest first
+    h = np.zeros((H, 2), np.float32)
+    seq = [np.array([i + 1.0, 10.0 * (i + 1)], np.float32) for i in range(4)]
+    for a in seq:
+        h = o.amax_and_scale_update(a, h, np.ones(2, np.float32), np.zeros(2, np.uint8))["hist"]
+    assert (h[:4] == np.array(seq[::-1])).all() and (h[4:] == 0).all()
+
+
+def pin_scale_update_keep_previous(o):
+    prev = np.array([0.5, 0.25, 2.0, 4.0, 8.0], np.float32)
+    amax = np.array([0.0, np.inf, np.nan, 1e-45, 3.0e38], np.float32)
+    # zero history: sel = amax itself
+    r = o.amax_and_scale_update(amax, np.zeros((1, 5), np.float32), prev,
+                                np.zeros(5, np.uint8), margin=0)
+    # 0 -> keep; inf -> keep; NaN -> keep; 1e-45/448 underflows to 0 -> keep;
+    assert list(r["scale"][:4]) == list(prev[:4])
+    assert r["scale"][4] == np.float32(np.float32(3.0e38) / np.float32(448))
+    r = o.amax_and_scale_update(amax, np.zeros((1, 5), np.float32), prev,
+                                np.zeros(5, np.uint8), margin=120)
+    # 3e38/448 * 2^120 overflows -> keep
+    assert r["scale"][4] == prev[4]
+    assert (r["scale_inv"] == (np.float32(1) / r["scale"]).astype(np.float32)).all()
+
+
+# ------------------------------------------------------------------ pins: dequantize
+def pin_dequantize_matches_torch(o):
+    codes = np.arange(256, dtype=np.uint8)
+    for fmt in (E4M3, E5M2):
+        dec = torch.from_numpy(codes).view(TORCH_FP8[fmt]).float()
+        for s in (1.0, 0.0123, 3.7e4, 2.0 ** -20):
+            y = o.dequantize(codes, fmt, s)
+            want = (dec * torch.tensor(s, dtype=torch.float32)).numpy()
+            fin = ~np.isnan(want)
+            assert (y[fin].view(np.uint32) == want[fin].view(np.uint32)).all()
+            nanb = 0x7FC00000 | ((codes[~fin].astype(np.uint32) & 0x80) << 24)
+            assert (y[~fin].view(np.uint32) == nanb).all()
+            yb = o.dequantize(codes, fmt, s, out_dtype=BF16)
+            wb = torch.from_numpy(want).to(torch.bfloat16).view(torch.int16).numpy().view(
+                np.uint16)
+            assert (yb[fin] == wb[fin]).all()
+            assert (yb[~fin] == (nanb >> 16).astype(np.uint16)).all()
+
+
+def pin_bf16_rounding_random(o):
+    """bf16 output rounding vs torch's RNE cast on values with random low bits, incl.
+    overflow to inf and bf16-subnormal results."""
+    g = np.random.Generator(np.random.PCG64(29))
+    codes = g.integers(0, 256, 5000).astype(np.uint8)
+    for fmt in (E4M3, E5M2):
+        dec = torch.from_numpy(codes).view(TORCH_FP8[fmt]).float()
+        for s in (float(np.float32(1.2345678)), 3.0e36, 1.7e-41):
+            want = (dec * torch.tensor(s, dtype=torch.float32))
+            yb = o.dequantize(codes, fmt, s, out_dtype=BF16)
+            fin = ~torch.isnan(want).numpy()
+            wb = want.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+            assert (yb[fin] == wb[fin]).all()
+
+
+ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

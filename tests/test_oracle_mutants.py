@@ -1,0 +1,82 @@
+"""Planted mistakes in the CPU oracle must each fail at least one pin.
+
+Each mutant is a copy of oracle/fp8_oracle.c with one plausible mistake (a dropped
+term, a wrong sign, index, constant or rounding rule), compiled with the same flags
+into a temporary directory.  Nothing here touches the GPU or the real oracle build.
+"""
+import os
+import time
+
+import pytest
+
+import oracle
+import oracle_pins
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "fp8_oracle.c")
+
+MUTANTS = [
+    ("ties_away_from_zero", "double n = nearbyint(ldexp(a, mbits - e));",
+     "double n = round(ldexp(a, mbits - e));"),
+    ("truncating_encode", "double n = nearbyint(ldexp(a, mbits - e));",
+     "double n = trunc(ldexp(a, mbits - e));"),
+    ("fnuz_e4m3_bias", "return fmt == ORC_E4M3 ? 7 : 15;", "return fmt == ORC_E4M3 ? 8 : 15;"),
+    ("subnormals_flushed", "if (e < emin) e = emin;", "if (e < emin) return sign;"),
+    ("decode_subnormal_exponent", "v = ldexp((double)m, 1 - bias - mbits);",
+     "v = ldexp((double)m, -bias - mbits);"),
+    ("e5m2_inf_as_nan", "v = (m == 0) ? INFINITY : NAN;", "v = NAN;"),
+    ("no_saturation", "if (v > mx) v = mx;", ""),
+    ("multiply_by_scale", "float v = x / scale;", "float v = x * scale;"),
+    ("nan_sign_dropped", "return (uint8_t)(0x7F | (signbit(x) ? 0x80 : 0x00));",
+     "return (uint8_t)0x7F;"),
+    ("amax_keeps_sign", "uint32_t mag = f2u(x) & 0x7FFFFFFFu;", "uint32_t mag = f2u(x);"),
+    ("amax_not_accumulated", "uint32_t acc = f2u(*amax);\n  for (int64_t i = 0; i < n; ++i) {\n    float x",
+     "uint32_t acc = 0;\n  for (int64_t i = 0; i < n; ++i) {\n    float x"),
+    ("no_history_roll", "hist_out[h * n + t] = hist_in[(h - 1) * n + t];",
+     "hist_out[h * n + t] = hist_in[h * n + t];"),
+    ("new_amax_not_in_window", "for (int64_t h = 0; h < H; ++h) {\n        uint32_t b",
+     "for (int64_t h = 1; h < H; ++h) {\n        uint32_t b"),
+    ("select_from_old_history", "uint32_t b = f2u(hist_out[h * n + t]);",
+     "uint32_t b = f2u(hist_in[h * n + t]);"),
+    ("most_recent_is_max", "if (algo == ORC_AMAX_MOST_RECENT) {", "if (algo == 12345) {"),
+    ("margin_sign", "c = ldexpf(c, margin);", "c = ldexpf(c, -margin);"),
+    ("scale_inverted", "float c = sel / mx;", "float c = mx / sel;"),
+    ("scale_inv_from_amax", "scale_inv_out[t] = 1.0f / s;", "scale_inv_out[t] = mx / sel;"),
+    # (dropping only the guard on sel is equivalent: the guard on c then catches 0,
+    # inf and NaN; so the mistake planted is dropping the guard on the result)
+    ("no_keep_previous_guard", "if (isfinite(c) && c > 0.0f) s = c;", "s = c;"),
+    ("reset_ignored", "amax_out[t] = reset_amax ? 0.0f : amax[t];", "amax_out[t] = amax[t];"),
+    ("formats_swapped", "float mx = oracle_fp8_max(formats[t] ? ORC_E5M2 : ORC_E4M3);",
+     "float mx = oracle_fp8_max(formats[t] ? ORC_E4M3 : ORC_E5M2);"),
+    ("dequant_divides", "float y = oracle_fp8_decode(fmt, src[i]) * scale;",
+     "float y = oracle_fp8_decode(fmt, src[i]) / scale;"),
+    ("bf16_truncates", "double r = ldexp(nearbyint(ldexp(a, 7 - e)), e - 7);",
+     "double r = ldexp(trunc(ldexp(a, 7 - e)), e - 7);"),
+    ("dequant_nan_unsigned", "uint32_t nan_bits = 0x7FC00000u | ((uint32_t)(src[i] & 0x80) << 24);",
+     "uint32_t nan_bits = 0x7FC00000u;"),
+]
+
+# cheap pins first; a mutant stops at its first failing pin
+_ORDER = sorted(oracle_pins.ALL_PINS,
+                key=lambda p: p.__name__ in ("pin_quantize_exact_quotient",
+                                             "pin_encode_bruteforce_all_bf16"))
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_mutant_is_caught(tmp_path, name, old, new):
+    src = open(SRC).read()
+    assert src.count(old) == 1, "mutation site not found uniquely: %s" % name
+    mpath = tmp_path / ("mut_%s.c" % name)
+    mpath.write_text(src.replace(old, new))
+    lib = oracle.build(lib_path=str(tmp_path / ("lib_%s.so" % name)), src=str(mpath))
+    o = oracle.Oracle(lib)
+    caught = []
+    for pin in _ORDER:
+        try:
+            pin(o)
+        except AssertionError:
+            caught.append(pin.__name__)
+            break
+        except Exception as e:          # a crash in the mutant also counts as caught
+            caught.append("%s:%s" % (pin.__name__, type(e).__name__))
+            break
+    assert caught, "planted mistake %r passed every pin" % name
