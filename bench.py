@@ -1,0 +1,274 @@
+"""Benchmark of the FP8 delayed-scaling hot path on one MI355X.
+
+One step = one multi-tensor fused quantize+amax launch over every tensor of the
+workload (bf16 -> FP8 with the previous step's scale) followed by one batched
+amax_and_scale_update launch (history roll, amax selection, new scale/scale_inv,
+amax reset), on inputs already resident in HBM.  Default workload: the MLP at hidden
+4096 / ffn 16384 (activation (2048,4,4096), weights 4096x16384 and 16384x4096, all
+E4M3, history 16).  Prints one JSON line.
+
+Also measured in the same run: the batched update of 1152 tensors with history 1024
+(kernel time warm and cold, host wall time per call), a device-to-device copy as the
+achievable-bandwidth context, and the CPU oracle on the same step (cpu_baseline), whose
+output is compared byte for byte with the GPU's first step.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E, published
+METRIC = "fused quantize+amax GB/s & % HBM peak; µs per batched scale update"
+KERNEL_SOURCE = os.path.join(ROOT, "delayed_scaling_amax_amd", "csrc", "quantize_amax.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "quantize_amax_mlp_4096_traffic.txt")
+
+
+def log(msg):
+    print("[bench] " + msg, file=sys.stderr, flush=True)
+
+
+def kernel_hash() -> str:
+    h = hashlib.sha256()
+    for name in ("quantize_amax.hip", "device_common.h", "host_common.h"):
+        with open(os.path.join(ROOT, "delayed_scaling_amax_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per quantize launch from the committed rocprofv3 counter summary, or
+    None if absent, for another workload, or taken on a different kernel source."""
+    try:
+        kv = {}
+        with open(TRAFFIC_FILE) as f:
+            for line in f:
+                if "=" in line and not line.startswith("#"):
+                    k, v = line.split("=", 1)
+                    kv[k.strip()] = v.strip()
+        if kv.get("kernel_source_sha256_16") != kernel_hash() or kv.get("workload") != workload:
+            return None
+        return float(kv["hbm_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
+def alg_bytes_quantize(w) -> int:
+    """Algorithmic bytes of one quantize launch: read every source element, write one
+    FP8 byte per element, read each scale (4 B), read+write each amax (8 B)."""
+    return sum(int(t.data.nbytes) + int(t.data.size) + 12 for t in w.tensors)
+
+
+def alg_bytes_update(n: int, H: int) -> int:
+    """History read + in-place write, amax read (and reset write), scale read + write,
+    scale_inv write, format byte."""
+    return 2 * H * n * 4 + n * 4 * 2 + n * 4 * 2 + n * 4 + n
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="mlp_4096",
+                    choices=["single_1024", "mlp_4096", "grad_8192x16384", "mlp_12288"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--update-calls", type=int, default=200)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (the amax "
+              "all-reduce across replicas is described in the design notes, not built); "
+              "run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import delayed_scaling_amax_amd as d
+    import workloads
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    threads = workloads.default_threads()
+
+    # ------------------------------------------------------------ inputs in HBM
+    t0 = time.time()
+    w = workloads.make(args.workload, threads=threads)
+    log("generated %s (%d tensors, %d elements) in %.1fs" % (w.name, len(w.tensors), w.numel,
+                                                             time.time() - t0))
+    fmts = [0 if t.fmt == workloads.E4M3 else 1 for t in w.tensors]
+    n = len(w.tensors)
+    srcs = [torch.from_numpy(t.data.view(np.int16)).view(torch.bfloat16).to(dev)
+            for t in w.tensors]
+    dsts = [torch.empty(t.data.size, dtype=torch.uint8, device=dev) for t in w.tensors]
+    scale = torch.tensor(w.first_scale, dtype=torch.float32, device=dev)
+    scale_inv = torch.empty(n, dtype=torch.float32, device=dev)
+    amax = torch.zeros(n, dtype=torch.float32, device=dev)
+    hist = torch.zeros(w.history_len, n, dtype=torch.float32, device=dev)
+    fdev = torch.tensor(fmts, dtype=torch.uint8, device=dev)
+    entries = [(srcs[i], dsts[i], scale[i:i + 1], amax[i:i + 1], fmts[i]) for i in range(n)]
+
+    def quantize():
+        d.fp8_multi_quantize_amax(entries)
+
+    def update():
+        d.fp8_amax_and_scale_update(amax, hist, scale, scale_inv, fdev, reset_amax=True)
+
+    # first step (prior scale): kept on the host for the parity check against the oracle
+    quantize()
+    torch.cuda.synchronize()
+    first_codes = [x.cpu().numpy() for x in dsts]
+    first_amax = amax.cpu().numpy().copy()
+    update()
+
+    for _ in range(args.warmup):
+        quantize()
+        update()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for k in range(K):
+        ev[k][0].record()
+        quantize()
+        ev[k][1].record()
+        update()
+        ev[k][2].record()
+    torch.cuda.synchronize()
+    t_end = time.perf_counter()
+    q_ms = [ev[k][0].elapsed_time(ev[k][1]) for k in range(K)]
+    u_ms = [ev[k][1].elapsed_time(ev[k][2]) for k in range(K)]
+    ms_per_step = (t_end - t_start) * 1e3 / K
+    qbytes = alg_bytes_quantize(w)
+    ubytes = alg_bytes_update(n, w.history_len)
+    value = (qbytes + ubytes) / (ms_per_step * 1e-3) / 1e9
+    q_avg_us = 1e3 * float(np.mean(q_ms))
+    q_gbps = qbytes / (q_avg_us * 1e-6) / 1e9
+    log("step %.3f ms; quantize avg %.2f us (median %.2f) = %.1f GB/s; update avg %.2f us"
+        % (ms_per_step, q_avg_us, 1e3 * float(np.median(q_ms)), q_gbps,
+           1e3 * float(np.mean(u_ms))))
+
+    # ------------------------------------------------------------ batched update, 1152 tensors
+    uw = workloads.update_1152(threads=threads)
+    un, uH = uw.amax.size, uw.history_len
+    u_amax = torch.from_numpy(uw.amax).to(dev)
+    u_hist = torch.from_numpy(uw.hist).to(dev)
+    u_scale = torch.from_numpy(uw.scale).to(dev)
+    u_sinv = torch.empty_like(u_scale)
+    u_fmt = torch.tensor([0 if f == workloads.E4M3 else 1 for f in uw.formats],
+                         dtype=torch.uint8, device=dev)
+
+    def update_1152():
+        d.fp8_amax_and_scale_update(u_amax, u_hist, u_scale, u_sinv, u_fmt, margin=0)
+
+    for _ in range(10):
+        update_1152()
+    torch.cuda.synchronize()
+    C = args.update_calls
+    uev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(C)]
+    for a, b in uev:
+        a.record()
+        update_1152()
+        b.record()
+    torch.cuda.synchronize()
+    warm_us = 1e3 * float(np.mean([a.elapsed_time(b) for a, b in uev]))
+    t0 = time.perf_counter()
+    for _ in range(C):
+        update_1152()
+    torch.cuda.synchronize()
+    wall_us = (time.perf_counter() - t0) * 1e6 / C
+    flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)  # 1 GiB > L2 + MALL
+    cold = []
+    for _ in range(20):
+        flush.fill_(1.0)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        update_1152()
+        b.record()
+        torch.cuda.synchronize()
+        cold.append(a.elapsed_time(b))
+    cold_us = 1e3 * float(np.mean(cold))
+    del flush
+    log("update 1152x%d: warm %.2f us, cold %.2f us, host wall %.2f us/call"
+        % (uH, warm_us, cold_us, wall_us))
+
+    # ------------------------------------------------------------ copy context
+    cbuf = torch.empty(1 << 27, dtype=torch.float32, device=dev)  # 512 MiB
+    cdst = torch.empty_like(cbuf)
+    for _ in range(3):
+        cdst.copy_(cbuf)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(10):
+        cdst.copy_(cbuf)
+    b.record()
+    torch.cuda.synchronize()
+    copy_gbps = 2 * cbuf.numel() * 4 * 10 / (a.elapsed_time(b) * 1e-3) / 1e9
+    del cbuf, cdst
+
+    traffic = measured_traffic(w.name)
+    out = {
+        "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
+        "steps": K, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic (seeded numpy PCG64, seed 12; shapes/distributions of the workload)",
+        "config": {"workload": w.name, "description": w.description, "tensors": n,
+                   "elements": w.numel, "history_len": w.history_len,
+                   "formats": [t.fmt for t in w.tensors], "src_dtype": "bf16"},
+        "quantize_amax": {"avg_us": round(q_avg_us, 3),
+                          "median_us": round(1e3 * float(np.median(q_ms)), 3),
+                          "gbps": round(q_gbps, 1), "pct_hbm_peak": round(100 * q_gbps /
+                                                                          PEAK_HBM_GBPS, 2),
+                          "alg_bytes": qbytes},
+        "scale_update_us": {"workload": "update_1152 (96 layers x 4 linears x 3 tensors, "
+                                        "history 1024, margin 0)",
+                            "kernel_warm_us": round(warm_us, 3),
+                            "kernel_cold_us": round(cold_us, 3),
+                            "host_wall_us_per_call": round(wall_us, 3),
+                            "alg_bytes": alg_bytes_update(un, uH),
+                            "step_update_us": round(1e3 * float(np.mean(u_ms)), 3)},
+        "copy_d2d_gbps": round(copy_gbps, 1),
+        "roofline": {"bound": "hbm", "achieved": round(q_gbps, 1), "peak": PEAK_HBM_GBPS,
+                     "unit": "GB/s", "frac": round(q_gbps / PEAK_HBM_GBPS, 4),
+                     "traffic": traffic},
+    }
+
+    # ------------------------------------------------------------ CPU oracle baseline
+    if not args.no_cpu_baseline:
+        import oracle
+        orc = oracle.load()
+        t0 = time.perf_counter()
+        o_amax = np.zeros(n, np.float32)
+        same = True
+        for i, t in enumerate(w.tensors):
+            codes, o_amax[i] = orc.quantize_amax(t.data, fmts[i], float(w.first_scale[i]),
+                                                 threads=threads)
+            same &= bool(np.array_equal(codes.reshape(-1), first_codes[i]))
+            del codes
+        orc.amax_and_scale_update(o_amax, np.zeros((w.history_len, n), np.float32),
+                                  np.asarray(w.first_scale, np.float32),
+                                  np.array(fmts, np.uint8), reset_amax=True)
+        dt = time.perf_counter() - t0
+        same &= bool((o_amax.view(np.uint32) == first_amax.view(np.uint32)).all())
+        out["cpu_baseline"] = {"value": round((qbytes + ubytes) / dt / 1e9, 3), "unit": "GB/s",
+                               "cores": threads, "kind": "oracle",
+                               "sample": "one full step of %s (all %d elements, first step "
+                                         "with the prior scale), %d threads over contiguous "
+                                         "chunks, %.1f s" % (w.name, w.numel, threads, dt)}
+        out["parity_first_step"] = "bit-exact" if same else "MISMATCH"
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,48 @@
+// device_common.h -- small gfx950 device helpers shared by the libfp8q kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fp8q {
+
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kE4M3Max = 448.0f;    // largest finite float8_e4m3fn
+constexpr float kE5M2Max = 57344.0f;  // largest finite float8_e5m2
+
+__device__ __forceinline__ float as_float(uint32_t u) { return __uint_as_float(u); }
+__device__ __forceinline__ uint32_t as_uint(float f) { return __float_as_uint(f); }
+
+// Lane-wise unsigned max of the two 16-bit halves (one v_pk_max_u16).
+__device__ __forceinline__ uint32_t pk_max_u16(uint32_t a, uint32_t b) {
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(u16x2, a),
+                                                                __builtin_bit_cast(u16x2, b)));
+}
+
+// Max over the 64 lanes of a wavefront (butterfly through ds_swizzle/bpermute).
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    uint32_t o = __shfl_xor(v, off, 64);
+    v = v > o ? v : o;
+  }
+  return v;
+}
+
+// Block-wide max of one value per thread; every thread gets the result.  `red`
+// holds one slot per wavefront.  Contains two barriers: all threads must call it.
+template <int kBlock>
+__device__ __forceinline__ uint32_t block_max_u32(uint32_t v, uint32_t* red) {
+  v = wave_max_u32(v);
+  const int wave = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) red[wave] = v;
+  __syncthreads();
+  uint32_t r = red[0];
+#pragma unroll
+  for (int w = 1; w < kBlock / 64; ++w) r = r > red[w] ? r : red[w];
+  __syncthreads();  // red may be reused right after
+  return r;
+}
+
+}  // namespace fp8q

@@ -1,0 +1,468 @@
+// quantize_amax.hip -- fused FP8 quantize + amax over one or many tensors, one launch.
+//
+// What it computes ("User Guide on Native XLA-FP8", section "JAX"; "Fusion of Fp8
+// quantization and amax reduction kernels", openxla/xla issue 7432): for every element
+// x of a tensor, code = FP8(saturate(RN32(x / scale))) with the scale of the previous
+// step, and in the same pass amax = max(amax, max|x|).
+//
+// Design (gfx950, HBM-bound at 3 bytes/element for bf16 -> fp8):
+//  * A unit is 8 elements.  A tensor's units are its aligned body, read as 16-byte
+//    bf16x8 loads (8-byte code stores), then its unaligned head/tail elements ("scalar
+//    units").  Units are grouped into chunks of kQChunk that never straddle tensors;
+//    all tensors' chunks form one chunk space.  The grid is persistent (a few blocks
+//    per CU) and walks that space grid-stride, so at any moment the whole chip streams
+//    one contiguous window of memory; a block issues one amax atomic per tensor.
+//  * amax is an integer max: |x| is the bit pattern with the sign cleared (bf16: two
+//    halves at once with v_pk_max_u16), reduced lane -> wavefront -> block, then one
+//    atomicMax on the binary32 bit pattern.  Non-negative floats order like their
+//    bits, NaN above inf, so the result does not depend on atomic order.
+//  * Division.  r = RN(1/scale) once per tensor (IEEE).  Per element the quotient is
+//    q0 = RN(x*r) corrected by Markstein's step (q = q0 - (q0*s - x)*r as two FMAs;
+//    twice for fp32 sources), which equals the IEEE quotient while scale is in
+//    [2^-80, 2^125] and |x| < scale*2^126 -- the host sweep in the tests covers every
+//    bf16 mantissa against every scale mantissa.  A group of 8 with any element
+//    outside that window (or inf/NaN) takes the IEEE divide per element.
+//  * Saturation with v_med3_f32 against +-FP8_MAX, then the native OCP convert
+//    v_cvt_pk_fp8_f32 / v_cvt_pk_bf8_f32 (round to nearest even).  NaN quotients
+//    (only possible on the IEEE path) are written as 0x7F with the sign of x.
+#include "device_common.h"
+#include "host_common.h"
+
+namespace fp8q {
+
+// Launch shape (measured on MI355X; overridable at build time for tuning sweeps).
+#ifndef FP8Q_Q_BLOCK
+#define FP8Q_Q_BLOCK 256
+#endif
+#ifndef FP8Q_Q_UNROLL
+#define FP8Q_Q_UNROLL 8
+#endif
+#ifndef FP8Q_Q_BLOCKS_PER_CU
+#define FP8Q_Q_BLOCKS_PER_CU 4
+#endif
+#ifndef FP8Q_Q_NT  // bit 0: non-temporal loads, bit 1: non-temporal stores
+#define FP8Q_Q_NT 1
+#endif
+constexpr int kQBlock = FP8Q_Q_BLOCK;             // threads per block
+constexpr int kQUnroll = FP8Q_Q_UNROLL;           // 8-element groups in flight per thread
+constexpr int kQMaxEntries = 32;                  // tensors per launch (kernel-argument table)
+constexpr int kQBlocksPerCU = FP8Q_Q_BLOCKS_PER_CU;  // persistent grid size per CU
+constexpr int kQChunk = kQBlock * kQUnroll;       // units (8-element groups) per chunk
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint4 load16(const uint4* p) {
+  u32x4 v;
+  if constexpr (FP8Q_Q_NT & 1) v = __builtin_nontemporal_load((const u32x4*)p);
+  else v = *(const u32x4*)p;
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
+__device__ __forceinline__ void store8(uint2* p, uint2 o) {
+  u32x2 v = {o.x, o.y};
+  if constexpr (FP8Q_Q_NT & 2) __builtin_nontemporal_store(v, (u32x2*)p);
+  else *(u32x2*)p = v;
+}
+
+struct QEntry {
+  const void* src;
+  uint8_t* dst;
+  const float* scale;
+  uint32_t* amax;
+  int64_t cbegin;   // first chunk of this tensor in the launch's chunk space
+  int64_t n_chunks; // ceil(n_units / kQChunk)
+  int64_t n_units;  // vector groups + scalar units
+  int64_t n_vec;    // 8-element groups at [head, head + 8*n_vec), 16B/8B aligned
+  int64_t head;     // elements before the first vector group
+  int64_t numel;
+  int32_t dtype;
+  int32_t fmt;
+};
+
+struct QTable {
+  QEntry e[kQMaxEntries];
+  int64_t total_chunks;
+  int32_t n;
+};
+
+// ---------------------------------------------------------------- element math
+template <int kFmt>
+__device__ __forceinline__ float saturate(float q) {
+  constexpr float m = kFmt == FP8Q_E4M3 ? kE4M3Max : kE5M2Max;
+  return __builtin_amdgcn_fmed3f(q, -m, m);
+}
+
+template <int kFmt>
+__device__ __forceinline__ uint32_t pack4(float c0, float c1, float c2, float c3) {
+  // the first convert fills bytes 0-1 and the second bytes 2-3, so the initial
+  // contents of the word are irrelevant: seed it with a register already live
+  int w = __builtin_bit_cast(int, c0);
+  if constexpr (kFmt == FP8Q_E4M3) {
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(c0, c1, w, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(c2, c3, w, true);
+  } else {
+    w = __builtin_amdgcn_cvt_pk_bf8_f32(c0, c1, w, false);
+    w = __builtin_amdgcn_cvt_pk_bf8_f32(c2, c3, w, true);
+  }
+  return (uint32_t)w;
+}
+
+// Quotient for bf16 x inside the window: one Markstein correction.
+__device__ __forceinline__ float div_corrected1(float x, float s, float r) {
+  float q0 = x * r;
+  float e = __builtin_fmaf(q0, s, -x);
+  return __builtin_fmaf(-e, r, q0);
+}
+
+// Quotient for fp32 x inside the window: two corrections (the first makes the
+// quotient faithful, the second rounds it correctly).
+__device__ __forceinline__ float div_corrected2(float x, float s, float r) {
+  float q0 = x * r;
+  float e0 = __builtin_fmaf(q0, s, -x);
+  float q1 = __builtin_fmaf(-e0, r, q0);
+  float e1 = __builtin_fmaf(q1, s, -x);
+  return __builtin_fmaf(-e1, r, q1);
+}
+
+// Inside the window an element with |x| >= xlim (magnitude bits) is +-inf, NaN, or
+// finite with |x/s| >= 2^125: its code is fixed without any division -- NaN gives 0x7F,
+// everything else saturates to the largest finite code -- with the sign bit of x.
+template <int kFmt>
+__device__ __forceinline__ uint32_t fixed_code(uint32_t mag, uint32_t inf_bits, uint32_t sign) {
+  constexpr uint32_t kMaxCode = kFmt == FP8Q_E4M3 ? 0x7Eu : 0x7Bu;
+  return (mag > inf_bits ? 0x7Fu : kMaxCode) | sign;
+}
+
+// Replace byte k of the 8 codes wherever element k has magnitude >= xlim.  `mag[k]`
+// and `sign[k]` (0 or 0x80) are in the source's own bit layout; inf_bits likewise.
+template <int kFmt>
+__device__ __forceinline__ uint2 patch_codes(uint2 codes, const uint32_t (&mag)[8],
+                                             const uint32_t (&sign)[8], uint32_t xlim,
+                                             uint32_t inf_bits) {
+  uint32_t w[2] = {codes.x, codes.y};
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const int sh = 8 * (k & 3);
+    const uint32_t fixed = (w[k >> 2] & ~(0xFFu << sh)) |
+                           (fixed_code<kFmt>(mag[k], inf_bits, sign[k]) << sh);
+    w[k >> 2] = mag[k] >= xlim ? fixed : w[k >> 2];
+  }
+  return make_uint2(w[0], w[1]);
+}
+
+// One element through the IEEE divide: any x, any scale (head/tail elements and
+// tensors whose scale lies outside the window).
+template <int kFmt>
+__device__ __forceinline__ uint32_t code_ieee(float x, float s) {
+  const float v = x / s;
+  const float c = saturate<kFmt>(v);
+  const uint32_t code = pack4<kFmt>(c, c, c, c) & 0xFFu;
+  return (v != v) ? (0x7Fu | ((as_uint(x) >> 24) & 0x80u)) : code;
+}
+
+// ---------------------------------------------------------------- 8-element groups
+// bf16: w holds 8 bf16 values; acc keeps the packed 16-bit magnitude max.
+template <int kFmt>
+__device__ __forceinline__ uint2 quant8_bf16(uint4 w, float s, float r, uint32_t xlim,
+                                             uint32_t& acc) {
+  const uint32_t m = pk_max_u16(pk_max_u16(w.x & 0x7FFF7FFFu, w.y & 0x7FFF7FFFu),
+                                pk_max_u16(w.z & 0x7FFF7FFFu, w.w & 0x7FFF7FFFu));
+  acc = pk_max_u16(acc, m);
+  const uint32_t mlo = m & 0xFFFFu, mhi = m >> 16;
+  const uint32_t mm = mlo > mhi ? mlo : mhi;
+  const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+  float c[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const float x = as_float((k & 1) ? (u[k >> 1] & 0xFFFF0000u) : (u[k >> 1] << 16));
+    c[k] = saturate<kFmt>(div_corrected1(x, s, r));
+  }
+  uint2 out = make_uint2(pack4<kFmt>(c[0], c[1], c[2], c[3]), pack4<kFmt>(c[4], c[5], c[6], c[7]));
+  if (mm >= xlim) {  // rare: inf/NaN or a quotient far beyond the FP8 range
+    uint32_t mag[8], sign[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const uint32_t h = (k & 1) ? (u[k >> 1] >> 16) : (u[k >> 1] & 0xFFFFu);
+      mag[k] = h & 0x7FFFu;
+      sign[k] = (h >> 8) & 0x80u;
+    }
+    out = patch_codes<kFmt>(out, mag, sign, xlim, 0x7F80u);
+  }
+  return out;
+}
+
+// fp32: lo/hi hold 8 floats; acc keeps the 32-bit magnitude max.
+template <int kFmt>
+__device__ __forceinline__ uint2 quant8_f32(uint4 lo, uint4 hi, float s, float r, uint32_t xlim,
+                                            uint32_t& acc) {
+  const uint32_t u[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+  uint32_t m = 0;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const uint32_t a = u[k] & 0x7FFFFFFFu;
+    m = m > a ? m : a;
+  }
+  acc = acc > m ? acc : m;
+  float c[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) c[k] = saturate<kFmt>(div_corrected2(as_float(u[k]), s, r));
+  uint2 out = make_uint2(pack4<kFmt>(c[0], c[1], c[2], c[3]), pack4<kFmt>(c[4], c[5], c[6], c[7]));
+  if (m >= xlim) {
+    uint32_t mag[8], sign[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      mag[k] = u[k] & 0x7FFFFFFFu;
+      sign[k] = (u[k] >> 24) & 0x80u;
+    }
+    out = patch_codes<kFmt>(out, mag, sign, xlim, 0x7F800000u);
+  }
+  return out;
+}
+
+// ---------------------------------------------------------------- element-wise units
+// Units [g0, g1) of a tensor, one element at a time through the IEEE divide.  Vector
+// unit g holds elements head + 8g .. head + 8g + 7; scalar element j (unit n_vec +
+// j/8) is tensor element j (head part) or j + 8*n_vec (tail part).
+template <bool kBF16, int kFmt>
+__device__ __forceinline__ void elementwise_units(const void* __restrict__ src,
+                                                  uint8_t* __restrict__ dst, int64_t head,
+                                                  int64_t n_vec, int64_t numel, int64_t g0,
+                                                  int64_t g1, float s, uint32_t& acc) {
+  const int64_t n_scalar = numel - 8 * n_vec;
+  for (int64_t g = g0 + threadIdx.x; g < g1; g += kQBlock) {
+    for (int q = 0; q < 8; ++q) {
+      int64_t i;
+      if (g < n_vec) {
+        i = head + 8 * g + q;
+      } else {
+        const int64_t j = (g - n_vec) * 8 + q;
+        if (j >= n_scalar) break;
+        i = j < head ? j : j + 8 * n_vec;
+      }
+      float x;
+      if constexpr (kBF16) {
+        const uint32_t b = ((const uint16_t*)src)[i];
+        x = as_float(b << 16);
+        acc = pk_max_u16(acc, b & 0x7FFFu);  // low half of the packed accumulator
+      } else {
+        x = ((const float*)src)[i];
+        const uint32_t mag = as_uint(x) & 0x7FFFFFFFu;
+        acc = acc > mag ? acc : mag;
+      }
+      dst[i] = (uint8_t)code_ieee<kFmt>(x, s);
+    }
+  }
+}
+
+// ---------------------------------------------------------------- one chunk of a tensor
+// A chunk is kQChunk consecutive units of one tensor.  Full chunks of the aligned body
+// issue all their 16-byte loads before any use; the last chunk of a tensor (partial,
+// or reaching into the scalar head/tail) runs element-group by element-group.
+template <bool kBF16, int kFmt>
+__device__ __forceinline__ void process_chunk(const void* __restrict__ src, uint8_t* __restrict__ dst,
+                                              int64_t head, int64_t n_vec, int64_t numel,
+                                              int64_t n_units, int64_t k, float s, float r,
+                                              uint32_t xlim, uint32_t& acc) {
+  constexpr int esz = kBF16 ? 2 : 4;
+  constexpr int kL = kBF16 ? 1 : 2;                    // 16-byte loads per group
+  constexpr int kU = kBF16 ? kQUnroll : kQUnroll / 2;  // groups per pass, same bytes in flight
+  const uint4* __restrict__ in = (const uint4*)((const char*)src + head * esz);
+  uint2* __restrict__ out = (uint2*)(dst + head);
+  const int64_t u0 = k * kQChunk;
+  const int64_t u1 = min(u0 + (int64_t)kQChunk, n_units);
+  if (u0 + kQChunk <= n_vec) {
+#pragma unroll
+    for (int pass = 0; pass < kQUnroll / kU; ++pass) {
+      const int64_t g = u0 + (int64_t)pass * kU * kQBlock + threadIdx.x;
+      uint4 w[kU][kL];
+#pragma unroll
+      for (int u = 0; u < kU; ++u)
+#pragma unroll
+        for (int l = 0; l < kL; ++l) w[u][l] = load16(in + (g + u * kQBlock) * kL + l);
+      // keep every load of the pass ahead of the first use (memory-level parallelism)
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        uint2 o;
+        if constexpr (kBF16) o = quant8_bf16<kFmt>(w[u][0], s, r, xlim, acc);
+        else o = quant8_f32<kFmt>(w[u][0], w[u][kL - 1], s, r, xlim, acc);
+        store8(out + g + u * kQBlock, o);
+      }
+    }
+    return;
+  }
+  const int64_t vhi = u1 < n_vec ? u1 : n_vec;
+  for (int64_t g = u0 + threadIdx.x; g < vhi; g += kQBlock) {
+    uint2 o;
+    if constexpr (kBF16) o = quant8_bf16<kFmt>(load16(in + g), s, r, xlim, acc);
+    else o = quant8_f32<kFmt>(load16(in + 2 * g), load16(in + 2 * g + 1), s, r, xlim, acc);
+    store8(out + g, o);
+  }
+  elementwise_units<kBF16, kFmt>(src, dst, head, n_vec, numel, u0 > n_vec ? u0 : n_vec, u1, s,
+                                 acc);
+}
+
+// All chunks of tensor e that this block owns: [c, c_end) step c_step, capped at the
+// tensor's last chunk.  Returns the next chunk index.
+template <bool kBF16, int kFmt>
+__device__ __forceinline__ int64_t tensor_chunks(const QEntry& e, int64_t c, int64_t c_end,
+                                                 int64_t c_step, uint32_t& acc) {
+  const float s = *e.scale;
+  // per-tensor constants of the Markstein window (uniform)
+  const float r = 1.0f / s;
+  const bool window = (s >= 0x1p-80f) && (s <= 0x1p125f);
+  const uint32_t lim = as_uint(s * 0x1p126f);  // +inf when s >= 4
+  const uint32_t xlim = kBF16 ? min(lim >> 16, 0x7F80u) : min(lim, 0x7F800000u);
+  const int64_t stop = min(c_end, e.cbegin + e.n_chunks);
+  if (window) {
+    for (; c < stop; c += c_step)
+      process_chunk<kBF16, kFmt>(e.src, e.dst, e.head, e.n_vec, e.numel, e.n_units,
+                                 c - e.cbegin, s, r, xlim, acc);
+  } else {  // scale outside the window (tiny, huge, zero, negative, inf or NaN)
+    for (; c < stop; c += c_step) {
+      const int64_t u0 = (c - e.cbegin) * kQChunk;
+      const int64_t u1 = min(u0 + (int64_t)kQChunk, e.n_units);
+      elementwise_units<kBF16, kFmt>(e.src, e.dst, e.head, e.n_vec, e.numel, u0, u1, s, acc);
+    }
+  }
+  return c;
+}
+
+// Chunk schedule across the grid: 1 = grid-stride (block b takes chunks b, b+G, ...:
+// the whole grid streams one window of memory at a time), 0 = contiguous ranges.
+#ifndef FP8Q_Q_SCHEDULE
+#define FP8Q_Q_SCHEDULE 1
+#endif
+
+// kSrc: bit 0 = the table holds bf16 sources, bit 1 = fp32 sources.  The bf16-only
+// instance (the common case) keeps its register budget to the bf16 path.
+template <int kSrc>
+__global__ __launch_bounds__(kQBlock) void quantize_amax_kernel(const QTable tab) {
+  __shared__ uint32_t red[kQBlock / 64];
+  const int64_t nc = tab.total_chunks;
+#if FP8Q_Q_SCHEDULE == 1
+  int64_t c = blockIdx.x;
+  const int64_t c_end = nc, c_step = gridDim.x;
+#else
+  int64_t c = nc * blockIdx.x / gridDim.x;
+  const int64_t c_end = nc * (blockIdx.x + 1) / gridDim.x, c_step = 1;
+#endif
+  int t = 0;
+  while (c < c_end) {
+    while (c >= tab.e[t].cbegin + tab.e[t].n_chunks) ++t;  // chunks never straddle tensors
+    const QEntry& e = tab.e[t];
+    uint32_t acc = 0;
+    const int kind = e.dtype * 2 + e.fmt;  // uniform branch
+    if ((kSrc & 1) && kind == FP8Q_BF16 * 2 + FP8Q_E4M3)
+      c = tensor_chunks<true, FP8Q_E4M3>(e, c, c_end, c_step, acc);
+    else if ((kSrc & 1) && kind == FP8Q_BF16 * 2 + FP8Q_E5M2)
+      c = tensor_chunks<true, FP8Q_E5M2>(e, c, c_end, c_step, acc);
+    else if ((kSrc & 2) && kind == FP8Q_F32 * 2 + FP8Q_E4M3)
+      c = tensor_chunks<false, FP8Q_E4M3>(e, c, c_end, c_step, acc);
+    else if (kSrc & 2)
+      c = tensor_chunks<false, FP8Q_E5M2>(e, c, c_end, c_step, acc);
+    uint32_t m32 = acc;
+    if (e.dtype == FP8Q_BF16) {
+      const uint32_t lo = acc & 0xFFFFu, hi = acc >> 16;
+      m32 = (lo > hi ? lo : hi) << 16;
+    }
+    m32 = block_max_u32<kQBlock>(m32, red);
+    if (threadIdx.x == 0 && m32 != 0) atomicMax(e.amax, m32);
+  }
+}
+
+// ---------------------------------------------------------------- host side
+static int validate_entry(const fp8q_tensor& t) {
+  if (t.numel < 0) return FP8Q_EINVAL;
+  if (t.src_dtype != FP8Q_BF16 && t.src_dtype != FP8Q_F32) return FP8Q_EINVAL;
+  if (t.format != FP8Q_E4M3 && t.format != FP8Q_E5M2) return FP8Q_EINVAL;
+  if (t.scale == nullptr || t.amax == nullptr) return FP8Q_EINVAL;
+  if (t.numel > 0 && (t.src == nullptr || t.dst == nullptr)) return FP8Q_EINVAL;
+  return FP8Q_OK;
+}
+
+// Split one tensor into aligned body and scalar head/tail.
+static void plan_entry(const fp8q_tensor& t, QEntry* e) {
+  const int64_t esz = t.src_dtype == FP8Q_BF16 ? 2 : 4;
+  const uintptr_t s = (uintptr_t)t.src, d = (uintptr_t)t.dst;
+  int64_t head = -1;
+  for (int64_t h = 0; h < 8; ++h)
+    if ((s + h * esz) % 16 == 0 && (d + h) % 8 == 0) {
+      head = h;
+      break;
+    }
+  e->src = t.src;
+  e->dst = t.dst;
+  e->scale = t.scale;
+  e->amax = (uint32_t*)t.amax;
+  e->numel = t.numel;
+  e->dtype = t.src_dtype;
+  e->fmt = t.format;
+  if (head < 0 || t.numel < head + 8) {  // no aligned body: all elements scalar
+    e->head = t.numel;
+    e->n_vec = 0;
+  } else {
+    e->head = head;
+    e->n_vec = (t.numel - head) / 8;
+  }
+  e->n_units = e->n_vec + ceil_div(t.numel - 8 * e->n_vec, 8);
+  e->n_chunks = ceil_div(e->n_units, kQChunk);
+}
+
+static int launch_table(QTable* tab, hipStream_t stream) {
+  if (tab->total_chunks == 0) return FP8Q_OK;
+  int cus = 0;
+  int st = current_device_cus(&cus);
+  if (st != FP8Q_OK) return st;
+  const int64_t max_blocks = (int64_t)cus * kQBlocksPerCU;
+  int64_t blocks = tab->total_chunks;
+  if (blocks > max_blocks) blocks = max_blocks;
+  if (blocks < 1) blocks = 1;
+  int src_kinds = 0;
+  for (int i = 0; i < tab->n; ++i) src_kinds |= tab->e[i].dtype == FP8Q_BF16 ? 1 : 2;
+  const void* fn = src_kinds == 1   ? (const void*)quantize_amax_kernel<1>
+                   : src_kinds == 2 ? (const void*)quantize_amax_kernel<2>
+                                    : (const void*)quantize_amax_kernel<3>;
+  void* args[] = {tab};
+  return launch_status(hipLaunchKernel(fn, dim3((unsigned)blocks), dim3(kQBlock), args, 0, stream));
+}
+
+}  // namespace fp8q
+
+using namespace fp8q;
+
+extern "C" int fp8_multi_quantize_amax(const fp8q_tensor* tensors, int n, void* stream) {
+  if (n < 0 || (n > 0 && tensors == nullptr)) return FP8Q_EINVAL;
+  for (int i = 0; i < n; ++i) {
+    int st = validate_entry(tensors[i]);
+    if (st != FP8Q_OK) return st;
+  }
+  for (int base = 0; base < n; base += kQMaxEntries) {
+    QTable tab;
+    tab.n = 0;
+    tab.total_chunks = 0;
+    for (int i = base; i < n && i < base + kQMaxEntries; ++i) {
+      QEntry& e = tab.e[tab.n++];
+      plan_entry(tensors[i], &e);
+      e.cbegin = tab.total_chunks;
+      tab.total_chunks += e.n_chunks;
+    }
+    int st = launch_table(&tab, (hipStream_t)stream);
+    if (st != FP8Q_OK) return st;
+  }
+  return FP8Q_OK;
+}
+
+extern "C" int fp8_quantize_amax(const void* src, int src_dtype, uint8_t* dst, int64_t numel,
+                                 int format, const float* scale, float* amax, void* stream) {
+  fp8q_tensor t;
+  t.src = src;
+  t.dst = dst;
+  t.numel = numel;
+  t.src_dtype = src_dtype;
+  t.format = format;
+  t.scale = scale;
+  t.amax = amax;
+  return fp8_multi_quantize_amax(&t, 1, stream);
+}

@@ -1,0 +1,174 @@
+// scale_update.hip -- batched delayed-scaling update of n tensors in one launch.
+//
+// What it computes ("Implement fused kernel for FP8 scale update", TransformerEngine
+// PR 593: the history roll, the amax selection and the scale computation fused into
+// one in-place kernel; "User Guide on Native XLA-FP8", section "JAX": scale =
+// amax / FP8_MAX; "Gradient accumulation of FP8 params": FP8 meta combines with max):
+//   hist[h][t] <- hist[h-1][t] (h = H-1..1, oldest row dropped), hist[0][t] <- amax[t]
+//   sel = max_h hist[h][t] by bit pattern (or amax[t] for most-recent)
+//   scale[t] = RN32(sel / FP8_MAX) * 2^margin if that is finite and > 0, else kept
+//   scale_inv[t] = RN32(1 / scale[t]);  amax[t] = 0 if reset_amax
+//
+// Layout and schedule.  hist is [H][n] row-major, so one history row of kCols adjacent
+// tensors is one kCols*4-byte vector.  A block owns kCols tensors (columns) and all H
+// rows, so the in-place roll never races with another block: each thread loads its
+// rows into registers, a barrier separates every load of a chunk from every store,
+// and the stores go one row down.  Chunks of rows run from the oldest row upward, so
+// a chunk's stores only overwrite rows that were already loaded.  The per-tensor
+// inputs (amax, scale, format) are fetched at kernel start, alongside the history,
+// so the update costs one memory round trip.  Blocks with the same blockIdx % 8 land
+// on the same XCD; they get adjacent column groups so the lines they share stay in
+// one L2.
+#include "device_common.h"
+#include "host_common.h"
+
+namespace fp8q {
+
+#ifndef FP8Q_U_BLOCK
+#define FP8Q_U_BLOCK 256
+#endif
+#ifndef FP8Q_U_COLS
+#define FP8Q_U_COLS 4
+#endif
+#ifndef FP8Q_U_ROWS
+#define FP8Q_U_ROWS 4
+#endif
+constexpr int kUBlock = FP8Q_U_BLOCK;
+constexpr int kUCols = FP8Q_U_COLS;          // tensors per block (1, 2 or 4)
+constexpr int kURowsPerThread = FP8Q_U_ROWS;
+constexpr int kUChunk = kUBlock * kURowsPerThread;  // history rows per chunk
+
+typedef uint32_t RowVec __attribute__((ext_vector_type(kUCols)));  // one history row segment
+
+template <bool kVec>
+__device__ __forceinline__ void load_row(const float* __restrict__ row, int ncols,
+                                         uint32_t (&v)[kUCols]) {
+  if constexpr (kVec) {
+    const RowVec q = *(const RowVec*)row;
+#pragma unroll
+    for (int c = 0; c < kUCols; ++c) v[c] = q[c];
+  } else {
+#pragma unroll
+    for (int c = 0; c < kUCols; ++c) v[c] = c < ncols ? as_uint(row[c]) : 0u;
+  }
+}
+
+template <bool kVec>
+__device__ __forceinline__ void store_row(float* __restrict__ row, int ncols,
+                                          const uint32_t (&v)[kUCols]) {
+  if constexpr (kVec) {
+    RowVec q;
+#pragma unroll
+    for (int c = 0; c < kUCols; ++c) q[c] = v[c];
+    *(RowVec*)row = q;
+  } else {
+#pragma unroll
+    for (int c = 0; c < kUCols; ++c)
+      if (c < ncols) row[c] = as_float(v[c]);
+  }
+}
+
+template <bool kVec>
+__global__ __launch_bounds__(kUBlock) void amax_and_scale_update_kernel(
+    float* __restrict__ amax, float* __restrict__ hist, float* __restrict__ scale,
+    float* __restrict__ scale_inv, const uint8_t* __restrict__ formats, int64_t n, int64_t H,
+    int algo, int margin, int reset_amax, int64_t groups, int64_t groups_per_xcd) {
+  __shared__ uint32_t red[kUCols][kUBlock / 64];
+  const int64_t g = (int64_t)(blockIdx.x % 8) * groups_per_xcd + blockIdx.x / 8;
+  if (g >= groups) return;  // whole block, before any barrier
+  const int64_t c0 = g * kUCols;
+  const int ncols = (int)min((int64_t)kUCols, n - c0);
+  const int tid = threadIdx.x;
+
+  // per-tensor inputs, fetched now so their latency overlaps the history loads
+  float a_in = 0.0f, s_old = 0.0f;
+  uint32_t fmt = 0;
+  if (tid < ncols) {
+    a_in = amax[c0 + tid];
+    s_old = scale[c0 + tid];
+    fmt = formats[c0 + tid];
+  }
+
+  uint32_t m[kUCols];
+#pragma unroll
+  for (int c = 0; c < kUCols; ++c) m[c] = 0u;
+  // destination rows d in [1, H) take source row d-1; oldest chunk first
+  for (int64_t d_hi = H; d_hi > 1; d_hi -= kUChunk) {
+    const int64_t d_lo = d_hi - kUChunk > 1 ? d_hi - kUChunk : 1;
+    uint32_t v[kURowsPerThread][kUCols];
+#pragma unroll
+    for (int k = 0; k < kURowsPerThread; ++k) {
+      const int64_t d = d_lo + tid + (int64_t)k * kUBlock;
+      if (d < d_hi) load_row<kVec>(hist + (d - 1) * n + c0, ncols, v[k]);
+    }
+#pragma unroll
+    for (int k = 0; k < kURowsPerThread; ++k) {
+      const int64_t d = d_lo + tid + (int64_t)k * kUBlock;
+      if (d < d_hi)
+#pragma unroll
+        for (int c = 0; c < kUCols; ++c) m[c] = m[c] > v[k][c] ? m[c] : v[k][c];
+    }
+    __syncthreads();  // every load of this chunk (values already in registers) ...
+#pragma unroll
+    for (int k = 0; k < kURowsPerThread; ++k) {  // ... before any store one row down
+      const int64_t d = d_lo + tid + (int64_t)k * kUBlock;
+      if (d < d_hi) store_row<kVec>(hist + d * n + c0, ncols, v[k]);
+    }
+  }
+
+  // block max per column over the rolled window (row 0 = the new amax, added below)
+#pragma unroll
+  for (int c = 0; c < kUCols; ++c) {
+    const uint32_t w = wave_max_u32(m[c]);
+    if ((tid & 63) == 0) red[c][tid >> 6] = w;
+  }
+  __syncthreads();
+  if (tid < ncols) {
+    const int64_t t = c0 + tid;
+    const uint32_t ab = as_uint(a_in);
+    uint32_t sel_bits = ab;
+#pragma unroll
+    for (int w = 0; w < kUBlock / 64; ++w) sel_bits = sel_bits > red[tid][w] ? sel_bits : red[tid][w];
+    hist[t] = a_in;  // row 0; row 0 was loaded (as source of row 1) before the last barrier
+    if (algo == FP8Q_AMAX_MOST_RECENT) sel_bits = ab;
+    const float sel = as_float(sel_bits);
+    const float fmax = fmt ? kE5M2Max : kE4M3Max;
+    float s = s_old;
+    if (__builtin_isfinite(sel) && sel > 0.0f) {
+      float c = sel / fmax;
+      c = ldexpf(c, margin);
+      if (__builtin_isfinite(c) && c > 0.0f) s = c;
+    }
+    scale[t] = s;
+    scale_inv[t] = 1.0f / s;
+    if (reset_amax) amax[t] = 0.0f;
+  }
+}
+
+}  // namespace fp8q
+
+using namespace fp8q;
+
+extern "C" int fp8_amax_and_scale_update(float* amax, float* amax_history, float* scale,
+                                         float* scale_inv, const uint8_t* formats, int64_t n,
+                                         int64_t history_len, int algo, int margin,
+                                         int reset_amax, void* stream) {
+  if (n < 0 || history_len < 1) return FP8Q_EINVAL;
+  if (algo != FP8Q_AMAX_MAX && algo != FP8Q_AMAX_MOST_RECENT) return FP8Q_EINVAL;
+  if (margin < -126 || margin > 126) return FP8Q_EINVAL;
+  if (n == 0) return FP8Q_OK;
+  if (!amax || !amax_history || !scale || !scale_inv || !formats) return FP8Q_EINVAL;
+  if (history_len > (INT64_MAX / 8) / n) return FP8Q_EINVAL;  // H*n floats must be addressable
+  const int64_t groups = ceil_div(n, kUCols);
+  const int64_t per_xcd = ceil_div(groups, 8);
+  const int64_t blocks = 8 * per_xcd;
+  if (blocks > 0x7FFFFFFF) return FP8Q_EINVAL;
+  const bool vec = (n % kUCols == 0) && ((uintptr_t)amax_history % (4 * kUCols) == 0);
+  int rm = reset_amax ? 1 : 0;
+  void* args[] = {&amax, &amax_history, &scale, &scale_inv, (void*)&formats, &n, &history_len,
+                  &algo, &margin, &rm, (void*)&groups, (void*)&per_xcd};
+  const void* fn = vec ? (const void*)amax_and_scale_update_kernel<true>
+                       : (const void*)amax_and_scale_update_kernel<false>;
+  return launch_status(hipLaunchKernel(fn, dim3((unsigned)blocks), dim3(kUBlock), args, 0,
+                                       (hipStream_t)stream));
+}

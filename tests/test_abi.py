@@ -1,0 +1,124 @@
+"""The C-ABI library loads without a GPU, exports what include/fp8q.h declares, and
+rejects invalid arguments on the host before touching the device."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fp8q.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fp8_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    assert declared_functions() == sorted([
+        "fp8_quantize_amax", "fp8_multi_quantize_amax", "fp8_dequantize",
+        "fp8_amax_and_scale_update", "fp8_status_string"])
+
+
+def test_library_exports_every_declared_symbol():
+    import delayed_scaling_amax_amd as d
+    out = subprocess.run(["nm", "-D", "--defined-only", d.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r" T (\w+)$", out, flags=re.M))
+    missing = set(declared_functions()) - exported
+    assert not missing, missing
+    for name in declared_functions():
+        assert hasattr(d.lib, name)
+
+
+def test_header_compiles_as_c_and_cxx(tmp_path):
+    for lang, comp in (("c", "gcc"), ("c++", "g++")):
+        src = tmp_path / ("t." + ("c" if lang == "c" else "cpp"))
+        src.write_text('#include "fp8q.h"\nint main(void){ fp8q_tensor t; (void)t; '
+                       'return FP8Q_OK + (int)sizeof(fp8q_tensor) - 48; }\n')
+        exe = tmp_path / ("t_" + lang)
+        subprocess.run([comp, "-Wall", "-Werror", "-I", os.path.dirname(HEADER), str(src),
+                        "-o", str(exe)], check=True)
+        assert subprocess.run([str(exe)]).returncode == 0
+
+
+def test_struct_layout_matches_binding():
+    import delayed_scaling_amax_amd as d
+    assert ctypes.sizeof(d.fp8q_tensor) == 48
+    assert [f[0] for f in d.fp8q_tensor._fields_] == ["src", "dst", "numel", "src_dtype",
+                                                        "format", "scale", "amax"]
+
+
+def test_status_strings():
+    import delayed_scaling_amax_amd as d
+    assert d.fp8_status_string(0) == "ok"
+    for st in (-1, -2, -3, 7):
+        assert isinstance(d.fp8_status_string(st), str) and d.fp8_status_string(st)
+
+
+BAD = 0x1000  # a non-NULL pointer value that is never dereferenced (validation fails first)
+
+
+@pytest.mark.parametrize("args", [
+    (None, 0, None, 10, 0, BAD, BAD),        # NULL src/dst with numel > 0
+    (BAD, 0, BAD, -1, 0, BAD, BAD),          # negative numel
+    (BAD, 2, BAD, 10, 0, BAD, BAD),          # bad src dtype
+    (BAD, 0, BAD, 10, 2, BAD, BAD),          # bad format
+    (BAD, 0, BAD, 10, 0, None, BAD),         # NULL scale
+    (BAD, 0, BAD, 10, 0, BAD, None),         # NULL amax
+])
+def test_quantize_rejects_invalid(args):
+    import delayed_scaling_amax_amd as d
+    assert d.lib.fp8_quantize_amax(*args, None) == d.EINVAL
+
+
+def test_multi_rejects_before_enqueue():
+    import delayed_scaling_amax_amd as d
+    arr = (d.fp8q_tensor * 3)()
+    # entries 0 and 1 would be valid zero-size no-ops; entry 2 is invalid -> EINVAL for all
+    for i in range(3):
+        arr[i] = d.fp8q_tensor(None, None, 0, 0, 0, BAD, BAD)
+    arr[2].format = 9
+    assert d.lib.fp8_multi_quantize_amax(arr, 3, None) == d.EINVAL
+    assert d.lib.fp8_multi_quantize_amax(arr, -1, None) == d.EINVAL
+    assert d.lib.fp8_multi_quantize_amax(None, 2, None) == d.EINVAL
+
+
+def test_zero_size_is_noop_without_device():
+    import delayed_scaling_amax_amd as d
+    arr = (d.fp8q_tensor * 2)()
+    for i in range(2):
+        arr[i] = d.fp8q_tensor(None, None, 0, 1, 1, BAD, BAD)
+    assert d.lib.fp8_multi_quantize_amax(arr, 2, None) == d.OK
+    assert d.lib.fp8_multi_quantize_amax(None, 0, None) == d.OK
+    assert d.lib.fp8_quantize_amax(None, 0, None, 0, 0, BAD, BAD, None) == d.OK
+    assert d.lib.fp8_dequantize(None, 0, None, 1, 0, BAD, None) == d.OK
+    assert d.lib.fp8_amax_and_scale_update(None, None, None, None, None, 0, 4, 0, 0, 0,
+                                           None) == d.OK
+
+
+@pytest.mark.parametrize("args", [
+    (BAD, 0, BAD, 1, -1, BAD),    # negative numel
+    (BAD, 3, BAD, 1, 10, BAD),    # bad format
+    (BAD, 0, BAD, 5, 10, BAD),    # bad dst dtype
+    (BAD, 0, BAD, 1, 10, None),   # NULL scale
+    (None, 0, BAD, 1, 10, BAD),   # NULL src
+])
+def test_dequantize_rejects_invalid(args):
+    import delayed_scaling_amax_amd as d
+    assert d.lib.fp8_dequantize(*args, None) == d.EINVAL
+
+
+@pytest.mark.parametrize("n,H,algo,margin,ptrs", [
+    (-1, 4, 0, 0, 5), (4, 0, 0, 0, 5), (4, 4, 2, 0, 5), (4, 4, 0, 127, 5), (4, 4, 0, -127, 5),
+    (4, 4, 0, 0, 4),
+])
+def test_update_rejects_invalid(n, H, algo, margin, ptrs):
+    import delayed_scaling_amax_amd as d
+    p = [BAD] * 5
+    if ptrs < 5:
+        p[ptrs] = None
+    assert d.lib.fp8_amax_and_scale_update(*p, n, H, algo, margin, 0, None) == d.EINVAL
