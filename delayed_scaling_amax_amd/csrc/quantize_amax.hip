@@ -55,6 +55,14 @@ constexpr int kQUnroll = FP8Q_Q_UNROLL;           // 8-element groups in flight 
 constexpr int kQMaxEntries = 32;                  // tensors per launch (kernel-argument table)
 constexpr int kQBlocksPerCU = FP8Q_Q_BLOCKS_PER_CU;  // persistent grid size per CU
 constexpr int kQChunk = kQBlock * kQUnroll;       // units (8-element groups) per chunk
+#ifndef FP8Q_Q_DEPTH
+#define FP8Q_Q_DEPTH 1
+#endif
+#ifndef FP8Q_Q_PASS
+#define FP8Q_Q_PASS 8
+#endif
+constexpr int kQDepth = FP8Q_Q_DEPTH;  // passes in flight ahead of the one being converted
+constexpr int kQPass = FP8Q_Q_PASS;    // bf16 groups per pass (fp32: half)
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -90,8 +98,8 @@ struct QEntry {
   uint8_t* dst;
   const float* scale;
   uint32_t* amax;
-  int64_t cbegin;   // first chunk of this tensor in the launch's chunk space
-  int64_t n_chunks; // ceil(n_units / kQChunk)
+  int64_t fbegin;   // first full chunk of this tensor in the launch's full-chunk space
+  int64_t nfull;    // full chunks of the aligned body: n_vec / kQChunk
   int64_t n_units;  // vector groups + scalar units
   int64_t n_vec;    // 8-element groups at [head, head + 8*n_vec), 16B/8B aligned
   int64_t head;     // elements before the first vector group
@@ -100,10 +108,12 @@ struct QEntry {
   int32_t fmt;
 };
 
+// Entries are sorted by kind (dtype * 2 + fmt): kind k occupies [run_end[k-1], run_end[k]).
 struct QTable {
   QEntry e[kQMaxEntries];
-  int64_t total_chunks;
+  int64_t total_full;
   int32_t n;
+  int32_t run_end[4];
 };
 
 // ---------------------------------------------------------------- element math
@@ -240,6 +250,105 @@ __device__ __forceinline__ uint2 quant8_f32(uint4 lo, uint4 hi, float s, float r
   return out;
 }
 
+// ---------------------------------------------------------------- pass helpers
+// The streaming body splits a group's work so that the patch test runs once per pass:
+// magnitude max of the group, codes assuming no element needs the fixed-code path,
+// and the patch, applied only where the pass max shows it is needed.
+__device__ __forceinline__ uint32_t mag8_bf16(uint4 w) {  // packed 16-bit magnitude max
+  return pk_max_u16(pk_max_u16(w.x & 0x7FFF7FFFu, w.y & 0x7FFF7FFFu),
+                    pk_max_u16(w.z & 0x7FFF7FFFu, w.w & 0x7FFF7FFFu));
+}
+
+__device__ __forceinline__ uint32_t mag8_f32(uint4 lo, uint4 hi) {
+  const uint32_t u[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+  uint32_t m = 0;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const uint32_t a = u[k] & 0x7FFFFFFFu;
+    m = m > a ? m : a;
+  }
+  return m;
+}
+
+template <int kFmt>
+__device__ __forceinline__ uint2 codes8_bf16(uint4 w, float s, float r) {
+  const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+  float c[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const float x = as_float((k & 1) ? (u[k >> 1] & 0xFFFF0000u) : (u[k >> 1] << 16));
+    c[k] = saturate<kFmt>(div_corrected1(x, s, r));
+  }
+  return make_uint2(pack4<kFmt>(c[0], c[1], c[2], c[3]), pack4<kFmt>(c[4], c[5], c[6], c[7]));
+}
+
+template <int kFmt>
+__device__ __forceinline__ uint2 codes8_f32(uint4 lo, uint4 hi, float s, float r) {
+  const uint32_t u[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+  float c[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) c[k] = saturate<kFmt>(div_corrected2(as_float(u[k]), s, r));
+  return make_uint2(pack4<kFmt>(c[0], c[1], c[2], c[3]), pack4<kFmt>(c[4], c[5], c[6], c[7]));
+}
+
+template <int kFmt>
+__device__ __forceinline__ uint2 patch8_bf16(uint2 codes, uint4 w, uint32_t xlim) {
+  const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+  uint32_t mag[8], sign[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const uint32_t h = (k & 1) ? (u[k >> 1] >> 16) : (u[k >> 1] & 0xFFFFu);
+    mag[k] = h & 0x7FFFu;
+    sign[k] = (h >> 8) & 0x80u;
+  }
+  return patch_codes<kFmt>(codes, mag, sign, xlim, 0x7F80u);
+}
+
+template <int kFmt>
+__device__ __forceinline__ uint2 patch8_f32(uint2 codes, uint4 lo, uint4 hi, uint32_t xlim) {
+  const uint32_t u[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+  uint32_t mag[8], sign[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    mag[k] = u[k] & 0x7FFFFFFFu;
+    sign[k] = (u[k] >> 24) & 0x80u;
+  }
+  return patch_codes<kFmt>(codes, mag, sign, xlim, 0x7F800000u);
+}
+
+__device__ __forceinline__ uint32_t max_halves(uint32_t m) {
+  const uint32_t lo = m & 0xFFFFu, hi = m >> 16;
+  return lo > hi ? lo : hi;
+}
+
+// ---------------------------------------------------------------- per-tensor constants
+// Filled once per block at kernel start (one thread per tensor) so that switching to
+// the next tensor costs an LDS read, not a dependent global load.
+struct QShared {
+  float scale[kQMaxEntries];
+  float rcp[kQMaxEntries];      // RN(1/scale)
+  uint32_t xlim[kQMaxEntries];  // magnitude bits at which the fixed-code path starts
+  uint32_t win[kQMaxEntries];   // scale inside the Markstein window
+  uint32_t amax[kQMaxEntries];  // this block's amax bits per tensor
+};
+
+__device__ __forceinline__ uint32_t uniform(uint32_t v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ __forceinline__ float uniform(float v) {
+  return as_float(__builtin_amdgcn_readfirstlane(as_uint(v)));
+}
+
+// Fold a thread's accumulator into the block's amax slot of tensor t: wavefront max,
+// then one LDS atomic max per wavefront (no barrier).
+template <bool kBF16>
+__device__ __forceinline__ void flush_amax(uint32_t acc, QShared& sh, int t) {
+  if constexpr (kBF16) {
+    const uint32_t lo = acc & 0xFFFFu, hi = acc >> 16;
+    acc = (lo > hi ? lo : hi) << 16;
+  }
+  acc = wave_max_u32(acc);
+  if ((threadIdx.x & 63) == 0 && acc != 0) atomicMax(&sh.amax[t], acc);
+}
+
 // ---------------------------------------------------------------- element-wise units
 // Units [g0, g1) of a tensor, one element at a time through the IEEE divide.  Vector
 // unit g holds elements head + 8g .. head + 8g + 7; scalar element j (unit n_vec +
@@ -275,31 +384,70 @@ __device__ __forceinline__ void elementwise_units(const void* __restrict__ src,
   }
 }
 
-// ---------------------------------------------------------------- full chunks, pipelined
-// A chunk is kQChunk consecutive units of one tensor.  Full chunks of the aligned body
-// are read as passes of kU*kL 16-byte loads per thread (one pass per bf16 chunk, two
-// per fp32 chunk) through buffer resources based at the chunk.  The loads of the next
-// pass (same chunk, or this block's next chunk) are issued before the current pass is
-// converted, so the HBM requests of a wave stay in flight while it computes.
+// ---------------------------------------------------------------- phase 1: full chunks
+// A chunk is kQChunk consecutive units of one tensor; the full chunks of every tensor
+// form one space, and block b owns chunks b, b+G, b+2G, ... (grid-stride: the whole
+// grid streams one window of memory at a time).  A chunk is read as passes of kU*kL
+// 16-byte loads per thread (one pass per bf16 chunk, two per fp32 chunk) through
+// buffer resources based at the chunk.  The next pass's loads -- same chunk, next
+// chunk, or the next tensor of the same kind -- are issued before the current pass is
+// converted, so a wave's HBM requests stay in flight while it computes and across
+// tensor boundaries.  Tensors whose scale is outside the Markstein window are skipped
+// here and done element-wise in phase 2.
 template <bool kBF16, int kFmt>
-__device__ __forceinline__ void full_chunks(const void* __restrict__ src, uint8_t* __restrict__ dst,
-                                            int64_t head, int64_t k0, int64_t k_end,
-                                            int64_t k_step, float s, float r, uint32_t xlim,
-                                            uint32_t& acc) {
+__device__ __forceinline__ void run_full_chunks(const QTable& tab, QShared& sh, int t_begin,
+                                                int t_end) {
+  constexpr int kL = kBF16 ? 1 : 2;                // 16-byte loads per group
+  constexpr int kU = kBF16 ? kQPass : kQPass / 2;  // groups per pass
+  constexpr int kP = kQUnroll / kU;                // passes per chunk
+  static_assert(kQUnroll % kU == 0, "a chunk is a whole number of passes");
   constexpr int esz = kBF16 ? 2 : 4;
-  constexpr int kL = kBF16 ? 1 : 2;                    // 16-byte loads per group
-  constexpr int kU = kBF16 ? kQUnroll : kQUnroll / 2;  // groups per pass
-  constexpr int kP = kQUnroll / kU;                    // passes per chunk
-  const uint4* __restrict__ in = (const uint4*)((const char*)src + head * esz);
-  uint2* __restrict__ out = (uint2*)(dst + head);
+  const int64_t G = gridDim.x, b = blockIdx.x;
   const uint32_t tid = threadIdx.x;
+
+  // first chunk of this block in the run, and the tensor holding it
+  const int64_t f0 = tab.e[t_begin].fbegin;
+  int64_t j = f0 + ((b - f0 % G) % G + G) % G;
+  int t = t_begin;
+  auto settle = [&](int& tt, int64_t& jj) {  // move (tt, jj) to a chunk this phase does
+    while (tt < t_end) {
+      const int64_t end = tab.e[tt].fbegin + tab.e[tt].nfull;
+      if (jj >= end) {
+        ++tt;
+      } else if (!sh.win[tt]) {  // skip the tensor: next owned chunk at or after its end
+        jj += (end - jj + G - 1) / G * G;
+        ++tt;
+      } else {
+        break;
+      }
+    }
+  };
+  settle(t, j);
+  if (t >= t_end) return;
+
+  // Fields of a tensor the pipeline touches, kept in registers: re-read from the
+  // table only when the pipeline moves to another tensor.
+  struct TensorView {
+    const uint4* in;    // aligned body, 16-byte units
+    uint2* out;         // aligned body codes, 8-byte units
+    int64_t fbegin;     // first full chunk
+    int64_t fend;       // one past the last full chunk
+  };
+  auto view = [&](int tt) {
+    TensorView v;
+    v.in = (const uint4*)((const char*)tab.e[tt].src + tab.e[tt].head * esz);
+    v.out = (uint2*)(tab.e[tt].dst + tab.e[tt].head);
+    v.fbegin = tab.e[tt].fbegin;
+    v.fend = v.fbegin + tab.e[tt].nfull;
+    return v;
+  };
 
   struct Pass {
     uint4 w[kU][kL];
   };
-  auto load_pass = [&](Pass& P, int64_t k, int p) {
-    const __amdgpu_buffer_rsrc_t rin =
-        buffer_rsrc(in + (k * kQChunk + p * kU * kQBlock) * kL, kU * kQBlock * kL * 16);
+  auto load_pass = [&](Pass& P, const TensorView& v, int64_t jj, int pp) {
+    const int64_t unit0 = (jj - v.fbegin) * kQChunk + pp * kU * kQBlock;
+    const __amdgpu_buffer_rsrc_t rin = buffer_rsrc(v.in + unit0 * kL, kU * kQBlock * kL * 16);
 #pragma unroll
     for (int u = 0; u < kU; ++u)
 #pragma unroll
@@ -307,136 +455,189 @@ __device__ __forceinline__ void full_chunks(const void* __restrict__ src, uint8_
         P.w[u][l] = buffer_load16(rin, (tid * kL + l) * 16, u * kQBlock * kL * 16);
   };
 
-  Pass cur, nxt;
-  int64_t k = k0;
-  int p = 0;
-  load_pass(cur, k, p);
-  for (;;) {
-    int64_t kn = k;
-    int pn = p + 1;
-    if (pn == kP) {
-      pn = 0;
-      kn = k + k_step;
+  // A pipeline slot: a pass position and the view of its tensor.
+  struct Slot {
+    int t;
+    int64_t j;
+    int p;
+    TensorView v;
+  };
+  auto advance = [&](const Slot& a) {  // the pass after a (t == t_end: none)
+    Slot n = a;
+    if (++n.p == kP) {
+      n.p = 0;
+      n.j += G;
+      if (n.j >= a.v.fend) {  // leaving the tensor (uniform; rare)
+        settle(n.t, n.j);
+        if (n.t < t_end) n.v = view(n.t);
+      }
     }
-    const bool more = kn < k_end;  // uniform
-    if (more) load_pass(nxt, kn, pn);
-    // the next pass's loads are issued; keep them ahead of this pass's arithmetic
+    return n;
+  };
+
+  // kQDepth passes are in flight ahead of the one being converted
+  Pass buf[kQDepth + 1];
+  Slot pos[kQDepth + 1];
+  pos[0] = Slot{t, j, 0, view(t)};
+  load_pass(buf[0], pos[0].v, pos[0].j, pos[0].p);
+#pragma unroll
+  for (int d = 1; d < kQDepth; ++d) {
+    pos[d] = pos[d - 1].t < t_end ? advance(pos[d - 1]) : pos[d - 1];
+    if (pos[d].t < t_end) load_pass(buf[d], pos[d].v, pos[d].j, pos[d].p);
+  }
+  float s = uniform(sh.scale[t]), r = uniform(sh.rcp[t]);
+  uint32_t xlim = uniform(sh.xlim[t]);
+  uint32_t acc = 0;
+  for (;;) {
+    Slot& c = pos[0];
+    Slot& last = pos[kQDepth - 1];
+    pos[kQDepth] = last.t < t_end ? advance(last) : last;
+    if (pos[kQDepth].t < t_end)
+      load_pass(buf[kQDepth], pos[kQDepth].v, pos[kQDepth].j, pos[kQDepth].p);
+    // the next passes' loads are issued; keep them ahead of this pass's arithmetic
     __builtin_amdgcn_sched_barrier(0);
-    const __amdgpu_buffer_rsrc_t rout =
-        buffer_rsrc(out + k * kQChunk + p * kU * kQBlock, kU * kQBlock * 8);
+    const Pass& cur = buf[0];
+    const __amdgpu_buffer_rsrc_t rout = buffer_rsrc(
+        c.v.out + (c.j - c.v.fbegin) * kQChunk + c.p * kU * kQBlock, kU * kQBlock * 8);
+    uint2 o[kU];
+    uint32_t pm = 0;  // pass magnitude max
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
-      uint2 o;
-      if constexpr (kBF16) o = quant8_bf16<kFmt>(cur.w[u][0], s, r, xlim, acc);
-      else o = quant8_f32<kFmt>(cur.w[u][0], cur.w[u][kL - 1], s, r, xlim, acc);
-      buffer_store8(rout, tid * 8, u * kQBlock * 8, o);
+      if constexpr (kBF16) {
+        pm = pk_max_u16(pm, mag8_bf16(cur.w[u][0]));
+        o[u] = codes8_bf16<kFmt>(cur.w[u][0], s, r);
+      } else {
+        const uint32_t m = mag8_f32(cur.w[u][0], cur.w[u][kL - 1]);
+        pm = pm > m ? pm : m;
+        o[u] = codes8_f32<kFmt>(cur.w[u][0], cur.w[u][kL - 1], s, r);
+      }
     }
-    if (!more) break;
-    cur = nxt;
-    k = kn;
-    p = pn;
+    if constexpr (kBF16) {
+      acc = pk_max_u16(acc, pm);
+      if (max_halves(pm) >= xlim) {  // rare: inf/NaN or a quotient far beyond FP8
+#pragma unroll
+        for (int u = 0; u < kU; ++u)
+          if (max_halves(mag8_bf16(cur.w[u][0])) >= xlim)
+            o[u] = patch8_bf16<kFmt>(o[u], cur.w[u][0], xlim);
+      }
+    } else {
+      acc = acc > pm ? acc : pm;
+      if (pm >= xlim) {
+#pragma unroll
+        for (int u = 0; u < kU; ++u)
+          if (mag8_f32(cur.w[u][0], cur.w[u][kL - 1]) >= xlim)
+            o[u] = patch8_f32<kFmt>(o[u], cur.w[u][0], cur.w[u][kL - 1], xlim);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u) buffer_store8(rout, tid * 8, u * kQBlock * 8, o[u]);
+    const Slot& nx = pos[1];
+    const bool more = nx.t < t_end;  // uniform
+    if (!more || nx.t != c.t) {
+      flush_amax<kBF16>(acc, sh, c.t);
+      acc = 0;
+      if (!more) break;
+      s = uniform(sh.scale[nx.t]);
+      r = uniform(sh.rcp[nx.t]);
+      xlim = uniform(sh.xlim[nx.t]);
+    }
+#pragma unroll
+    for (int d = 0; d < kQDepth; ++d) {
+      buf[d] = buf[d + 1];
+      pos[d] = pos[d + 1];
+    }
   }
 }
 
-// ---------------------------------------------------------------- a tensor's last chunk
-// The chunk that is partial or reaches into the scalar head/tail runs group by group.
+// ---------------------------------------------------------------- phase 2
+// Per tensor t: this block's full chunks if the scale is outside the window (all
+// element-wise), and the tensor's remainder -- the units past its last full chunk:
+// aligned groups, then the scalar head/tail -- done by block t mod G.
 template <bool kBF16, int kFmt>
-__device__ __forceinline__ void process_chunk(const void* __restrict__ src, uint8_t* __restrict__ dst,
-                                              int64_t head, int64_t n_vec, int64_t numel,
-                                              int64_t n_units, int64_t k, float s, float r,
-                                              uint32_t xlim, uint32_t& acc) {
-  constexpr int esz = kBF16 ? 2 : 4;
-  const uint4* __restrict__ in = (const uint4*)((const char*)src + head * esz);
-  uint2* __restrict__ out = (uint2*)(dst + head);
-  const int64_t u0 = k * kQChunk;
-  const int64_t u1 = min(u0 + (int64_t)kQChunk, n_units);
-  const int64_t vhi = u1 < n_vec ? u1 : n_vec;
-  for (int64_t g = u0 + threadIdx.x; g < vhi; g += kQBlock) {
-    uint2 o;
-    if constexpr (kBF16) o = quant8_bf16<kFmt>(load16(in + g), s, r, xlim, acc);
-    else o = quant8_f32<kFmt>(load16(in + 2 * g), load16(in + 2 * g + 1), s, r, xlim, acc);
-    store8(out + g, o);
-  }
-  elementwise_units<kBF16, kFmt>(src, dst, head, n_vec, numel, u0 > n_vec ? u0 : n_vec, u1, s,
-                                 acc);
-}
-
-// All chunks of tensor e that this block owns: [c, c_end) step c_step, capped at the
-// tensor's last chunk.  Returns the next chunk index.
-template <bool kBF16, int kFmt>
-__device__ __forceinline__ int64_t tensor_chunks(const QEntry& e, int64_t c, int64_t c_end,
-                                                 int64_t c_step, uint32_t& acc) {
-  const float s = *e.scale;
-  // per-tensor constants of the Markstein window (uniform)
-  const float r = 1.0f / s;
-  const bool window = (s >= 0x1p-80f) && (s <= 0x1p125f);
-  const uint32_t lim = as_uint(s * 0x1p126f);  // +inf when s >= 4
-  const uint32_t xlim = kBF16 ? min(lim >> 16, 0x7F80u) : min(lim, 0x7F800000u);
-  const int64_t stop = min(c_end, e.cbegin + e.n_chunks);
-  if (window) {
-    // this block's full chunks of the aligned body, pipelined; then the tensor's last
-    // (partial) chunk if this block owns it
-    const int64_t full_stop = min(stop, e.cbegin + e.n_vec / kQChunk);
-    if (c < full_stop) {
-      const int64_t n_mine = (full_stop - c + c_step - 1) / c_step;
-      full_chunks<kBF16, kFmt>(e.src, e.dst, e.head, c - e.cbegin, full_stop - e.cbegin, c_step,
-                               s, r, xlim, acc);
-      c += n_mine * c_step;
-    }
-    for (; c < stop; c += c_step)
-      process_chunk<kBF16, kFmt>(e.src, e.dst, e.head, e.n_vec, e.numel, e.n_units,
-                                 c - e.cbegin, s, r, xlim, acc);
-  } else {  // scale outside the window (tiny, huge, zero, negative, inf or NaN)
-    for (; c < stop; c += c_step) {
-      const int64_t u0 = (c - e.cbegin) * kQChunk;
-      const int64_t u1 = min(u0 + (int64_t)kQChunk, e.n_units);
-      elementwise_units<kBF16, kFmt>(e.src, e.dst, e.head, e.n_vec, e.numel, u0, u1, s, acc);
+__device__ __forceinline__ void tensor_rest(const QTable& tab, QShared& sh, int t) {
+  const QEntry& e = tab.e[t];
+  const int64_t G = gridDim.x, b = blockIdx.x;
+  const float s = uniform(sh.scale[t]);
+  const bool win = uniform(sh.win[t]) != 0;
+  uint32_t acc = 0;
+  bool touched = false;
+  if (!win) {
+    for (int64_t k = (b - e.fbegin % G + G) % G; k < e.nfull; k += G) {
+      elementwise_units<kBF16, kFmt>(e.src, e.dst, e.head, e.n_vec, e.numel, k * kQChunk,
+                                     (k + 1) * kQChunk, s, acc);
+      touched = true;
     }
   }
-  return c;
+  const int64_t u0 = e.nfull * kQChunk;
+  if (u0 < e.n_units && t % G == b) {
+    touched = true;
+    if (win) {
+      constexpr int esz = kBF16 ? 2 : 4;
+      const uint4* in = (const uint4*)((const char*)e.src + e.head * esz);
+      uint2* out = (uint2*)(e.dst + e.head);
+      const float r = uniform(sh.rcp[t]);
+      const uint32_t xlim = uniform(sh.xlim[t]);
+      for (int64_t g = u0 + threadIdx.x; g < e.n_vec; g += kQBlock) {
+        uint2 o;
+        if constexpr (kBF16) o = quant8_bf16<kFmt>(load16(in + g), s, r, xlim, acc);
+        else o = quant8_f32<kFmt>(load16(in + 2 * g), load16(in + 2 * g + 1), s, r, xlim, acc);
+        store8(out + g, o);
+      }
+      elementwise_units<kBF16, kFmt>(e.src, e.dst, e.head, e.n_vec, e.numel,
+                                     u0 > e.n_vec ? u0 : e.n_vec, e.n_units, s, acc);
+    } else {
+      elementwise_units<kBF16, kFmt>(e.src, e.dst, e.head, e.n_vec, e.numel, u0, e.n_units, s,
+                                     acc);
+    }
+  }
+  if (touched) flush_amax<kBF16>(acc, sh, t);
 }
-
-// Chunk schedule across the grid: 1 = grid-stride (block b takes chunks b, b+G, ...:
-// the whole grid streams one window of memory at a time), 0 = contiguous ranges.
-#ifndef FP8Q_Q_SCHEDULE
-#define FP8Q_Q_SCHEDULE 1
-#endif
 
 // kSrc: bit 0 = the table holds bf16 sources, bit 1 = fp32 sources.  The bf16-only
 // instance (the common case) keeps its register budget to the bf16 path.
 template <int kSrc>
 __global__ __launch_bounds__(kQBlock) void quantize_amax_kernel(const QTable tab) {
-  __shared__ uint32_t red[kQBlock / 64];
-  const int64_t nc = tab.total_chunks;
-#if FP8Q_Q_SCHEDULE == 1
-  int64_t c = blockIdx.x;
-  const int64_t c_end = nc, c_step = gridDim.x;
-#else
-  int64_t c = nc * blockIdx.x / gridDim.x;
-  const int64_t c_end = nc * (blockIdx.x + 1) / gridDim.x, c_step = 1;
-#endif
-  int t = 0;
-  while (c < c_end) {
-    while (c >= tab.e[t].cbegin + tab.e[t].n_chunks) ++t;  // chunks never straddle tensors
-    const QEntry& e = tab.e[t];
-    uint32_t acc = 0;
-    const int kind = e.dtype * 2 + e.fmt;  // uniform branch
-    if ((kSrc & 1) && kind == FP8Q_BF16 * 2 + FP8Q_E4M3)
-      c = tensor_chunks<true, FP8Q_E4M3>(e, c, c_end, c_step, acc);
-    else if ((kSrc & 1) && kind == FP8Q_BF16 * 2 + FP8Q_E5M2)
-      c = tensor_chunks<true, FP8Q_E5M2>(e, c, c_end, c_step, acc);
-    else if ((kSrc & 2) && kind == FP8Q_F32 * 2 + FP8Q_E4M3)
-      c = tensor_chunks<false, FP8Q_E4M3>(e, c, c_end, c_step, acc);
-    else if (kSrc & 2)
-      c = tensor_chunks<false, FP8Q_E5M2>(e, c, c_end, c_step, acc);
-    uint32_t m32 = acc;
-    if (e.dtype == FP8Q_BF16) {
-      const uint32_t lo = acc & 0xFFFFu, hi = acc >> 16;
-      m32 = (lo > hi ? lo : hi) << 16;
-    }
-    m32 = block_max_u32<kQBlock>(m32, red);
-    if (threadIdx.x == 0 && m32 != 0) atomicMax(e.amax, m32);
+  __shared__ QShared sh;
+  const int n = tab.n;
+  const int tid = threadIdx.x;
+  if (tid < n) {
+    const float s = *tab.e[tid].scale;
+    sh.scale[tid] = s;
+    sh.rcp[tid] = 1.0f / s;
+    // the window needs r normal and every residual exact (see the division notes)
+    sh.win[tid] = (s >= 0x1p-80f) && (s <= 0x1p125f);
+    const uint32_t lim = as_uint(s * 0x1p126f);  // +inf when s >= 4
+    sh.xlim[tid] = tab.e[tid].dtype == FP8Q_BF16 ? min(lim >> 16, 0x7F80u)
+                                                 : min(lim, 0x7F800000u);
+    sh.amax[tid] = 0;
   }
+  __syncthreads();
+
+  // phase 1, one run of same-kind tensors at a time
+  int tb = 0;
+#pragma unroll
+  for (int kind = 0; kind < 4; ++kind) {
+    const int te = tab.run_end[kind];
+    const bool bf16 = kind < 2;
+    if (te > tb && ((kSrc & 1) || !bf16) && ((kSrc & 2) || bf16)) {
+      if (kind == 0) run_full_chunks<true, FP8Q_E4M3>(tab, sh, tb, te);
+      else if (kind == 1) run_full_chunks<true, FP8Q_E5M2>(tab, sh, tb, te);
+      else if (kind == 2) run_full_chunks<false, FP8Q_E4M3>(tab, sh, tb, te);
+      else run_full_chunks<false, FP8Q_E5M2>(tab, sh, tb, te);
+    }
+    tb = te;
+  }
+  // phase 2
+  for (int t = 0; t < n; ++t) {
+    const int kind = tab.e[t].dtype * 2 + tab.e[t].fmt;  // uniform
+    if ((kSrc & 1) && kind == 0) tensor_rest<true, FP8Q_E4M3>(tab, sh, t);
+    else if ((kSrc & 1) && kind == 1) tensor_rest<true, FP8Q_E5M2>(tab, sh, t);
+    else if ((kSrc & 2) && kind == 2) tensor_rest<false, FP8Q_E4M3>(tab, sh, t);
+    else if (kSrc & 2) tensor_rest<false, FP8Q_E5M2>(tab, sh, t);
+  }
+  __syncthreads();
+  // one global atomic per tensor this block saw a non-zero |x| in
+  if (tid < n && sh.amax[tid] != 0) atomicMax(tab.e[tid].amax, sh.amax[tid]);
 }
 
 // ---------------------------------------------------------------- host side
@@ -474,23 +675,36 @@ static void plan_entry(const fp8q_tensor& t, QEntry* e) {
     e->n_vec = (t.numel - head) / 8;
   }
   e->n_units = e->n_vec + ceil_div(t.numel - 8 * e->n_vec, 8);
-  e->n_chunks = ceil_div(e->n_units, kQChunk);
+  e->nfull = e->n_vec / kQChunk;
 }
 
 static int launch_table(QTable* tab, hipStream_t stream) {
-  if (tab->total_chunks == 0) return FP8Q_OK;
+  int64_t units = 0;
+  for (int i = 0; i < tab->n; ++i) units += tab->e[i].n_units;
+  if (units == 0) return FP8Q_OK;
   int cus = 0;
   int st = current_device_cus(&cus);
   if (st != FP8Q_OK) return st;
-  const int64_t max_blocks = (int64_t)cus * kQBlocksPerCU;
-  int64_t blocks = tab->total_chunks;
-  if (blocks > max_blocks) blocks = max_blocks;
-  if (blocks < 1) blocks = 1;
   int src_kinds = 0;
   for (int i = 0; i < tab->n; ++i) src_kinds |= tab->e[i].dtype == FP8Q_BF16 ? 1 : 2;
   const void* fn = src_kinds == 1   ? (const void*)quantize_amax_kernel<1>
                    : src_kinds == 2 ? (const void*)quantize_amax_kernel<2>
                                     : (const void*)quantize_amax_kernel<3>;
+  // The grid-stride schedule needs every block resident at once: cap the blocks per
+  // CU at what the instance's register use allows.
+  static std::atomic<int> fit[4];
+  int per_cu = fit[src_kinds].load(std::memory_order_relaxed);
+  if (per_cu <= 0) {
+    int occ = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, fn, kQBlock, 0) != hipSuccess)
+      return FP8Q_EHIP;
+    per_cu = occ < kQBlocksPerCU ? (occ > 0 ? occ : 1) : kQBlocksPerCU;
+    fit[src_kinds].store(per_cu, std::memory_order_relaxed);
+  }
+  const int64_t max_blocks = (int64_t)cus * per_cu;
+  int64_t blocks = tab->total_full > tab->n ? tab->total_full : tab->n;
+  if (blocks > max_blocks) blocks = max_blocks;
+  if (blocks < 1) blocks = 1;
   void* args[] = {tab};
   return launch_status(hipLaunchKernel(fn, dim3((unsigned)blocks), dim3(kQBlock), args, 0, stream));
 }
@@ -508,12 +722,18 @@ extern "C" int fp8_multi_quantize_amax(const fp8q_tensor* tensors, int n, void* 
   for (int base = 0; base < n; base += kQMaxEntries) {
     QTable tab;
     tab.n = 0;
-    tab.total_chunks = 0;
-    for (int i = base; i < n && i < base + kQMaxEntries; ++i) {
-      QEntry& e = tab.e[tab.n++];
-      plan_entry(tensors[i], &e);
-      e.cbegin = tab.total_chunks;
-      tab.total_chunks += e.n_chunks;
+    tab.total_full = 0;
+    const int end = n < base + kQMaxEntries ? n : base + kQMaxEntries;
+    // entries grouped by kind (dtype * 2 + format), stable within a kind
+    for (int kind = 0; kind < 4; ++kind) {
+      for (int i = base; i < end; ++i) {
+        if (tensors[i].src_dtype * 2 + tensors[i].format != kind) continue;
+        QEntry& e = tab.e[tab.n++];
+        plan_entry(tensors[i], &e);
+        e.fbegin = tab.total_full;
+        tab.total_full += e.nfull;
+      }
+      tab.run_end[kind] = tab.n;
     }
     int st = launch_table(&tab, (hipStream_t)stream);
     if (st != FP8Q_OK) return st;

@@ -25,13 +25,13 @@
 namespace fp8q {
 
 #ifndef FP8Q_U_BLOCK
-#define FP8Q_U_BLOCK 256
+#define FP8Q_U_BLOCK 512
 #endif
 #ifndef FP8Q_U_COLS
-#define FP8Q_U_COLS 16
+#define FP8Q_U_COLS 8
 #endif
 #ifndef FP8Q_U_ROWS
-#define FP8Q_U_ROWS 4
+#define FP8Q_U_ROWS 2
 #endif
 #ifndef FP8Q_U_XCD
 #define FP8Q_U_XCD 1
