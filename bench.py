@@ -82,6 +82,8 @@ def main():
                     choices=["single_1024", "mlp_4096", "grad_8192x16384", "mlp_12288"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--update-calls", type=int, default=200)
+    ap.add_argument("--rotate", type=int, default=3,
+                    help="input/output sets used in turn by successive steps")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (the amax "
@@ -106,18 +108,28 @@ def main():
                                                              time.time() - t0))
     fmts = [0 if t.fmt == workloads.E4M3 else 1 for t in w.tensors]
     n = len(w.tensors)
-    srcs = [torch.from_numpy(t.data.view(np.int16)).view(torch.bfloat16).to(dev)
-            for t in w.tensors]
-    dsts = [torch.empty(t.data.size, dtype=torch.uint8, device=dev) for t in w.tensors]
+    # R copies of the inputs and outputs, used in turn by successive steps: a step's
+    # tensors were last touched R-1 steps (>= 1 GB of traffic) earlier, so they stream
+    # from HBM and not from the 256 MB MALL, as in a training step where the GEMMs run
+    # between two quantizations of the same tensor
+    srcs0 = [torch.from_numpy(t.data.view(np.int16)).view(torch.bfloat16).to(dev)
+             for t in w.tensors]
+    sets = [srcs0] + [[x.clone() for x in srcs0] for _ in range(args.rotate - 1)]
+    outs = [[torch.empty(t.data.size, dtype=torch.uint8, device=dev) for t in w.tensors]
+            for _ in range(args.rotate)]
     scale = torch.tensor(w.first_scale, dtype=torch.float32, device=dev)
     scale_inv = torch.empty(n, dtype=torch.float32, device=dev)
     amax = torch.zeros(n, dtype=torch.float32, device=dev)
     hist = torch.zeros(w.history_len, n, dtype=torch.float32, device=dev)
     fdev = torch.tensor(fmts, dtype=torch.uint8, device=dev)
-    entries = [(srcs[i], dsts[i], scale[i:i + 1], amax[i:i + 1], fmts[i]) for i in range(n)]
+    entry_sets = [[(sets[r][i], outs[r][i], scale[i:i + 1], amax[i:i + 1], fmts[i])
+                   for i in range(n)] for r in range(args.rotate)]
+    dsts = outs[0]
+    step_no = [0]
 
     def quantize():
-        d.fp8_multi_quantize_amax(entries)
+        d.fp8_multi_quantize_amax(entry_sets[step_no[0] % args.rotate])
+        step_no[0] += 1
 
     def update():
         d.fp8_amax_and_scale_update(amax, hist, scale, scale_inv, fdev, reset_amax=True)
@@ -253,7 +265,8 @@ def main():
         "data": "synthetic (seeded numpy PCG64, seed 12; shapes/distributions of the workload)",
         "config": {"workload": w.name, "description": w.description, "tensors": n,
                    "elements": w.numel, "history_len": w.history_len,
-                   "formats": [t.fmt for t in w.tensors], "src_dtype": "bf16"},
+                   "formats": [t.fmt for t in w.tensors], "src_dtype": "bf16",
+                   "rotating_input_sets": args.rotate},
         "quantize_amax": {"avg_us": round(q_avg_us, 3),
                           "median_us": round(1e3 * float(np.median(q_ms)), 3),
                           "gbps": round(q_gbps, 1), "pct_hbm_peak": round(100 * q_gbps /

@@ -35,10 +35,10 @@ namespace fp8q {
 #define FP8Q_Q_BLOCK 256
 #endif
 #ifndef FP8Q_Q_UNROLL
-#define FP8Q_Q_UNROLL 8
+#define FP8Q_Q_UNROLL 16
 #endif
 #ifndef FP8Q_Q_BLOCKS_PER_CU
-#define FP8Q_Q_BLOCKS_PER_CU 4
+#define FP8Q_Q_BLOCKS_PER_CU 2
 #endif
 // Cache policy of the streaming body (gfx950 buffer-op aux bits: 1 = sc0, 2 = nt,
 // 16 = sc1).  Measured on the read-16B/write-8B shape of this kernel: non-temporal
@@ -349,6 +349,61 @@ __device__ __forceinline__ void flush_amax(uint32_t acc, QShared& sh, int t) {
   if ((threadIdx.x & 63) == 0 && acc != 0) atomicMax(&sh.amax[t], acc);
 }
 
+// Fill the per-tensor constants (one thread per tensor) and zero the block's amax
+// slots.  Contains a barrier: every thread of the block calls it exactly once.
+__device__ __forceinline__ void setup_shared(const QTable& tab, QShared& sh) {
+  const int tid = threadIdx.x;
+  if (tid < tab.n) {
+    const float s = *tab.e[tid].scale;
+    sh.scale[tid] = s;
+    sh.rcp[tid] = 1.0f / s;
+    // the window needs r normal and every residual exact (see the division notes)
+    sh.win[tid] = (s >= 0x1p-80f) && (s <= 0x1p125f);
+    const uint32_t lim = as_uint(s * 0x1p126f);  // +inf when s >= 4
+    sh.xlim[tid] = tab.e[tid].dtype == FP8Q_BF16 ? min(lim >> 16, 0x7F80u)
+                                                 : min(lim, 0x7F800000u);
+    sh.amax[tid] = 0;
+  }
+  __syncthreads();
+}
+
+// ---------------------------------------------------------------- chunk ownership
+// The full chunks of one run of same-kind tensors, [f0, f1), are split over the grid:
+// grid-stride (block b owns f0' + b + kG, the whole grid streams one window of memory)
+// or contiguous ranges (block b owns [f0 + (f1-f0)*b/G, f0 + (f1-f0)*(b+1)/G)).
+#ifndef FP8Q_Q_SCHEDULE
+#define FP8Q_Q_SCHEDULE 1
+#endif
+struct Owned {
+  int64_t first;  // first owned chunk (>= limit: none)
+  int64_t limit;  // owned chunks are < limit
+  int64_t step;
+};
+
+__device__ __forceinline__ Owned owned_chunks(int64_t f0, int64_t f1) {
+  const int64_t G = gridDim.x, b = blockIdx.x;
+  Owned o;
+#if FP8Q_Q_SCHEDULE == 1
+  o.first = f0 + ((b - f0 % G) % G + G) % G;
+  o.limit = f1;
+  o.step = G;
+#else
+  o.first = f0 + (f1 - f0) * b / G;
+  o.limit = f0 + (f1 - f0) * (b + 1) / G;
+  o.step = 1;
+#endif
+  return o;
+}
+
+// Full-chunk range [f0, f1) of the run (same-kind tensors) holding table entry t.
+__device__ __forceinline__ void run_bounds(const QTable& tab, int t, int64_t& f0, int64_t& f1) {
+  const int kind = tab.e[t].dtype * 2 + tab.e[t].fmt;
+  const int tb = kind > 0 ? tab.run_end[kind - 1] : 0;
+  const int te = tab.run_end[kind];
+  f0 = tab.e[tb].fbegin;
+  f1 = tab.e[te - 1].fbegin + tab.e[te - 1].nfull;
+}
+
 // ---------------------------------------------------------------- element-wise units
 // Units [g0, g1) of a tensor, one element at a time through the IEEE divide.  Vector
 // unit g holds elements head + 8g .. head + 8g + 7; scalar element j (unit n_vec +
@@ -394,37 +449,42 @@ __device__ __forceinline__ void elementwise_units(const void* __restrict__ src,
 // converted, so a wave's HBM requests stay in flight while it computes and across
 // tensor boundaries.  Tensors whose scale is outside the Markstein window are skipped
 // here and done element-wise in phase 2.
+//
+// With `setup`, this is the block's first run: the loads of its first pass are issued
+// speculatively (assuming that tensor's scale is in the window) before the per-tensor
+// constants are set up, so the block's first HBM requests do not wait for the scale
+// loads, the reciprocals and the barrier.
 template <bool kBF16, int kFmt>
 __device__ __forceinline__ void run_full_chunks(const QTable& tab, QShared& sh, int t_begin,
-                                                int t_end) {
+                                                int t_end, bool setup) {
   constexpr int kL = kBF16 ? 1 : 2;                // 16-byte loads per group
   constexpr int kU = kBF16 ? kQPass : kQPass / 2;  // groups per pass
   constexpr int kP = kQUnroll / kU;                // passes per chunk
   static_assert(kQUnroll % kU == 0, "a chunk is a whole number of passes");
   constexpr int esz = kBF16 ? 2 : 4;
-  const int64_t G = gridDim.x, b = blockIdx.x;
   const uint32_t tid = threadIdx.x;
 
   // first chunk of this block in the run, and the tensor holding it
-  const int64_t f0 = tab.e[t_begin].fbegin;
-  int64_t j = f0 + ((b - f0 % G) % G + G) % G;
+  int64_t f0, f1;
+  run_bounds(tab, t_begin, f0, f1);
+  const Owned own = owned_chunks(f0, f1);
+  int64_t j = own.first;
   int t = t_begin;
   auto settle = [&](int& tt, int64_t& jj) {  // move (tt, jj) to a chunk this phase does
     while (tt < t_end) {
       const int64_t end = tab.e[tt].fbegin + tab.e[tt].nfull;
-      if (jj >= end) {
+      if (jj >= own.limit) {
+        tt = t_end;
+      } else if (jj >= end) {
         ++tt;
       } else if (!sh.win[tt]) {  // skip the tensor: next owned chunk at or after its end
-        jj += (end - jj + G - 1) / G * G;
+        jj += (end - jj + own.step - 1) / own.step * own.step;
         ++tt;
       } else {
         break;
       }
     }
   };
-  settle(t, j);
-  if (t >= t_end) return;
-
   // Fields of a tensor the pipeline touches, kept in registers: re-read from the
   // table only when the pipeline moves to another tensor.
   struct TensorView {
@@ -466,8 +526,8 @@ __device__ __forceinline__ void run_full_chunks(const QTable& tab, QShared& sh, 
     Slot n = a;
     if (++n.p == kP) {
       n.p = 0;
-      n.j += G;
-      if (n.j >= a.v.fend) {  // leaving the tensor (uniform; rare)
+      n.j += own.step;
+      if (n.j >= a.v.fend || n.j >= own.limit) {  // leaving the tensor or the range (rare)
         settle(n.t, n.j);
         if (n.t < t_end) n.v = view(n.t);
       }
@@ -478,8 +538,18 @@ __device__ __forceinline__ void run_full_chunks(const QTable& tab, QShared& sh, 
   // kQDepth passes are in flight ahead of the one being converted
   Pass buf[kQDepth + 1];
   Slot pos[kQDepth + 1];
+  int ts = t_begin;  // speculative first position: chunk ranges only
+  int64_t js = j;
+  if (setup) {
+    while (ts < t_end && js < own.limit && js >= tab.e[ts].fbegin + tab.e[ts].nfull) ++ts;
+    if (js >= own.limit) ts = t_end;
+    if (ts < t_end) load_pass(buf[0], view(ts), js, 0);
+    setup_shared(tab, sh);
+  }
+  settle(t, j);
+  if (t >= t_end) return;
   pos[0] = Slot{t, j, 0, view(t)};
-  load_pass(buf[0], pos[0].v, pos[0].j, pos[0].p);
+  if (!setup || ts != t || js != j) load_pass(buf[0], pos[0].v, pos[0].j, pos[0].p);
 #pragma unroll
   for (int d = 1; d < kQDepth; ++d) {
     pos[d] = pos[d - 1].t < t_end ? advance(pos[d - 1]) : pos[d - 1];
@@ -562,7 +632,15 @@ __device__ __forceinline__ void tensor_rest(const QTable& tab, QShared& sh, int 
   uint32_t acc = 0;
   bool touched = false;
   if (!win) {
-    for (int64_t k = (b - e.fbegin % G + G) % G; k < e.nfull; k += G) {
+    int64_t f0, f1;
+    run_bounds(tab, t, f0, f1);
+    const Owned own = owned_chunks(f0, f1);
+    // this block's chunks of tensor t, in the same ownership as phase 1
+    int64_t jj = own.first;
+    if (jj < e.fbegin) jj += (e.fbegin - jj + own.step - 1) / own.step * own.step;
+    const int64_t stop = min(own.limit, e.fbegin + e.nfull);
+    for (; jj < stop; jj += own.step) {
+      const int64_t k = jj - e.fbegin;
       elementwise_units<kBF16, kFmt>(e.src, e.dst, e.head, e.n_vec, e.numel, k * kQChunk,
                                      (k + 1) * kQChunk, s, acc);
       touched = true;
@@ -600,33 +678,24 @@ __global__ __launch_bounds__(kQBlock) void quantize_amax_kernel(const QTable tab
   __shared__ QShared sh;
   const int n = tab.n;
   const int tid = threadIdx.x;
-  if (tid < n) {
-    const float s = *tab.e[tid].scale;
-    sh.scale[tid] = s;
-    sh.rcp[tid] = 1.0f / s;
-    // the window needs r normal and every residual exact (see the division notes)
-    sh.win[tid] = (s >= 0x1p-80f) && (s <= 0x1p125f);
-    const uint32_t lim = as_uint(s * 0x1p126f);  // +inf when s >= 4
-    sh.xlim[tid] = tab.e[tid].dtype == FP8Q_BF16 ? min(lim >> 16, 0x7F80u)
-                                                 : min(lim, 0x7F800000u);
-    sh.amax[tid] = 0;
-  }
-  __syncthreads();
 
-  // phase 1, one run of same-kind tensors at a time
+  // phase 1, one run of same-kind tensors at a time; the first run also sets up sh
+  bool ready = false;
   int tb = 0;
 #pragma unroll
   for (int kind = 0; kind < 4; ++kind) {
     const int te = tab.run_end[kind];
     const bool bf16 = kind < 2;
     if (te > tb && ((kSrc & 1) || !bf16) && ((kSrc & 2) || bf16)) {
-      if (kind == 0) run_full_chunks<true, FP8Q_E4M3>(tab, sh, tb, te);
-      else if (kind == 1) run_full_chunks<true, FP8Q_E5M2>(tab, sh, tb, te);
-      else if (kind == 2) run_full_chunks<false, FP8Q_E4M3>(tab, sh, tb, te);
-      else run_full_chunks<false, FP8Q_E5M2>(tab, sh, tb, te);
+      if (kind == 0) run_full_chunks<true, FP8Q_E4M3>(tab, sh, tb, te, !ready);
+      else if (kind == 1) run_full_chunks<true, FP8Q_E5M2>(tab, sh, tb, te, !ready);
+      else if (kind == 2) run_full_chunks<false, FP8Q_E4M3>(tab, sh, tb, te, !ready);
+      else run_full_chunks<false, FP8Q_E5M2>(tab, sh, tb, te, !ready);
+      ready = true;
     }
     tb = te;
   }
+  if (!ready) setup_shared(tab, sh);
   // phase 2
   for (int t = 0; t < n; ++t) {
     const int kind = tab.e[t].dtype * 2 + tab.e[t].fmt;  // uniform
