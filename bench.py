@@ -243,6 +243,24 @@ def main():
         "wall %.2f us/call" % (uH, "%.2f" % graph_us if graph_us else "n/a", warm_us, cold_us,
                                wall_us))
 
+    # ------------------------------------------------------------ dequantize (not in the step)
+    # codes of the largest tensor of the step back to bf16 with its scale
+    big = max(range(n), key=lambda i: w.tensors[i].data.size)
+    dq_out = torch.empty(w.tensors[big].data.size, dtype=torch.bfloat16, device=dev)
+    for _ in range(3):
+        d.fp8_dequantize(dsts[big], dq_out, scale[big:big + 1], fmts[big])
+    torch.cuda.synchronize()
+    dq_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+             for _ in range(20)]
+    for a, b in dq_ev:
+        a.record()
+        d.fp8_dequantize(dsts[big], dq_out, scale[big:big + 1], fmts[big])
+        b.record()
+    torch.cuda.synchronize()
+    dq_us = 1e3 * float(np.median([a.elapsed_time(b) for a, b in dq_ev]))
+    dq_bytes = 3 * w.tensors[big].data.size + 4
+    del dq_out
+
     # ------------------------------------------------------------ copy context
     cbuf = torch.empty(1 << 27, dtype=torch.float32, device=dev)  # 512 MiB
     cdst = torch.empty_like(cbuf)
@@ -281,6 +299,9 @@ def main():
                             "host_wall_us_per_call": round(wall_us, 3),
                             "alg_bytes": alg_bytes_update(un, uH),
                             "step_update_events_us": round(1e3 * float(np.mean(u_ms)), 3)},
+        "dequantize": {"tensor": w.tensors[big].name, "elements": int(w.tensors[big].data.size),
+                       "out": "bf16", "events_median_us": round(dq_us, 3),
+                       "gbps": round(dq_bytes / (dq_us * 1e-6) / 1e9, 1)},
         "copy_d2d_gbps": round(copy_gbps, 1),
         "roofline": {"bound": "hbm", "achieved": round(q_gbps, 1), "peak": PEAK_HBM_GBPS,
                      "unit": "GB/s", "frac": round(q_gbps / PEAK_HBM_GBPS, 4),

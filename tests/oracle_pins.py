@@ -473,4 +473,22 @@ def pin_bf16_rounding_random(o):
             assert (yb[fin] == wb[fin]).all()
 
 
+
+
+def pin_microbatch_accumulation(o):
+    """Max-accumulating amax over microbatches ("Gradient accumulation of FP8 params":
+    FP8 meta combines with max) equals the amax of the concatenated tensor, and the
+    codes of each microbatch do not depend on the accumulated amax."""
+    g = np.random.Generator(np.random.PCG64(31))
+    parts = [(g.standard_normal(n) * 10.0 ** g.uniform(-2, 2)).astype(np.float32)
+             for n in (1000, 1, 777, 4096)]
+    a = 0.0
+    for p in parts:
+        codes, a = o.quantize_amax(p, E4M3, 0.25, amax_in=a)
+        alone, _ = o.quantize_amax(p, E4M3, 0.25)
+        assert (codes == alone).all()
+    _, whole = o.quantize_amax(np.concatenate(parts), E4M3, 0.25)
+    assert f2u(a) == f2u(whole)
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -81,3 +81,79 @@ def test_grad_8192x16384_saturation(orc):
 @pytest.mark.timeout(1200)
 def test_mlp_12288_full_step(orc):
     two_steps(orc, workloads.mlp_12288())
+
+
+def test_microbatch_accumulation_once_per_step(orc):
+    """Several quantize launches per step (microbatches) max-accumulate into one amax per
+    tensor; one batched update with reset_amax per step ("Implement fused kernel for FP8
+    scale update": update once per training step instead of per microbatch).  Three steps
+    x four microbatches x (activation E4M3, gradient E5M2), bit-exact against the oracle
+    running the same schedule."""
+    import delayed_scaling_amax_amd as d
+    n_micro, steps, H = 4, 3, 8
+    acts = [workloads.random_bf16(300_000, 500 + m, -6, 3) for m in range(n_micro)]
+    grads = [workloads.random_bf16(200_003, 600 + m, -20, -8) for m in range(n_micro)]
+    fmts = [0, 1]
+    amax = torch.zeros(2, dtype=torch.float32, device="cuda")
+    scale = torch.ones(2, dtype=torch.float32, device="cuda")
+    scale_inv = torch.empty(2, dtype=torch.float32, device="cuda")
+    hist = torch.zeros(H, 2, dtype=torch.float32, device="cuda")
+    fdev = torch.tensor(fmts, dtype=torch.uint8, device="cuda")
+    o_scale, o_hist = np.ones(2, np.float32), np.zeros((H, 2), np.float32)
+    srcs = [(dev_src(a), dev_src(g)) for a, g in zip(acts, grads)]
+    for step in range(steps):
+        note("microbatch step %d" % step)
+        o_amax = np.zeros(2, np.float32)
+        for m in range(n_micro):
+            qa = torch.empty(acts[m].size, dtype=torch.uint8, device="cuda")
+            qg = torch.empty(grads[m].size, dtype=torch.uint8, device="cuda")
+            d.fp8_multi_quantize_amax([(srcs[m][0], qa, scale[0:1], amax[0:1], 0),
+                                       (srcs[m][1], qg, scale[1:2], amax[1:2], 1)])
+            torch.cuda.synchronize()
+            wa, o_amax[0] = orc.quantize_amax(acts[m], 0, float(o_scale[0]),
+                                              amax_in=float(o_amax[0]))
+            wg, o_amax[1] = orc.quantize_amax(grads[m], 1, float(o_scale[1]),
+                                              amax_in=float(o_amax[1]))
+            assert qa.cpu().numpy().tobytes() == wa.tobytes()
+            assert qg.cpu().numpy().tobytes() == wg.tobytes()
+        assert (bits(amax.cpu().numpy()) == bits(o_amax)).all()
+        d.fp8_amax_and_scale_update(amax, hist, scale, scale_inv, fdev, reset_amax=True)
+        torch.cuda.synchronize()
+        r = orc.amax_and_scale_update(o_amax, o_hist, o_scale, np.array(fmts, np.uint8),
+                                      reset_amax=True)
+        o_hist, o_scale = r["hist"], r["scale"]
+        assert (bits(hist.cpu().numpy()) == bits(o_hist)).all()
+        assert (bits(scale.cpu().numpy()) == bits(o_scale)).all()
+        assert (bits(scale_inv.cpu().numpy()) == bits(r["scale_inv"])).all()
+        assert (amax.cpu().numpy() == 0).all()
+
+
+def test_resume_is_bit_identical(orc):
+    """Checkpoint/resume of the FP8 meta: run 4 steps; separately run 2, copy history /
+    scale / scale_inv to the host and into fresh device buffers, run 2 more; both end in
+    identical bytes (every operation is deterministic)."""
+    import delayed_scaling_amax_amd as d
+    x = workloads.random_bf16(500_000, 700, -4, 4)
+    src = dev_src(x)
+
+    def run(steps, state=None):
+        hist = torch.zeros(16, 1, device="cuda") if state is None else state[0].cuda()
+        scale = torch.ones(1, device="cuda") if state is None else state[1].cuda()
+        sinv = torch.ones(1, device="cuda") if state is None else state[2].cuda()
+        amax = torch.zeros(1, device="cuda")
+        f = torch.zeros(1, dtype=torch.uint8, device="cuda")
+        q = torch.empty(x.size, dtype=torch.uint8, device="cuda")
+        for k in range(steps):
+            xs = src if k % 2 == 0 else (src.float() * 1.5).to(torch.bfloat16)
+            d.fp8_quantize_amax(xs, q, scale, amax, 0)
+            d.fp8_amax_and_scale_update(amax, hist, scale, sinv, f, reset_amax=True)
+        torch.cuda.synchronize()
+        return hist.cpu(), scale.cpu(), sinv.cpu(), q.cpu()
+
+    note("resume")
+    full = run(4)
+    half = run(2)
+    resumed = run(2, state=half[:3])
+    for a, b in zip(full, resumed):
+        assert torch.equal(a.view(torch.uint8) if a.dtype == torch.uint8 else a.view(torch.int32),
+                           b.view(torch.uint8) if b.dtype == torch.uint8 else b.view(torch.int32))
