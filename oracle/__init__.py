@@ -63,6 +63,10 @@ def _declare(lib):
     lib.oracle_dequantize.restype = None
     lib.oracle_count_saturated.argtypes = [vp, i32, i64, i32, c.c_float]
     lib.oracle_count_saturated.restype = i64
+    lib.oracle_gelu_bf16_array.argtypes = [vp, vp, vp, i64]
+    lib.oracle_gelu_bf16_array.restype = None
+    lib.oracle_gelu_double.argtypes = [c.c_double]
+    lib.oracle_gelu_double.restype = c.c_double
     return lib
 
 
@@ -151,6 +155,35 @@ class Oracle:
         self.lib.oracle_dequantize(codes.ctypes.data, fmt, dst.ctypes.data, out_dtype,
                                    codes.size, float(scale))
         return dst
+
+    def gelu_bf16(self, x: np.ndarray):
+        """y = RN_bf16(gelu_tanh(x)) for bf16 bits x; returns (y, alt) uint16 arrays where
+        alt is the other admissible neighbour near a rounding midpoint (else alt == y)."""
+        x = np.ascontiguousarray(x, np.uint16)
+        y = np.empty_like(x)
+        alt = np.empty_like(x)
+        self.lib.oracle_gelu_bf16_array(x.ctypes.data, y.ctypes.data, alt.ctypes.data, x.size)
+        return y, alt
+
+    def gelu_double(self, x: float) -> float:
+        return float(self.lib.oracle_gelu_double(float(x)))
+
+    def gelu_quantize_amax(self, x: np.ndarray, fmt: int, scale: float, amax_in: float = 0.0,
+                           threads: int = 1):
+        """Producer-fused quantize of gelu(x): returns (codes, amax, codes_alt, amax_lo,
+        amax_hi).  codes/amax follow y = RN_bf16(gelu(x)); codes_alt are the codes of the
+        admissible alternative y; [amax_lo, amax_hi] bounds the amax over every admissible
+        choice (bit patterns)."""
+        y, alt = self.gelu_bf16(x)
+        codes, amax = self.quantize_amax(y, fmt, scale, amax_in=amax_in, threads=threads)
+        codes_alt, _ = self.quantize_amax(alt, fmt, scale, amax_in=amax_in, threads=threads)
+        my = y.astype(np.uint32) & 0x7FFF
+        ma = alt.astype(np.uint32) & 0x7FFF
+        a_in = int(np.float32(amax_in).view(np.uint32))
+        lo = max(int(np.minimum(my, ma).max(initial=0)) << 16, a_in)
+        hi = max(int(np.maximum(my, ma).max(initial=0)) << 16, a_in)
+        return (codes.reshape(x.shape), amax, codes_alt.reshape(x.shape),
+                np.uint32(lo).view(np.float32), np.uint32(hi).view(np.float32))
 
     def count_saturated(self, x: np.ndarray, fmt: int, scale: float) -> int:
         x, dt = self._src(x)

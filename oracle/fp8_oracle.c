@@ -225,3 +225,83 @@ int64_t oracle_count_saturated(const void* src, int src_dtype, int64_t n, int fm
   }
   return c;
 }
+
+/* ------------------------------------------------------------------------------
+ * Producer-fused quantize: the FFN activation of the reproducer in "Fusion of Fp8
+ * quantization and amax reduction kernels" (test.py: Dense wi -> nn.gelu -> Dense wo,
+ * the wo input quantized to FP8).  Readings (pages silent):
+ *  G1 gelu is the tanh form 0.5*x*(1 + tanh(sqrt(2/pi)*(x + 0.044715*x^3))) (the default
+ *     of the reproducer's nn.gelu), evaluated here in double precision;
+ *  G2 the activation tensor is bf16 (the model's dtype): y = RN_bf16(gelu(x)), one
+ *     rounding of the double value; gelu(+inf) = +inf, gelu(-inf) = -0, gelu(NaN) = NaN;
+ *  G3 y is then quantized and reduced exactly as a bf16 tensor (R1-R5).
+ * A single-precision evaluation of gelu carries a small relative error, growing with
+ * |2u| through exp (u = sqrt(2/pi)*(x + 0.044715 x^3)); where the double value lies so
+ * close to a bf16 rounding midpoint that such an evaluation may round either way, the
+ * other neighbour is returned too (`alt`), so a check can accept either. */
+static double gelu_tanh_d(double x) {
+  if (isnan(x)) return x;
+  if (isinf(x)) return x > 0 ? x : -0.0;
+  const double c = sqrt(2.0 / 3.14159265358979323846);
+  const double u = c * (x + 0.044715 * x * x * x);
+  /* 0.5 * (1 + tanh(u)) == 1 / (1 + exp(-2u)) exactly; the right side keeps full
+   * relative precision where 1 + tanh(u) would cancel (x below about -5) */
+  return x / (1.0 + exp(-2.0 * u));
+}
+
+/* Round a double to bf16 (8 significant bits, subnormals, overflow to inf), RNE;
+ * returns the bf16 bits.  If `lo`/`hi` are non-NULL they receive the two bf16 values
+ * bracketing |v| (equal when v is exactly representable). */
+static uint16_t round_d_to_bf16(double v, double* lo_out, double* hi_out) {
+  uint16_t sign = signbit(v) ? 0x8000 : 0;
+  double a = fabs(v);
+  if (isnan(v)) return (uint16_t)(0x7FC0 | sign);
+  if (isinf(v)) return (uint16_t)(0x7F80 | sign);
+  if (a == 0.0) {
+    if (lo_out) *lo_out = 0.0;
+    if (hi_out) *hi_out = 0.0;
+    return sign;
+  }
+  int e;
+  frexp(a, &e);
+  e -= 1;
+  if (e < -126) e = -126;
+  double q = ldexp(1.0, e - 7);           /* spacing of bf16 values near a */
+  double fl = floor(a / q) * q, ce = ceil(a / q) * q;
+  if (lo_out) *lo_out = fl;
+  if (hi_out) *hi_out = ce;
+  double r = ldexp(nearbyint(ldexp(a, 7 - e)), e - 7);  /* nearest bf16 magnitude */
+  if (r >= ldexp(1.0, 128)) return (uint16_t)(0x7F80 | sign);
+  return (uint16_t)((f2u((float)r) >> 16) | sign);
+}
+
+/* y = RN_bf16(gelu(x)) for one bf16 x; *alt = the other admissible bf16 result when the
+ * double value is within the single-precision error window of a rounding midpoint, else
+ * *alt = y.  Window (relative to |gelu|): 2^-24 * (16 + 4*|2u|), plus 2^-147 absolute. */
+uint16_t oracle_gelu_bf16(uint16_t xb, uint16_t* alt) {
+  float xf = u2f((uint32_t)xb << 16);
+  double x = (double)xf;
+  double g = gelu_tanh_d(x);
+  double lo = 0.0, hi = 0.0;
+  uint16_t y = round_d_to_bf16(g, &lo, &hi);
+  *alt = y;
+  if (isnan(g) || isinf(g) || lo == hi) return y;
+  const double c = sqrt(2.0 / 3.14159265358979323846);
+  double u2 = fabs(2.0 * c * (x + 0.044715 * x * x * x));
+  double win = ldexp(16.0 + 4.0 * u2, -24) * fabs(g) + ldexp(1.0, -147);
+  double mid = 0.5 * (lo + hi), a = fabs(g);
+  if (fabs(a - mid) <= win) {
+    double other = (a < mid) ? hi : lo;   /* the neighbour RN did not pick */
+    uint16_t sign = signbit(g) ? 0x8000 : 0;
+    if (other >= ldexp(1.0, 128)) *alt = (uint16_t)(0x7F80 | sign);
+    else *alt = (uint16_t)((f2u((float)other) >> 16) | sign);
+  }
+  return y;
+}
+
+/* Elementwise over n bf16 pre-activations: y (RN), alt (see above). */
+void oracle_gelu_bf16_array(const uint16_t* x, uint16_t* y, uint16_t* alt, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) y[i] = oracle_gelu_bf16(x[i], &alt[i]);
+}
+
+double oracle_gelu_double(double x) { return gelu_tanh_d(x); }

@@ -491,4 +491,91 @@ def pin_microbatch_accumulation(o):
     assert f2u(a) == f2u(whole)
 
 
+
+
+# ------------------------------------------------------------------ pins: fused gelu
+def _bf16_grid_sample():
+    allb = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    x = bf16_to_f32(allb)
+    return allb[np.isfinite(x) & (np.abs(x) < 30)], allb
+
+
+def gelu_decimal(x: float) -> float:
+    """tanh-GELU in its tanh form at 150 significant digits with Python's decimal module
+    (exp correctly rounded at the context precision; no libm; 150 digits absorb the
+    cancellation of 1 + tanh(u) for every x >= -14)."""
+    import decimal
+    with decimal.localcontext() as ctx:
+        ctx.prec = 150
+        X = decimal.Decimal(x)
+        pi = decimal.Decimal("3.14159265358979323846264338327950288419716939937510")
+        c = (2 / pi).sqrt()
+        u = c * (X + decimal.Decimal("0.044715") * X * X * X)
+        e2u = (2 * u).exp()
+        t = (e2u - 1) / (e2u + 1)
+        return float(decimal.Decimal("0.5") * X * (1 + t))
+
+
+def pin_gelu_double_vs_independent(o):
+    """The oracle's double gelu against a 50-digit decimal evaluation of the tanh form
+    (independent of libm; covers the negative tail), against torch's CPU float64
+    tanh-GELU where its 1 + tanh form does not cancel (|x| <= 4), and the exact identity
+    gelu(x) - gelu(-x) = x of the tanh form."""
+    g = np.random.Generator(np.random.PCG64(51))
+    xs = np.concatenate([g.standard_normal(300) * 3, g.uniform(-14, 12, 300),
+                         [0.0, 1.0, -1.0, 5.5, -5.5, -7.17, -9.0, -11.5]])
+    mine = np.array([o.gelu_double(x) for x in xs])
+    ref = np.array([gelu_decimal(x) for x in xs])
+    # double evaluation error: exp of an argument carrying |2u| * 2^-53 absolute error
+    u2 = np.abs(2 * np.sqrt(2 / np.pi) * (xs + 0.044715 * xs ** 3))
+    tol = (8 + 2 * u2) * 2.0 ** -52 * np.abs(ref)
+    assert (np.abs(mine - ref) <= tol).all(), np.max(np.abs(mine - ref) / np.abs(ref))
+    # torch evaluates the 1 + tanh(u) form, which loses ~|2u|/ln(10) digits to
+    # cancellation for negative x: compare where that loss is small
+    small = np.abs(xs) <= 2
+    t = torch.nn.functional.gelu(torch.from_numpy(xs[small]), approximate="tanh").numpy()
+    assert np.allclose(mine[small], t, rtol=1e-12, atol=1e-300), "torch"
+    sym = np.array([o.gelu_double(x) - o.gelu_double(-x) for x in xs[np.abs(xs) < 5]])
+    assert np.allclose(sym, xs[np.abs(xs) < 5], rtol=1e-14, atol=1e-14), "symmetry"
+
+
+def pin_gelu_bf16_rounding(o):
+    """y = RN_bf16(gelu(x)) for every finite bf16 x with |x| < 30: one rounding of the
+    double value (exact rational round-half-even here), specials by their limits, and
+    `alt` is either y or an adjacent bf16 value of the same sign."""
+    xs, _ = _bf16_grid_sample()
+    y, alt = o.gelu_bf16(xs)
+    for i in range(0, xs.size, 37):
+        gd = o.gelu_double(float(bf16_to_f32(xs[i:i + 1])[0]))
+        want = rn_binary(abs(Fraction(gd)), 7, -126, 128)
+        wb = (f2u(np.float32(float(want))) >> 16) | (0x8000 if gd < 0 or (gd == 0 and np.signbit(gd)) else 0)
+        assert y[i] == wb, (hex(xs[i]), hex(y[i]), hex(wb))
+    diff = y != alt
+    assert diff.mean() < 0.01
+    yd = y[diff].astype(np.int32)
+    ad = alt[diff].astype(np.int32)
+    assert ((yd ^ ad) & 0x8000 == 0).all() or ((yd & 0x7FFF) == 0).all()
+    assert (np.abs((yd & 0x7FFF) - (ad & 0x7FFF)) == 1).all()
+    sp = np.array([0x7F80, 0xFF80, 0x7FC0, 0x0000, 0x8000], np.uint16)
+    ys, _ = o.gelu_bf16(sp)
+    assert list(ys[:2]) == [0x7F80, 0x8000] and (ys[2] & 0x7FFF) > 0x7F80
+    assert list(ys[3:]) == [0x0000, 0x8000]
+
+
+def pin_gelu_quantize(o):
+    """The fused quantize is the plain bf16 quantize of y (and of alt)."""
+    g = np.random.Generator(np.random.PCG64(53))
+    x = f32_to_bf16_np((g.standard_normal(5000) * 4).astype(np.float32))
+    codes, amax, codes_alt, lo, hi = o.gelu_quantize_amax(x, E4M3, 0.05)
+    y, alt = o.gelu_bf16(x)
+    c2, a2 = o.quantize_amax(y, E4M3, 0.05)
+    assert (codes == c2).all() and f2u(amax) == f2u(a2)
+    assert f2u(lo) <= f2u(amax) <= f2u(hi)
+
+
+def f32_to_bf16_np(v: np.ndarray) -> np.ndarray:
+    u = v.view(np.uint32)
+    return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -49,8 +49,15 @@ MUTANTS = [
      "float mx = oracle_fp8_max(formats[t] ? ORC_E4M3 : ORC_E5M2);"),
     ("dequant_divides", "float y = oracle_fp8_decode(fmt, src[i]) * scale;",
      "float y = oracle_fp8_decode(fmt, src[i]) / scale;"),
-    ("bf16_truncates", "double r = ldexp(nearbyint(ldexp(a, 7 - e)), e - 7);",
-     "double r = ldexp(trunc(ldexp(a, 7 - e)), e - 7);"),
+    ("bf16_truncates", "double r = ldexp(nearbyint(ldexp(a, 7 - e)), e - 7);   /*",
+     "double r = ldexp(trunc(ldexp(a, 7 - e)), e - 7);   /*"),
+    ("gelu_bf16_truncates", "double r = ldexp(nearbyint(ldexp(a, 7 - e)), e - 7);  /* nearest bf16",
+     "double r = ldexp(trunc(ldexp(a, 7 - e)), e - 7);  /* nearest bf16"),
+    ("gelu_cubic_coefficient", "const double u = c * (x + 0.044715 * x * x * x);",
+     "const double u = c * (x + 0.04715 * x * x * x);"),
+    ("gelu_half_argument", "return x / (1.0 + exp(-2.0 * u));", "return x / (1.0 + exp(-u));"),
+    ("gelu_neg_inf_kept", "if (isinf(x)) return x > 0 ? x : -0.0;", "if (isinf(x)) return x;"),
+    ("gelu_bf16_sign_dropped", "uint16_t sign = signbit(v) ? 0x8000 : 0;", "uint16_t sign = 0;"),
     ("dequant_nan_unsigned", "uint32_t nan_bits = 0x7FC00000u | ((uint32_t)(src[i] & 0x80) << 24);",
      "uint32_t nan_bits = 0x7FC00000u;"),
 ]
