@@ -291,7 +291,9 @@ uint16_t oracle_gelu_bf16(uint16_t xb, uint16_t* alt) {
   double win = ldexp(16.0 + 4.0 * u2, -24) * fabs(g) + ldexp(1.0, -147);
   double mid = 0.5 * (lo + hi), a = fabs(g);
   if (fabs(a - mid) <= win) {
-    double other = (a < mid) ? hi : lo;   /* the neighbour RN did not pick */
+    /* the neighbour RN did not pick (at an exact tie RN picked the even one) */
+    double picked = (double)u2f((uint32_t)(y & 0x7FFF) << 16);
+    double other = (picked == lo) ? hi : lo;
     uint16_t sign = signbit(g) ? 0x8000 : 0;
     if (other >= ldexp(1.0, 128)) *alt = (uint16_t)(0x7F80 | sign);
     else *alt = (uint16_t)((f2u((float)other) >> 16) | sign);

@@ -562,6 +562,23 @@ def pin_gelu_bf16_rounding(o):
     assert list(ys[3:]) == [0x0000, 0x8000]
 
 
+def pin_gelu_ties_offer_both(o):
+    """For tiny x, exp(-2u) rounds to 1 and gelu(x) = x/2 exactly; for bf16 x just above
+    the normal minimum with an odd last bit, x/2 is an exact tie between two bf16
+    subnormals.  RN picks the even one, and since the tie is inside any error window the
+    other one must be offered as `alt` (both signs)."""
+    m = np.arange(1, 128, 2, dtype=np.uint16)
+    for sign in (0, 0x8000):
+        xs = (0x0080 | m | sign).astype(np.uint16)      # (1 + m/128) * 2^-126, m odd
+        y, alt = o.gelu_bf16(xs)
+        lo = ((0x0040 | (m >> 1)) | sign).astype(np.uint16)   # (64 + (m-1)/2) * 2^-133
+        hi = (lo + 1).astype(np.uint16)
+        even = np.where((lo & 1) == 0, lo, hi)
+        odd = np.where((lo & 1) == 0, hi, lo)
+        assert (y == even).all(), (y[:4], even[:4])
+        assert (alt == odd).all(), (alt[:4], odd[:4])
+
+
 def pin_gelu_quantize(o):
     """The fused quantize is the plain bf16 quantize of y (and of alt)."""
     g = np.random.Generator(np.random.PCG64(53))
