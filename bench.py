@@ -8,8 +8,9 @@ amax reset), on inputs already resident in HBM.  Default workload: the MLP at hi
 E4M3, history 16).  Prints one JSON line.
 
 Also measured in the same run: the batched update of 1152 tensors with history 1024
-(kernel time warm and cold, host wall time per call), a device-to-device copy as the
-achievable-bandwidth context, and the CPU oracle on the same step (cpu_baseline), whose
+(kernel time warm and cold, host wall time per call), dequantize, the gelu-fused
+quantize of the MLP's FFN activation against the unfused gelu-then-quantize sequence,
+a device-to-device copy as the achievable-bandwidth context, and the CPU oracle on the same step (cpu_baseline), whose
 output is compared byte for byte with the GPU's first step.
 """
 from __future__ import annotations
@@ -81,6 +82,8 @@ def main():
     ap.add_argument("--workload", default="mlp_4096",
                     choices=["single_1024", "mlp_4096", "grad_8192x16384", "mlp_12288"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-gelu", action="store_true",
+                    help="skip the gelu-fused quantize measurement")
     ap.add_argument("--update-calls", type=int, default=200)
     ap.add_argument("--rotate", type=int, default=3,
                     help="input/output sets used in turn by successive steps")
@@ -261,6 +264,56 @@ def main():
     dq_bytes = 3 * w.tensors[big].data.size + 4
     del dq_out
 
+    # ------------------------------------------------------------ gelu-fused quantize
+    # (not in the step) the FFN activation of mlp_4096: bf16 pre-activation (2048,4,16384)
+    # -> gelu -> E4M3 + amax in one kernel, against the unfused sequence (torch's tanh
+    # gelu writing the bf16 activation, then the plain quantize reading it back)
+    gelu_out = None
+    if not args.no_gelu:
+        gw = workloads.make("mlp_4096_preact", threads=threads)
+        gsets = [torch.from_numpy(gw.tensors[0].data.reshape(-1).view(np.int16)).view(
+            torch.bfloat16).to(dev)]
+        gsets.append(gsets[0].clone())
+        gn = gsets[0].numel()
+        gdst = torch.empty(gn, dtype=torch.uint8, device=dev)
+        gy = torch.empty(gn, dtype=torch.bfloat16, device=dev)
+        gscale = torch.tensor([0.0078125], dtype=torch.float32, device=dev)
+        gamax = torch.zeros(1, dtype=torch.float32, device=dev)
+
+        def fused(i):
+            d.fp8_gelu_quantize_amax(gsets[i % 2], gdst, gscale, gamax, 0)
+
+        def unfused(i):
+            torch.ops.aten.gelu.out(gsets[i % 2], approximate="tanh", out=gy)
+            d.fp8_quantize_amax(gy, gdst, gscale, gamax, 0)
+
+        def timed(fn, reps=20):
+            for i in range(3):
+                fn(i)
+            torch.cuda.synchronize()
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                  for _ in range(reps)]
+            for i, (a, b) in enumerate(ev):
+                a.record()
+                fn(i)
+                b.record()
+            torch.cuda.synchronize()
+            return 1e3 * float(np.median([a.elapsed_time(b) for a, b in ev]))
+
+        f_us = timed(fused)
+        u_us = timed(unfused)
+        g_bytes = 3 * gn + 8
+        gelu_out = {"workload": gw.name, "elements": gn, "format": "e4m3",
+                    "fused_events_median_us": round(f_us, 3),
+                    "fused_gbps": round(g_bytes / (f_us * 1e-6) / 1e9, 1),
+                    "fused_alg_bytes": g_bytes,
+                    "unfused_events_median_us": round(u_us, 3),
+                    "unfused": "torch gelu(tanh) bf16 out + fp8_quantize_amax",
+                    "speedup": round(u_us / f_us, 3)}
+        log("gelu fused %.2f us (%.1f GB/s), unfused %.2f us" % (
+            f_us, g_bytes / (f_us * 1e-6) / 1e9, u_us))
+        del gsets, gdst, gy
+
     # ------------------------------------------------------------ copy context
     cbuf = torch.empty(1 << 27, dtype=torch.float32, device=dev)  # 512 MiB
     cdst = torch.empty_like(cbuf)
@@ -302,6 +355,7 @@ def main():
         "dequantize": {"tensor": w.tensors[big].name, "elements": int(w.tensors[big].data.size),
                        "out": "bf16", "events_median_us": round(dq_us, 3),
                        "gbps": round(dq_bytes / (dq_us * 1e-6) / 1e9, 1)},
+        "gelu_quantize": gelu_out,
         "copy_d2d_gbps": round(copy_gbps, 1),
         "roofline": {"bound": "hbm", "achieved": round(q_gbps, 1), "peak": PEAK_HBM_GBPS,
                      "unit": "GB/s", "frac": round(q_gbps / PEAK_HBM_GBPS, 4),

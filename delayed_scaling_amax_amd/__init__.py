@@ -6,6 +6,7 @@ the current HIP stream.  Functions carry the C names:
 
   fp8_quantize_amax(src, dst, scale, amax, format)          one tensor, fused amax
   fp8_multi_quantize_amax([(src, dst, scale, amax, format), ...])   one launch
+  fp8_gelu_quantize_amax(src, dst, scale, amax, format)     gelu(bf16 src), quantized
   fp8_dequantize(src, dst, scale, format)
   fp8_amax_and_scale_update(amax, amax_history, scale, scale_inv, formats,
                             algo=AMAX_MAX, margin=0, reset_amax=False)
@@ -52,12 +53,13 @@ def _load():
     vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
     lib.fp8_quantize_amax.argtypes = [vp, i32, vp, i64, i32, vp, vp, vp]
     lib.fp8_multi_quantize_amax.argtypes = [ctypes.POINTER(fp8q_tensor), i32, vp]
+    lib.fp8_gelu_quantize_amax.argtypes = [vp, i32, vp, i64, i32, vp, vp, vp]
     lib.fp8_dequantize.argtypes = [vp, i32, vp, i32, i64, vp, vp]
     lib.fp8_amax_and_scale_update.argtypes = [vp, vp, vp, vp, vp, i64, i64, i32, i32, i32, vp]
     lib.fp8_status_string.argtypes = [i32]
     lib.fp8_status_string.restype = ctypes.c_char_p
-    for f in ("fp8_quantize_amax", "fp8_multi_quantize_amax", "fp8_dequantize",
-              "fp8_amax_and_scale_update"):
+    for f in ("fp8_quantize_amax", "fp8_multi_quantize_amax", "fp8_gelu_quantize_amax",
+              "fp8_dequantize", "fp8_amax_and_scale_update"):
         getattr(lib, f).restype = i32
     return lib
 
@@ -96,6 +98,17 @@ def fp8_quantize_amax(src: torch.Tensor, dst: torch.Tensor, scale: torch.Tensor,
         raise ValueError("dst must be uint8 with src.numel() elements")
     with torch.cuda.device(src.device):
         _check("fp8_quantize_amax", lib.fp8_quantize_amax(
+            _dense(src, "src"), _DTYPE.get(src.dtype, -1), _dense(dst, "dst"), src.numel(),
+            int(format), _one_float(scale, "scale"), _one_float(amax, "amax"),
+            _stream(src.device)))
+
+
+def fp8_gelu_quantize_amax(src: torch.Tensor, dst: torch.Tensor, scale: torch.Tensor,
+                           amax: torch.Tensor, format: int) -> None:
+    if dst.dtype != torch.uint8 or dst.numel() != src.numel():
+        raise ValueError("dst must be uint8 with src.numel() elements")
+    with torch.cuda.device(src.device):
+        _check("fp8_gelu_quantize_amax", lib.fp8_gelu_quantize_amax(
             _dense(src, "src"), _DTYPE.get(src.dtype, -1), _dense(dst, "dst"), src.numel(),
             int(format), _one_float(scale, "scale"), _one_float(amax, "amax"),
             _stream(src.device)))
@@ -150,6 +163,7 @@ def fp8_amax_and_scale_update(amax: torch.Tensor, amax_history: torch.Tensor,
             int(margin), int(bool(reset_amax)), _stream(amax.device)))
 
 
-__all__ = ["fp8_quantize_amax", "fp8_multi_quantize_amax", "fp8_dequantize",
+__all__ = ["fp8_quantize_amax", "fp8_multi_quantize_amax", "fp8_gelu_quantize_amax",
+           "fp8_dequantize",
            "fp8_amax_and_scale_update", "fp8_status_string", "fp8q_tensor", "Fp8qError",
            "E4M3", "E5M2", "BF16", "F32", "AMAX_MAX", "AMAX_MOST_RECENT", "LIB_PATH", "lib"]

@@ -106,15 +106,24 @@ struct QEntry {
   int64_t numel;
   int32_t dtype;
   int32_t fmt;
+  int32_t gelu;     // producer prologue: quantize RN_bf16(gelu(x)) instead of x (bf16 only)
+  int32_t pad;
 };
 
-// Entries are sorted by kind (dtype * 2 + fmt): kind k occupies [run_end[k-1], run_end[k]).
+// Kinds: dtype * 2 + fmt for plain entries (0..3), 4 + fmt for gelu-prologue entries.
+constexpr int kQKinds = 6;
+__host__ __device__ __forceinline__ int entry_kind(const QEntry& e) {
+  return e.gelu ? 4 + e.fmt : e.dtype * 2 + e.fmt;
+}
+
+// Entries are sorted by kind: kind k occupies [run_end[k-1], run_end[k]).
 struct QTable {
   QEntry e[kQMaxEntries];
   int64_t total_full;
   int32_t n;
-  int32_t run_end[4];
+  int32_t run_end[kQKinds];
 };
+static_assert(sizeof(QTable) <= 4096, "the table travels as the kernel argument");
 
 // ---------------------------------------------------------------- element math
 template <int kFmt>
@@ -248,6 +257,77 @@ __device__ __forceinline__ uint2 quant8_f32(uint4 lo, uint4 hi, float s, float r
     out = patch_codes<kFmt>(out, mag, sign, xlim, 0x7F800000u);
   }
   return out;
+}
+
+// ---------------------------------------------------------------- gelu prologue
+// y = RN_bf16(gelu(x)) for bf16 x, tanh form, in binary32 through its exact identity
+// gelu(x) = x / (1 + 2^t), t = -2 log2(e) u, u = sqrt(2/pi) * (x + 0.044715 x^3).
+// With h = t/2 and m = 2^-|h| (never below 2^-126 where it matters, so the exp unit's
+// lack of subnormal results is harmless), m^2 = 2^-|t| and
+//   t <= 0:  y = x / (1 + 2^t)          = x * d
+//   t >  0:  y = x 2^-t / (1 + 2^-t)    = ((x * d) * m) * m,   d = 1 / (1 + m^2),
+// the last product rounding once into the subnormal range for the tiny tails.  No
+// branches: one exp2, one reciprocal.  Error of the binary32 value before the bf16
+// rounding: h carries 3 roundings (constants folded so 1 + 0.044715 x^2 is one fma),
+// amplified by |2u| through the exponential, plus a few ulps from exp2, the reciprocal
+// and the products -- below (3|2u| + 10) * 2^-24 relative.
+// Non-finite inputs: +inf gives +inf by itself; -inf and NaN give NaN and are patched
+// (gelu(-inf) = -0, gelu(NaN) = the default NaN with the input's sign).
+__device__ __forceinline__ float gelu_f32(float x) {
+  constexpr float kH = (float)(-0.7978845608028654 * 1.4426950408889634);
+  constexpr float kH3 = (float)(-0.7978845608028654 * 1.4426950408889634 * 0.044715);
+  const float h = x * __builtin_fmaf(kH3, x * x, kH);
+  const float m = __builtin_amdgcn_exp2f(-__builtin_fabsf(h));
+  const float d = __builtin_amdgcn_rcpf(1.0f + m * m);
+  const float p = x * d;
+  return h > 0.0f ? (p * m) * m : p;
+}
+
+typedef float gelu_f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 gelu_bf16x2 __attribute__((ext_vector_type(2)));
+
+// Two binary32 values -> packed bf16 (lo in bits 0-15), round to nearest even.
+__device__ __forceinline__ uint32_t pack_bf16_rne(float lo, float hi) {
+  const gelu_f32x2 v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, gelu_bf16x2));
+}
+
+// gelu of a non-finite bf16 input h (exponent all ones).
+__device__ __forceinline__ uint32_t gelu_special(uint32_t h) {
+  if ((h & 0x7FFFu) > 0x7F80u) return (h & 0x8000u) | 0x7FC0u;  // NaN
+  return (h & 0x8000u) ? 0x8000u : 0x7F80u;                        // -inf -> -0, +inf
+}
+
+// One bf16 pre-activation (low 16 bits of h) -> bf16 bits of its gelu.
+__device__ __forceinline__ uint32_t gelu_bf16(uint32_t h) {
+  if ((h & 0x7F80u) == 0x7F80u) return gelu_special(h);
+  return pack_bf16_rne(gelu_f32(as_float(h << 16)), 0.0f) & 0xFFFFu;
+}
+
+// Eight bf16 pre-activations -> eight bf16 gelu outputs (same packing).  A NaN result
+// can only come from a NaN or -inf input; such groups (rare, tested once per wave)
+// are patched from the inputs.
+__device__ __forceinline__ uint4 gelu8_bf16(uint4 w) {
+  const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+  uint32_t o[4];
+  bool nan = false;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const float lo = gelu_f32(as_float(u[k] << 16));
+    const float hi = gelu_f32(as_float(u[k] & 0xFFFF0000u));
+    nan |= (lo != lo) | (hi != hi);
+    o[k] = pack_bf16_rne(lo, hi);
+  }
+  if (__builtin_amdgcn_ballot_w64(nan) != 0) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t lo = u[k] & 0xFFFFu, hi = u[k] >> 16;
+      const uint32_t ol = (lo & 0x7F80u) == 0x7F80u ? gelu_special(lo) : (o[k] & 0xFFFFu);
+      const uint32_t oh = (hi & 0x7F80u) == 0x7F80u ? gelu_special(hi) : (o[k] >> 16);
+      o[k] = ol | (oh << 16);
+    }
+  }
+  return make_uint4(o[0], o[1], o[2], o[3]);
 }
 
 // ---------------------------------------------------------------- pass helpers
@@ -397,7 +477,7 @@ __device__ __forceinline__ Owned owned_chunks(int64_t f0, int64_t f1) {
 
 // Full-chunk range [f0, f1) of the run (same-kind tensors) holding table entry t.
 __device__ __forceinline__ void run_bounds(const QTable& tab, int t, int64_t& f0, int64_t& f1) {
-  const int kind = tab.e[t].dtype * 2 + tab.e[t].fmt;
+  const int kind = entry_kind(tab.e[t]);
   const int tb = kind > 0 ? tab.run_end[kind - 1] : 0;
   const int te = tab.run_end[kind];
   f0 = tab.e[tb].fbegin;
@@ -408,7 +488,7 @@ __device__ __forceinline__ void run_bounds(const QTable& tab, int t, int64_t& f0
 // Units [g0, g1) of a tensor, one element at a time through the IEEE divide.  Vector
 // unit g holds elements head + 8g .. head + 8g + 7; scalar element j (unit n_vec +
 // j/8) is tensor element j (head part) or j + 8*n_vec (tail part).
-template <bool kBF16, int kFmt>
+template <bool kBF16, int kFmt, bool kGelu>
 __device__ __forceinline__ void elementwise_units(const void* __restrict__ src,
                                                   uint8_t* __restrict__ dst, int64_t head,
                                                   int64_t n_vec, int64_t numel, int64_t g0,
@@ -426,7 +506,8 @@ __device__ __forceinline__ void elementwise_units(const void* __restrict__ src,
       }
       float x;
       if constexpr (kBF16) {
-        const uint32_t b = ((const uint16_t*)src)[i];
+        uint32_t b = ((const uint16_t*)src)[i];
+        if constexpr (kGelu) b = gelu_bf16(b);
         x = as_float(b << 16);
         acc = pk_max_u16(acc, b & 0x7FFFu);  // low half of the packed accumulator
       } else {
@@ -454,7 +535,7 @@ __device__ __forceinline__ void elementwise_units(const void* __restrict__ src,
 // speculatively (assuming that tensor's scale is in the window) before the per-tensor
 // constants are set up, so the block's first HBM requests do not wait for the scale
 // loads, the reciprocals and the barrier.
-template <bool kBF16, int kFmt>
+template <bool kBF16, int kFmt, bool kGelu>
 __device__ __forceinline__ void run_full_chunks(const QTable& tab, QShared& sh, int t_begin,
                                                 int t_end, bool setup) {
   constexpr int kL = kBF16 ? 1 : 2;                // 16-byte loads per group
@@ -566,7 +647,7 @@ __device__ __forceinline__ void run_full_chunks(const QTable& tab, QShared& sh, 
       load_pass(buf[kQDepth], pos[kQDepth].v, pos[kQDepth].j, pos[kQDepth].p);
     // the next passes' loads are issued; keep them ahead of this pass's arithmetic
     __builtin_amdgcn_sched_barrier(0);
-    const Pass& cur = buf[0];
+    Pass& cur = buf[0];
     const __amdgpu_buffer_rsrc_t rout = buffer_rsrc(
         c.v.out + (c.j - c.v.fbegin) * kQChunk + c.p * kU * kQBlock, kU * kQBlock * 8);
     uint2 o[kU];
@@ -574,6 +655,7 @@ __device__ __forceinline__ void run_full_chunks(const QTable& tab, QShared& sh, 
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
       if constexpr (kBF16) {
+        if constexpr (kGelu) cur.w[u][0] = gelu8_bf16(cur.w[u][0]);
         pm = pk_max_u16(pm, mag8_bf16(cur.w[u][0]));
         o[u] = codes8_bf16<kFmt>(cur.w[u][0], s, r);
       } else {
@@ -623,7 +705,7 @@ __device__ __forceinline__ void run_full_chunks(const QTable& tab, QShared& sh, 
 // Per tensor t: this block's full chunks if the scale is outside the window (all
 // element-wise), and the tensor's remainder -- the units past its last full chunk:
 // aligned groups, then the scalar head/tail -- done by block t mod G.
-template <bool kBF16, int kFmt>
+template <bool kBF16, int kFmt, bool kGelu>
 __device__ __forceinline__ void tensor_rest(const QTable& tab, QShared& sh, int t) {
   const QEntry& e = tab.e[t];
   const int64_t G = gridDim.x, b = blockIdx.x;
@@ -641,8 +723,8 @@ __device__ __forceinline__ void tensor_rest(const QTable& tab, QShared& sh, int 
     const int64_t stop = min(own.limit, e.fbegin + e.nfull);
     for (; jj < stop; jj += own.step) {
       const int64_t k = jj - e.fbegin;
-      elementwise_units<kBF16, kFmt>(e.src, e.dst, e.head, e.n_vec, e.numel, k * kQChunk,
-                                     (k + 1) * kQChunk, s, acc);
+      elementwise_units<kBF16, kFmt, kGelu>(e.src, e.dst, e.head, e.n_vec, e.numel,
+                                            k * kQChunk, (k + 1) * kQChunk, s, acc);
       touched = true;
     }
   }
@@ -657,22 +739,58 @@ __device__ __forceinline__ void tensor_rest(const QTable& tab, QShared& sh, int 
       const uint32_t xlim = uniform(sh.xlim[t]);
       for (int64_t g = u0 + threadIdx.x; g < e.n_vec; g += kQBlock) {
         uint2 o;
-        if constexpr (kBF16) o = quant8_bf16<kFmt>(load16(in + g), s, r, xlim, acc);
-        else o = quant8_f32<kFmt>(load16(in + 2 * g), load16(in + 2 * g + 1), s, r, xlim, acc);
+        if constexpr (kBF16) {
+          uint4 w = load16(in + g);
+          if constexpr (kGelu) w = gelu8_bf16(w);
+          o = quant8_bf16<kFmt>(w, s, r, xlim, acc);
+        } else {
+          o = quant8_f32<kFmt>(load16(in + 2 * g), load16(in + 2 * g + 1), s, r, xlim, acc);
+        }
         store8(out + g, o);
       }
-      elementwise_units<kBF16, kFmt>(e.src, e.dst, e.head, e.n_vec, e.numel,
-                                     u0 > e.n_vec ? u0 : e.n_vec, e.n_units, s, acc);
+      elementwise_units<kBF16, kFmt, kGelu>(e.src, e.dst, e.head, e.n_vec, e.numel,
+                                            u0 > e.n_vec ? u0 : e.n_vec, e.n_units, s, acc);
     } else {
-      elementwise_units<kBF16, kFmt>(e.src, e.dst, e.head, e.n_vec, e.numel, u0, e.n_units, s,
-                                     acc);
+      elementwise_units<kBF16, kFmt, kGelu>(e.src, e.dst, e.head, e.n_vec, e.numel, u0,
+                                            e.n_units, s, acc);
     }
   }
   if (touched) flush_amax<kBF16>(acc, sh, t);
 }
 
-// kSrc: bit 0 = the table holds bf16 sources, bit 1 = fp32 sources.  The bf16-only
-// instance (the common case) keeps its register budget to the bf16 path.
+// kSrc: bit 0 = the table holds plain bf16 sources, bit 1 = fp32 sources, bit 2 = bf16
+// sources with the gelu prologue.  Each instance keeps its register budget to the
+// paths it can meet (the bf16-only one is the common case).
+template <int kKind>
+struct KindTraits {
+  static constexpr bool kGelu = kKind >= 4;
+  static constexpr bool kBF16 = kKind != 2 && kKind != 3;
+  static constexpr int kFmt = kKind & 1;
+  static constexpr int kSrcBit = kGelu ? 4 : kBF16 ? 1 : 2;
+};
+
+// Phase 1 for the run of kind kKind, if the instance handles that kind.
+template <int kSrc, int kKind>
+__device__ __forceinline__ void phase1_run(const QTable& tab, QShared& sh, int& tb, bool& ready) {
+  using T = KindTraits<kKind>;
+  const int te = tab.run_end[kKind];
+  if constexpr ((kSrc & T::kSrcBit) != 0) {
+    if (te > tb) {
+      run_full_chunks<T::kBF16, T::kFmt, T::kGelu>(tab, sh, tb, te, !ready);
+      ready = true;
+    }
+  }
+  tb = te;
+}
+
+// Phase 2 for table entry t if its kind is kKind.
+template <int kSrc, int kKind>
+__device__ __forceinline__ void phase2_entry(const QTable& tab, QShared& sh, int t, int kind) {
+  using T = KindTraits<kKind>;
+  if constexpr ((kSrc & T::kSrcBit) != 0)
+    if (kind == kKind) tensor_rest<T::kBF16, T::kFmt, T::kGelu>(tab, sh, t);
+}
+
 template <int kSrc>
 __global__ __launch_bounds__(kQBlock) void quantize_amax_kernel(const QTable tab) {
   __shared__ QShared sh;
@@ -682,27 +800,22 @@ __global__ __launch_bounds__(kQBlock) void quantize_amax_kernel(const QTable tab
   // phase 1, one run of same-kind tensors at a time; the first run also sets up sh
   bool ready = false;
   int tb = 0;
-#pragma unroll
-  for (int kind = 0; kind < 4; ++kind) {
-    const int te = tab.run_end[kind];
-    const bool bf16 = kind < 2;
-    if (te > tb && ((kSrc & 1) || !bf16) && ((kSrc & 2) || bf16)) {
-      if (kind == 0) run_full_chunks<true, FP8Q_E4M3>(tab, sh, tb, te, !ready);
-      else if (kind == 1) run_full_chunks<true, FP8Q_E5M2>(tab, sh, tb, te, !ready);
-      else if (kind == 2) run_full_chunks<false, FP8Q_E4M3>(tab, sh, tb, te, !ready);
-      else run_full_chunks<false, FP8Q_E5M2>(tab, sh, tb, te, !ready);
-      ready = true;
-    }
-    tb = te;
-  }
+  phase1_run<kSrc, 0>(tab, sh, tb, ready);
+  phase1_run<kSrc, 1>(tab, sh, tb, ready);
+  phase1_run<kSrc, 2>(tab, sh, tb, ready);
+  phase1_run<kSrc, 3>(tab, sh, tb, ready);
+  phase1_run<kSrc, 4>(tab, sh, tb, ready);
+  phase1_run<kSrc, 5>(tab, sh, tb, ready);
   if (!ready) setup_shared(tab, sh);
   // phase 2
   for (int t = 0; t < n; ++t) {
-    const int kind = tab.e[t].dtype * 2 + tab.e[t].fmt;  // uniform
-    if ((kSrc & 1) && kind == 0) tensor_rest<true, FP8Q_E4M3>(tab, sh, t);
-    else if ((kSrc & 1) && kind == 1) tensor_rest<true, FP8Q_E5M2>(tab, sh, t);
-    else if ((kSrc & 2) && kind == 2) tensor_rest<false, FP8Q_E4M3>(tab, sh, t);
-    else if (kSrc & 2) tensor_rest<false, FP8Q_E5M2>(tab, sh, t);
+    const int kind = entry_kind(tab.e[t]);  // uniform
+    phase2_entry<kSrc, 0>(tab, sh, t, kind);
+    phase2_entry<kSrc, 1>(tab, sh, t, kind);
+    phase2_entry<kSrc, 2>(tab, sh, t, kind);
+    phase2_entry<kSrc, 3>(tab, sh, t, kind);
+    phase2_entry<kSrc, 4>(tab, sh, t, kind);
+    phase2_entry<kSrc, 5>(tab, sh, t, kind);
   }
   __syncthreads();
   // one global atomic per tensor this block saw a non-zero |x| in
@@ -720,7 +833,7 @@ static int validate_entry(const fp8q_tensor& t) {
 }
 
 // Split one tensor into aligned body and scalar head/tail.
-static void plan_entry(const fp8q_tensor& t, QEntry* e) {
+static void plan_entry(const fp8q_tensor& t, bool gelu, QEntry* e) {
   const int64_t esz = t.src_dtype == FP8Q_BF16 ? 2 : 4;
   const uintptr_t s = (uintptr_t)t.src, d = (uintptr_t)t.dst;
   int64_t head = -1;
@@ -736,6 +849,8 @@ static void plan_entry(const fp8q_tensor& t, QEntry* e) {
   e->numel = t.numel;
   e->dtype = t.src_dtype;
   e->fmt = t.format;
+  e->gelu = gelu ? 1 : 0;
+  e->pad = 0;
   if (head < 0 || t.numel < head + 8) {  // no aligned body: all elements scalar
     e->head = t.numel;
     e->n_vec = 0;
@@ -755,13 +870,18 @@ static int launch_table(QTable* tab, hipStream_t stream) {
   int st = current_device_cus(&cus);
   if (st != FP8Q_OK) return st;
   int src_kinds = 0;
-  for (int i = 0; i < tab->n; ++i) src_kinds |= tab->e[i].dtype == FP8Q_BF16 ? 1 : 2;
+  for (int i = 0; i < tab->n; ++i)
+    src_kinds |= tab->e[i].gelu ? 4 : tab->e[i].dtype == FP8Q_BF16 ? 1 : 2;
+  // tables hold either plain entries (any mix of bf16 and fp32) or gelu entries only
   const void* fn = src_kinds == 1   ? (const void*)quantize_amax_kernel<1>
                    : src_kinds == 2 ? (const void*)quantize_amax_kernel<2>
-                                    : (const void*)quantize_amax_kernel<3>;
+                   : src_kinds == 3 ? (const void*)quantize_amax_kernel<3>
+                   : src_kinds == 4 ? (const void*)quantize_amax_kernel<4>
+                                    : nullptr;
+  if (fn == nullptr) return FP8Q_EINVAL;
   // The grid-stride schedule needs every block resident at once: cap the blocks per
   // CU at what the instance's register use allows.
-  static std::atomic<int> fit[4];
+  static std::atomic<int> fit[8];
   int per_cu = fit[src_kinds].load(std::memory_order_relaxed);
   if (per_cu <= 0) {
     int occ = 0;
@@ -778,40 +898,48 @@ static int launch_table(QTable* tab, hipStream_t stream) {
   return launch_status(hipLaunchKernel(fn, dim3((unsigned)blocks), dim3(kQBlock), args, 0, stream));
 }
 
-}  // namespace fp8q
-
-using namespace fp8q;
-
-extern "C" int fp8_multi_quantize_amax(const fp8q_tensor* tensors, int n, void* stream) {
+// Quantize n tensors (with the gelu prologue on every one if `gelu`), at most
+// kQMaxEntries per launch.
+static int quantize_entries(const fp8q_tensor* tensors, int n, bool gelu, hipStream_t stream) {
   if (n < 0 || (n > 0 && tensors == nullptr)) return FP8Q_EINVAL;
   for (int i = 0; i < n; ++i) {
     int st = validate_entry(tensors[i]);
     if (st != FP8Q_OK) return st;
+    if (gelu && tensors[i].src_dtype != FP8Q_BF16) return FP8Q_EUNSUPPORTED;
   }
   for (int base = 0; base < n; base += kQMaxEntries) {
     QTable tab;
     tab.n = 0;
     tab.total_full = 0;
     const int end = n < base + kQMaxEntries ? n : base + kQMaxEntries;
-    // entries grouped by kind (dtype * 2 + format), stable within a kind
-    for (int kind = 0; kind < 4; ++kind) {
+    // entries grouped by kind, stable within a kind
+    for (int kind = 0; kind < kQKinds; ++kind) {
       for (int i = base; i < end; ++i) {
-        if (tensors[i].src_dtype * 2 + tensors[i].format != kind) continue;
+        const int k = gelu ? 4 + tensors[i].format : tensors[i].src_dtype * 2 + tensors[i].format;
+        if (k != kind) continue;
         QEntry& e = tab.e[tab.n++];
-        plan_entry(tensors[i], &e);
+        plan_entry(tensors[i], gelu, &e);
         e.fbegin = tab.total_full;
         tab.total_full += e.nfull;
       }
       tab.run_end[kind] = tab.n;
     }
-    int st = launch_table(&tab, (hipStream_t)stream);
+    int st = launch_table(&tab, stream);
     if (st != FP8Q_OK) return st;
   }
   return FP8Q_OK;
 }
 
-extern "C" int fp8_quantize_amax(const void* src, int src_dtype, uint8_t* dst, int64_t numel,
-                                 int format, const float* scale, float* amax, void* stream) {
+}  // namespace fp8q
+
+using namespace fp8q;
+
+extern "C" int fp8_multi_quantize_amax(const fp8q_tensor* tensors, int n, void* stream) {
+  return quantize_entries(tensors, n, false, (hipStream_t)stream);
+}
+
+static fp8q_tensor single_entry(const void* src, int src_dtype, uint8_t* dst, int64_t numel,
+                                int format, const float* scale, float* amax) {
   fp8q_tensor t;
   t.src = src;
   t.dst = dst;
@@ -820,5 +948,18 @@ extern "C" int fp8_quantize_amax(const void* src, int src_dtype, uint8_t* dst, i
   t.format = format;
   t.scale = scale;
   t.amax = amax;
-  return fp8_multi_quantize_amax(&t, 1, stream);
+  return t;
+}
+
+extern "C" int fp8_quantize_amax(const void* src, int src_dtype, uint8_t* dst, int64_t numel,
+                                 int format, const float* scale, float* amax, void* stream) {
+  const fp8q_tensor t = single_entry(src, src_dtype, dst, numel, format, scale, amax);
+  return quantize_entries(&t, 1, false, (hipStream_t)stream);
+}
+
+extern "C" int fp8_gelu_quantize_amax(const void* src, int src_dtype, uint8_t* dst,
+                                      int64_t numel, int format, const float* scale,
+                                      float* amax, void* stream) {
+  const fp8q_tensor t = single_entry(src, src_dtype, dst, numel, format, scale, amax);
+  return quantize_entries(&t, 1, true, (hipStream_t)stream);
 }

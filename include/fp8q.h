@@ -115,6 +115,30 @@ int fp8_quantize_amax(const void* src, int src_dtype, uint8_t* dst, int64_t nume
 int fp8_multi_quantize_amax(const fp8q_tensor* tensors, int n, void* stream);
 
 /*
+ * fp8_gelu_quantize_amax -- the activation between the two dense layers of the MLP,
+ * quantized in the kernel that produces it: the bf16 pre-activation x is read, the
+ * tanh-form gelu is applied, and the result goes through fp8_quantize_amax's quantize
+ * and amax without the bf16 activation tensor ever being written
+ * ("Fusion of Fp8 quantization and amax reduction kernels": the reproducer's
+ * dense -> gelu -> dense MLP, whose activations are quantized and amax-reduced in
+ * passes of their own).
+ *   y[i]    = RN_bf16(gelu(src[i])),  gelu(x) = x / (1 + exp(-2u)),
+ *             u = sqrt(2/pi) * (x + 0.044715 x^3)      (= 0.5 x (1 + tanh u) exactly)
+ *   dst[i]  = FP8(saturate(RN32(y[i] / *scale)))
+ *   *amax   = max(*amax, max_i |y[i]|)
+ * gelu is evaluated in binary32 (exp2 and reciprocal on the hardware units): y[i] is
+ * the bf16 rounding of a value within a relative (16 + 4|2u|) * 2^-24 of the exact
+ * gelu, so it is the correctly rounded bf16 of gelu(x) except where that lies within
+ * this distance of a bf16 rounding midpoint (then it may be the other neighbour).
+ * gelu(+inf) = +inf, gelu(-inf) = -0, gelu(NaN) = NaN with the sign of x.
+ *   src_dtype  FP8Q_BF16 (FP8Q_F32 returns FP8Q_EUNSUPPORTED).   format  as above.
+ *   numel, pointers, alignment, amax accumulation and errors as fp8_quantize_amax.
+ * Returns FP8Q_OK, FP8Q_EINVAL, FP8Q_EUNSUPPORTED or FP8Q_EHIP.
+ */
+int fp8_gelu_quantize_amax(const void* src, int src_dtype, uint8_t* dst, int64_t numel,
+                           int format, const float* scale, float* amax, void* stream);
+
+/*
  * fp8_dequantize -- y[i] = RN32(decode(src[i]) * *scale), written as fp32, or
  * rounded to nearest even into bf16 ("User Guide on Native XLA-FP8", section "JAX":
  * dequantization casts up and multiplies by the scale).  A NaN result is written as

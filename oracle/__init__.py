@@ -156,13 +156,26 @@ class Oracle:
                                    codes.size, float(scale))
         return dst
 
-    def gelu_bf16(self, x: np.ndarray):
+    def gelu_bf16(self, x: np.ndarray, threads: int = 1):
         """y = RN_bf16(gelu_tanh(x)) for bf16 bits x; returns (y, alt) uint16 arrays where
-        alt is the other admissible neighbour near a rounding midpoint (else alt == y)."""
-        x = np.ascontiguousarray(x, np.uint16)
+        alt is the other admissible neighbour near a rounding midpoint (else alt == y).
+        `threads` splits the array into contiguous pieces (elementwise, so the result
+        does not depend on it)."""
+        x = np.ascontiguousarray(x, np.uint16).reshape(-1)
         y = np.empty_like(x)
         alt = np.empty_like(x)
-        self.lib.oracle_gelu_bf16_array(x.ctypes.data, y.ctypes.data, alt.ctypes.data, x.size)
+
+        def run(lo, hi):
+            self.lib.oracle_gelu_bf16_array(x[lo:].ctypes.data, y[lo:].ctypes.data,
+                                            alt[lo:].ctypes.data, hi - lo)
+
+        n = x.size
+        if threads <= 1 or n < (1 << 20):
+            run(0, n)
+        else:
+            bounds = np.linspace(0, n, threads + 1).astype(np.int64)
+            with ThreadPoolExecutor(threads) as ex:
+                list(ex.map(run, bounds[:-1], bounds[1:]))
         return y, alt
 
     def gelu_double(self, x: float) -> float:
@@ -174,7 +187,7 @@ class Oracle:
         amax_hi).  codes/amax follow y = RN_bf16(gelu(x)); codes_alt are the codes of the
         admissible alternative y; [amax_lo, amax_hi] bounds the amax over every admissible
         choice (bit patterns)."""
-        y, alt = self.gelu_bf16(x)
+        y, alt = self.gelu_bf16(x, threads=threads)
         codes, amax = self.quantize_amax(y, fmt, scale, amax_in=amax_in, threads=threads)
         codes_alt, _ = self.quantize_amax(alt, fmt, scale, amax_in=amax_in, threads=threads)
         my = y.astype(np.uint32) & 0x7FFF

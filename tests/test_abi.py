@@ -19,8 +19,8 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted([
-        "fp8_quantize_amax", "fp8_multi_quantize_amax", "fp8_dequantize",
-        "fp8_amax_and_scale_update", "fp8_status_string"])
+        "fp8_quantize_amax", "fp8_multi_quantize_amax", "fp8_gelu_quantize_amax",
+        "fp8_dequantize", "fp8_amax_and_scale_update", "fp8_status_string"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -73,6 +73,14 @@ BAD = 0x1000  # a non-NULL pointer value that is never dereferenced (validation 
 def test_quantize_rejects_invalid(args):
     import delayed_scaling_amax_amd as d
     assert d.lib.fp8_quantize_amax(*args, None) == d.EINVAL
+    assert d.lib.fp8_gelu_quantize_amax(*args, None) == d.EINVAL
+
+
+def test_gelu_quantize_takes_bf16_only():
+    import delayed_scaling_amax_amd as d
+    assert d.lib.fp8_gelu_quantize_amax(BAD, d.F32, BAD, 10, 0, BAD, BAD, None) == d.EUNSUPPORTED
+    assert d.lib.fp8_gelu_quantize_amax(None, d.F32, None, 0, 0, BAD, BAD, None) == d.EUNSUPPORTED
+    assert d.lib.fp8_gelu_quantize_amax(None, d.BF16, None, 0, 1, BAD, BAD, None) == d.OK
 
 
 def test_multi_rejects_before_enqueue():

@@ -26,6 +26,9 @@ design notes list):
                     12288x49152 ~ N(0,1/12288), 49152x12288 ~ N(0,1/49152); output
                     gradient (2048,12288) ~ N(0,1e-4) (variance); 4x E4M3 + 1x E5M2,
                     history 1024.
+  mlp_4096_preact   the FFN pre-activation of mlp_4096, (2048,4,16384) bf16 ~ N(0,1/3):
+                    the dense output of U[0,1) inputs (E[x^2] = 1/3) through unit-
+                    variance fan_in weights; the input of the gelu-fused quantize.
 """
 from __future__ import annotations
 
@@ -233,12 +236,22 @@ def mlp_12288(threads=None, hidden=12288, ffn=49152, tokens=2048) -> Workload:
                     history_len=1024, first_scale=[1.0] * 5)
 
 
+def mlp_4096_preact(threads=None, ffn=16384, seq=2048, batch=4) -> Workload:
+    th = threads or default_threads()
+    h = _generate(6, 0, (seq, batch, ffn), np.uint16, _normal(math.sqrt(1.0 / 3.0)), th)
+    return Workload("mlp_4096_preact",
+                    "FFN pre-activation (%d,%d,%d) N(0,1/3) -> gelu -> E4M3, history 16"
+                    % (seq, batch, ffn),
+                    [QTensor("h", h, E4M3)], history_len=16, first_scale=[1.0])
+
+
 WORKLOADS = {
     "single_1024": single_1024,
     "mlp_4096": mlp_4096,
     "grad_8192x16384": grad_8192x16384,
     "update_1152": update_1152,
     "mlp_12288": mlp_12288,
+    "mlp_4096_preact": mlp_4096_preact,
 }
 
 
