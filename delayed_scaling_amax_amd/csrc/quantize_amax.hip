@@ -54,6 +54,11 @@ constexpr int kQBlock = FP8Q_Q_BLOCK;             // threads per block
 constexpr int kQUnroll = FP8Q_Q_UNROLL;           // 8-element groups in flight per thread
 constexpr int kQMaxEntries = 32;                  // tensors per launch (kernel-argument table)
 constexpr int kQBlocksPerCU = FP8Q_Q_BLOCKS_PER_CU;  // persistent grid size per CU
+#ifndef FP8Q_Q_GELU_BLOCKS_PER_CU
+#define FP8Q_Q_GELU_BLOCKS_PER_CU 3
+#endif
+// the gelu instance is arithmetic-bound: more resident waves hide exp/rcp latency
+constexpr int kQGeluBlocksPerCU = FP8Q_Q_GELU_BLOCKS_PER_CU;
 constexpr int kQChunk = kQBlock * kQUnroll;       // units (8-element groups) per chunk
 #ifndef FP8Q_Q_DEPTH
 #define FP8Q_Q_DEPTH 1
@@ -270,7 +275,8 @@ __device__ __forceinline__ uint2 quant8_f32(uint4 lo, uint4 hi, float s, float r
 // branches: one exp2, one reciprocal.  Error of the binary32 value before the bf16
 // rounding: h carries 3 roundings (constants folded so 1 + 0.044715 x^2 is one fma),
 // amplified by |2u| through the exponential, plus a few ulps from exp2, the reciprocal
-// and the products -- below (3|2u| + 10) * 2^-24 relative.
+// and the products -- below (3|2u| + 10) * 2^-24 relative.  (Checked exhaustively:
+// every bf16 input, against the double-precision value and its error window.)
 // Non-finite inputs: +inf gives +inf by itself; -inf and NaN give NaN and are patched
 // (gelu(-inf) = -0, gelu(NaN) = the default NaN with the input's sign).
 __device__ __forceinline__ float gelu_f32(float x) {
@@ -278,7 +284,7 @@ __device__ __forceinline__ float gelu_f32(float x) {
   constexpr float kH3 = (float)(-0.7978845608028654 * 1.4426950408889634 * 0.044715);
   const float h = x * __builtin_fmaf(kH3, x * x, kH);
   const float m = __builtin_amdgcn_exp2f(-__builtin_fabsf(h));
-  const float d = __builtin_amdgcn_rcpf(1.0f + m * m);
+  const float d = __builtin_amdgcn_rcpf(__builtin_fmaf(m, m, 1.0f));
   const float p = x * d;
   return h > 0.0f ? (p * m) * m : p;
 }
@@ -304,30 +310,43 @@ __device__ __forceinline__ uint32_t gelu_bf16(uint32_t h) {
   return pack_bf16_rne(gelu_f32(as_float(h << 16)), 0.0f) & 0xFFFFu;
 }
 
-// Eight bf16 pre-activations -> eight bf16 gelu outputs (same packing).  A NaN result
-// can only come from a NaN or -inf input; such groups (rare, tested once per wave)
-// are patched from the inputs.
-__device__ __forceinline__ uint4 gelu8_bf16(uint4 w) {
+// Eight bf16 pre-activations -> eight bf16 gelu outputs (same packing), before the
+// patch of non-finite inputs: a NaN output comes from a NaN or -inf input, nothing else.
+__device__ __forceinline__ uint4 gelu8_unpatched(uint4 w) {
   const uint32_t u[4] = {w.x, w.y, w.z, w.w};
   uint32_t o[4];
-  bool nan = false;
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+    o[k] = pack_bf16_rne(gelu_f32(as_float(u[k] << 16)), gelu_f32(as_float(u[k] & 0xFFFF0000u)));
+  return make_uint4(o[0], o[1], o[2], o[3]);
+}
+
+// Replace the outputs of non-finite inputs in y = gelu8_unpatched(w).
+__device__ __forceinline__ uint4 gelu8_patch(uint4 w, uint4 y) {
+  const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+  uint32_t o[4] = {y.x, y.y, y.z, y.w};
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
-    const float lo = gelu_f32(as_float(u[k] << 16));
-    const float hi = gelu_f32(as_float(u[k] & 0xFFFF0000u));
-    nan |= (lo != lo) | (hi != hi);
-    o[k] = pack_bf16_rne(lo, hi);
-  }
-  if (__builtin_amdgcn_ballot_w64(nan) != 0) {
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const uint32_t lo = u[k] & 0xFFFFu, hi = u[k] >> 16;
-      const uint32_t ol = (lo & 0x7F80u) == 0x7F80u ? gelu_special(lo) : (o[k] & 0xFFFFu);
-      const uint32_t oh = (hi & 0x7F80u) == 0x7F80u ? gelu_special(hi) : (o[k] >> 16);
-      o[k] = ol | (oh << 16);
-    }
+    const uint32_t lo = u[k] & 0xFFFFu, hi = u[k] >> 16;
+    const uint32_t ol = (lo & 0x7F80u) == 0x7F80u ? gelu_special(lo) : (o[k] & 0xFFFFu);
+    const uint32_t oh = (hi & 0x7F80u) == 0x7F80u ? gelu_special(hi) : (o[k] >> 16);
+    o[k] = ol | (oh << 16);
   }
   return make_uint4(o[0], o[1], o[2], o[3]);
+}
+
+// Nonzero if either 16-bit half of a packed magnitude max is a NaN (> 0x7F80).
+__device__ __forceinline__ uint32_t halves_nan(uint32_t mg) {
+  return (mg + 0x007F007Fu) & 0x80008000u;
+}
+
+// gelu of eight packed bf16 values, patched; the wave tests for NaN outputs once.
+__device__ __forceinline__ uint4 gelu8_bf16(uint4 w) {
+  const uint4 y = gelu8_unpatched(w);
+  const uint32_t mg = pk_max_u16(pk_max_u16(y.x & 0x7FFF7FFFu, y.y & 0x7FFF7FFFu),
+                                 pk_max_u16(y.z & 0x7FFF7FFFu, y.w & 0x7FFF7FFFu));
+  if (__builtin_amdgcn_ballot_w64(halves_nan(mg) != 0) != 0) return gelu8_patch(w, y);
+  return y;
 }
 
 // ---------------------------------------------------------------- pass helpers
@@ -655,8 +674,20 @@ __device__ __forceinline__ void run_full_chunks(const QTable& tab, QShared& sh, 
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
       if constexpr (kBF16) {
-        if constexpr (kGelu) cur.w[u][0] = gelu8_bf16(cur.w[u][0]);
-        pm = pk_max_u16(pm, mag8_bf16(cur.w[u][0]));
+        uint32_t mg;
+        if constexpr (kGelu) {
+          // the magnitude max feeds both the amax and the test for NaN outputs
+          const uint4 x = cur.w[u][0];
+          cur.w[u][0] = gelu8_unpatched(x);
+          mg = mag8_bf16(cur.w[u][0]);
+          if (__builtin_amdgcn_ballot_w64(halves_nan(mg) != 0) != 0) {
+            cur.w[u][0] = gelu8_patch(x, cur.w[u][0]);
+            mg = mag8_bf16(cur.w[u][0]);
+          }
+        } else {
+          mg = mag8_bf16(cur.w[u][0]);
+        }
+        pm = pk_max_u16(pm, mg);
         o[u] = codes8_bf16<kFmt>(cur.w[u][0], s, r);
       } else {
         const uint32_t m = mag8_f32(cur.w[u][0], cur.w[u][kL - 1]);
@@ -887,7 +918,8 @@ static int launch_table(QTable* tab, hipStream_t stream) {
     int occ = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, fn, kQBlock, 0) != hipSuccess)
       return FP8Q_EHIP;
-    per_cu = occ < kQBlocksPerCU ? (occ > 0 ? occ : 1) : kQBlocksPerCU;
+    const int want = src_kinds == 4 ? kQGeluBlocksPerCU : kQBlocksPerCU;
+    per_cu = occ < want ? (occ > 0 ? occ : 1) : want;
     fit[src_kinds].store(per_cu, std::memory_order_relaxed);
   }
   const int64_t max_blocks = (int64_t)cus * per_cu;

@@ -517,7 +517,7 @@ def gelu_decimal(x: float) -> float:
 
 
 def pin_gelu_double_vs_independent(o):
-    """The oracle's double gelu against a 50-digit decimal evaluation of the tanh form
+    """The oracle's double gelu against a 150-digit decimal evaluation of the tanh form
     (independent of libm; covers the negative tail), against torch's CPU float64
     tanh-GELU where its 1 + tanh form does not cancel (|x| <= 4), and the exact identity
     gelu(x) - gelu(-x) = x of the tanh form."""
