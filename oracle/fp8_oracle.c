@@ -307,3 +307,119 @@ void oracle_gelu_bf16_array(const uint16_t* x, uint16_t* y, uint16_t* alt, int64
 }
 
 double oracle_gelu_double(double x) { return gelu_tanh_d(x); }
+
+/* ------------------------------------------------------------------------------
+ * Producer-fused quantize of the LayerNorm output: the transformer block of the
+ * reproducer in "Fusion of Fp8 quantization and amax reduction kernels" (test.py:
+ * BasicTransformer applies Flax nn.LayerNorm() to its input and feeds the result to
+ * the MLP's first dense, whose FP8 dot quantizes it).  Readings (the pages give only
+ * the call):
+ *  L1 the defaults of that layer: per row of the last axis (length H), the mean mu
+ *     and the biased variance V = mean((x - mu)^2);
+ *     y = gamma * (x - mu) / sqrt(V + eps) + beta, with eps = 1e-6 passed as its
+ *     binary32 value (the layer works in binary32) and per-feature binary32 gamma
+ *     (scale) and beta (bias); no gamma means 1, no beta means 0.
+ *  L2 the dense casts its input to the model's dtype: the quantized tensor is
+ *     RN_bf16(y) of the exact y (evaluated here in double, sums compensated), then
+ *     quantized and reduced as a bf16 tensor (R1-R5).
+ *  L3 a row whose normalization is undefined (an inf or NaN input, or V + eps = 0)
+ *     gives NaN, and every NaN of y is the positive default NaN 0x7FC0.
+ * Admissible alternative.  A binary32 evaluation -- tree sums of depth D <= ceil(log2 H)
+ * + 6, mu' = RN(S/H), d' = RN(x - mu'), a corrected second pass e' = sum(d')/H,
+ * V' = sum(d'^2)/H - e'^2, r' = 1/sqrt(V' + eps), y' = RN(fma(d' - e', RN(gamma r'),
+ * beta)) -- differs from y by at most, to first order in u = 2^-24,
+ *   u (|gamma| r (|d| (D/2 + 6 + (D+1)(D+2) u A A_d r^2) + (D+2) A_d + (D+2)^2 u A) + |y|)
+ * (d = x - mu, r = 1/sqrt(V + eps), A = mean|x|, A_d = mean|d|): d' - e' is off by
+ * 2u|d| plus the residual error of the corrected mean, (D+2) u A_d, plus (D+2)^2 u^2 A
+ * left from the first mean; V' is off relatively by (D+4) u plus the cross term
+ * 2 (D+1)(D+2) u^2 A A_d / (V + eps), which r' halves and to which sqrt, the
+ * divide and gamma r' add 3 ulps.  The window is twice that with L = ceil(log2 H) + 10
+ * >= D + 4, plus 2^-147 for a subnormal y:
+ *   w = 2^-23 (|gamma| r (|d| (L/2 + 7 + L^2 2^-24 A A_d r^2) + L A_d + L^2 2^-24 A)
+ *              + |y|) + 2^-147;
+ * where y lies within w of a bf16 rounding midpoint, the other neighbour is returned
+ * in `alt` too (at an exact tie, the one RN did not pick). */
+static uint16_t other_bf16_neighbour(double v, double lo, double hi, uint16_t y) {
+  double picked = (double)u2f((uint32_t)(y & 0x7FFF) << 16);
+  double other = (picked == lo) ? hi : lo;
+  uint16_t sg = signbit(v) ? 0x8000 : 0;
+  if (other >= ldexp(1.0, 128)) return (uint16_t)(0x7F80 | sg);
+  return (uint16_t)((f2u((float)other) >> 16) | sg);
+}
+
+static int ceil_log2_i64(int64_t n) {
+  int l = 0;
+  while (((int64_t)1 << l) < n) ++l;
+  return l;
+}
+
+/* Neumaier's compensated sum step: s + c carries the running sum. */
+static void comp_add(double* s, double* c, double v) {
+  double t = *s + v;
+  *c += (fabs(*s) >= fabs(v)) ? (*s - t) + v : (v - t) + *s;
+  *s = t;
+}
+
+/* rows x H bf16 inputs (row-major) -> y (RN_bf16 of the exact LayerNorm), alt (see
+ * above), per-row mean and rstd = 1/sqrt(V + eps) in double (NaN for an undefined row).
+ * gamma, beta: H binary32 values each, or NULL. */
+void oracle_layernorm_bf16(const uint16_t* x, const float* gamma, const float* beta,
+                           float eps, int64_t rows, int64_t H, uint16_t* y, uint16_t* alt,
+                           double* mean_out, double* rstd_out) {
+  const double L = (double)ceil_log2_i64(H) + 10.0;
+  for (int64_t r = 0; r < rows; ++r) {
+    const uint16_t* xr = x + r * H;
+    uint16_t* yr = y + r * H;
+    uint16_t* ar = alt + r * H;
+    int finite = 1;
+    for (int64_t i = 0; i < H; ++i)
+      if ((xr[i] & 0x7F80) == 0x7F80) finite = 0;
+    if (!finite) {
+      for (int64_t i = 0; i < H; ++i) yr[i] = ar[i] = 0x7FC0;
+      mean_out[r] = NAN;
+      rstd_out[r] = NAN;
+      continue;
+    }
+    double s = 0.0, c = 0.0, sabs = 0.0;
+    for (int64_t i = 0; i < H; ++i) {
+      double v = (double)u2f((uint32_t)xr[i] << 16);
+      comp_add(&s, &c, v);
+      sabs += fabs(v);
+    }
+    const double mu = (s + c) / (double)H;
+    double sv = 0.0, cv = 0.0, sad = 0.0;
+    for (int64_t i = 0; i < H; ++i) {
+      double d = (double)u2f((uint32_t)xr[i] << 16) - mu;
+      comp_add(&sv, &cv, d * d);
+      sad += fabs(d);
+    }
+    const double V = (sv + cv) / (double)H;
+    const double A = sabs / (double)H, Ad = sad / (double)H;
+    const double rr = 1.0 / sqrt(V + (double)eps);
+    mean_out[r] = mu;
+    rstd_out[r] = rr;
+    for (int64_t i = 0; i < H; ++i) {
+      const double g = gamma ? (double)gamma[i] : 1.0;
+      const double b = beta ? (double)beta[i] : 0.0;
+      const double d = (double)u2f((uint32_t)xr[i] << 16) - mu;
+      const double v = g * d * rr + b;
+      if (isnan(v)) {
+        yr[i] = ar[i] = 0x7FC0;
+        continue;
+      }
+      double lo = 0.0, hi = 0.0;
+      const uint16_t yb = round_d_to_bf16(v, &lo, &hi);
+      yr[i] = ar[i] = yb;
+      if (isinf(v) || lo == hi) continue;
+      const double w =
+          ldexp(fabs(g) * rr *
+                        (fabs(d) * (L / 2 + 7 + L * L * ldexp(A * Ad * rr * rr, -24)) +
+                         L * Ad + L * L * ldexp(A, -24)) +
+                    fabs(v),
+                -23) +
+          ldexp(1.0, -147);
+      const double a = fabs(v), mid = 0.5 * (lo + hi);
+      if (fabs(a - mid) <= w) ar[i] = other_bf16_neighbour(v, lo, hi, yb);
+    }
+  }
+}

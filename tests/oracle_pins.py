@@ -590,6 +590,108 @@ def pin_gelu_quantize(o):
     assert f2u(lo) <= f2u(amax) <= f2u(hi)
 
 
+def _ln_case(seed, rows, H, lo_exp=-4, hi_exp=3, affine=True):
+    g = np.random.Generator(np.random.PCG64(seed))
+    x = f32_to_bf16_np((g.standard_normal(rows * H) * np.exp2(g.integers(lo_exp, hi_exp, rows * H))
+                        + g.standard_normal(rows * H).astype(np.float32) * 0.5)
+                       .astype(np.float32)).reshape(rows, H)
+    gamma = (1 + 0.2 * g.standard_normal(H)).astype(np.float32) if affine else None
+    beta = (0.3 * g.standard_normal(H)).astype(np.float32) if affine else None
+    return x, gamma, beta
+
+
+def pin_layernorm_vs_torch(o):
+    """Mean, rstd and y against torch's CPU float64 layer_norm (an independent
+    implementation: biased variance, eps inside the square root, affine gamma/beta);
+    y must be RN_bf16 of torch's value wherever that value is not within 1e-9 relative
+    of a bf16 rounding midpoint."""
+    for seed, rows, H, eps in ((61, 16, 4096, 1e-6), (62, 9, 1000, 1e-6), (63, 5, 8, 1e-3),
+                               (64, 7, 768, 0.0)):
+        x, gamma, beta = _ln_case(seed, rows, H)
+        y, alt, mean, rstd = o.layernorm_bf16(x, gamma, beta, eps)
+        xt = torch.from_numpy(bf16_to_f32(x.reshape(-1)).astype(np.float64).reshape(rows, H))
+        e32 = float(np.float32(eps))
+        ref = torch.nn.functional.layer_norm(xt, (H,), torch.from_numpy(gamma.astype(np.float64)),
+                                             torch.from_numpy(beta.astype(np.float64)),
+                                             eps=e32).numpy()
+        var, mu = torch.var_mean(xt, dim=1, unbiased=False)
+        assert np.allclose(mean, mu.numpy(), rtol=1e-12, atol=1e-15)
+        assert np.allclose(rstd, 1 / np.sqrt(var.numpy() + e32), rtol=1e-12)
+        # rounding of torch's value: f32 cast is RN to 24 bits, then RN to bf16 of that
+        # f32 (double rounding) is only wrong near midpoints, which are excluded
+        r32 = ref.astype(np.float32)
+        want = f32_to_bf16_np(r32)
+        b = r32.view(np.uint32)
+        mid_dist = np.abs((b & 0xFFFF).astype(np.int64) - 0x8000)
+        safe = mid_dist > 2
+        assert (y.reshape(-1)[safe.reshape(-1)] == want.reshape(-1)[safe.reshape(-1)]).all()
+
+
+def pin_layernorm_closed_forms(o):
+    """Rows with known answers: +-a alternating (mean 0, V = a^2, y = +-a/sqrt(a^2+eps),
+    exactly +-1 at eps = 0); a constant row gives beta exactly (d = 0) at eps > 0 and the
+    positive NaN at eps = 0 (0/0); inf or NaN in a row makes the whole row NaN; H = 1 is
+    a constant row; shifting integer rows by 128 and doubling at eps = 0 change nothing."""
+    H = 64
+    a = 3.0
+    row = np.where(np.arange(H) % 2 == 0, a, -a).astype(np.float32)
+    xb = f32_to_bf16_np(row).reshape(1, H)
+    y, alt, mean, rstd = o.layernorm_bf16(xb, None, None, 0.0)
+    assert (y == f32_to_bf16_np(np.where(np.arange(H) % 2 == 0, 1.0, -1.0).astype(np.float32))).all()
+    assert mean[0] == 0.0 and rstd[0] == 1 / 3.0
+    eps = float(np.float32(1e-2))
+    y, _, _, _ = o.layernorm_bf16(xb, None, None, 1e-2)
+    v = a / np.sqrt(a * a + eps)
+    assert (bf16_to_f32(y.reshape(-1))[::2] == bf16_to_f32(f32_to_bf16_np(np.float32([v])))[0]).all()
+    const = np.full((2, 16), 0x4040, np.uint16)                 # 3.0
+    beta = np.linspace(-2, 2, 16).astype(np.float32)
+    y, _, mean, rstd = o.layernorm_bf16(const, None, beta, 1e-6)
+    assert (y == f32_to_bf16_np(beta)[None, :]).all() and mean[0] == 3.0
+    y, alt, _, _ = o.layernorm_bf16(const, None, beta, 0.0)
+    assert (y == 0x7FC0).all() and (alt == 0x7FC0).all()
+    bad = np.tile(np.uint16(0x3F80), (3, 8))
+    bad[0, 3] = 0x7F80
+    bad[1, 5] = 0xFFC1
+    bad[2, 0] = 0xFF80
+    y, alt, mean, rstd = o.layernorm_bf16(bad, None, None, 1e-6)
+    assert (y == 0x7FC0).all() and np.isnan(mean).all() and np.isnan(rstd).all()
+    y, _, _, _ = o.layernorm_bf16(np.array([[0x4000], [0xC2F6]], np.uint16), None,
+                                  np.array([0.75], np.float32), 1e-6)
+    assert list(y[:, 0]) == [0x3F40, 0x3F40]
+    g = np.random.Generator(np.random.PCG64(65))
+    ints = g.integers(0, 128, (4, 256)).astype(np.float32)
+    y1, _, _, _ = o.layernorm_bf16(f32_to_bf16_np(ints), None, None, 0.0)
+    y2, _, _, _ = o.layernorm_bf16(f32_to_bf16_np(ints + 128), None, None, 0.0)
+    y3, _, _, _ = o.layernorm_bf16(f32_to_bf16_np(ints * 2), None, None, 0.0)
+    assert (y1 == y2).all() and (y1 == y3).all()
+
+
+def pin_layernorm_alternative(o):
+    """`alt` is y or an adjacent bf16 of the same sign, offered for a small fraction of
+    elements; an exact tie (a constant row, so y = beta, with beta a bf16 midpoint)
+    gives the even neighbour as y and the odd one as alt; the fused quantize equals the
+    plain quantize of y."""
+    x, gamma, beta = _ln_case(66, 32, 2048)
+    y, alt, _, _ = o.layernorm_bf16(x, gamma, beta, 1e-6)
+    diff = y != alt
+    assert 0 < diff.mean() < 0.02
+    yd, ad = y[diff].astype(np.int32), alt[diff].astype(np.int32)
+    assert ((yd ^ ad) & 0x8000 == 0).all()
+    assert (np.abs((yd & 0x7FFF) - (ad & 0x7FFF)) == 1).all()
+    mids = np.array([1 + 2 ** -8, -(1 + 3 * 2 ** -8), 1.5 * 2 ** -9 + 2 ** -17], np.float32)
+    const = np.full((1, 3), 0x3F80, np.uint16)
+    y, alt, _, _ = o.layernorm_bf16(const, None, mids, 1e-6)
+    m = mids.view(np.uint32)
+    lo = (m >> 16).astype(np.uint16)
+    assert ((y[0] & 1) == 0).all() and (np.abs(y[0].astype(int) - alt[0].astype(int)) == 1).all()
+    assert set(map(int, y[0])) | set(map(int, alt[0])) == set(map(int, lo)) | set(map(int, lo + 1))
+    codes, amax, codes_alt, a_lo, a_hi, _, _ = o.layernorm_quantize_amax(x, E4M3, 0.02, gamma,
+                                                                         beta, 1e-6)
+    c2, am2 = o.quantize_amax(o.layernorm_bf16(x, gamma, beta, 1e-6)[0], E4M3, 0.02)
+    assert (codes == c2).all() and f2u(amax) == f2u(am2)
+    assert f2u(a_lo) <= f2u(amax) <= f2u(a_hi)
+
+
 def f32_to_bf16_np(v: np.ndarray) -> np.ndarray:
     u = v.view(np.uint32)
     return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)

@@ -58,6 +58,19 @@ MUTANTS = [
     ("gelu_half_argument", "return x / (1.0 + exp(-2.0 * u));", "return x / (1.0 + exp(-u));"),
     ("gelu_neg_inf_kept", "if (isinf(x)) return x > 0 ? x : -0.0;", "if (isinf(x)) return x;"),
     ("gelu_bf16_sign_dropped", "uint16_t sign = signbit(v) ? 0x8000 : 0;", "uint16_t sign = 0;"),
+    ("ln_unbiased_variance", "const double V = (sv + cv) / (double)H;",
+     "const double V = (sv + cv) / (double)(H - 1);"),
+    ("ln_eps_outside_sqrt", "const double rr = 1.0 / sqrt(V + (double)eps);",
+     "const double rr = 1.0 / (sqrt(V) + (double)eps);"),
+    ("ln_beta_dropped", "const double v = g * d * rr + b;", "const double v = g * d * rr;"),
+    ("ln_gamma_dropped", "const double v = g * d * rr + b;", "const double v = d * rr + b;"),
+    ("ln_mean_off_by_one", "const double mu = (s + c) / (double)H;",
+     "const double mu = (s + c) / (double)(H + 1);"),
+    ("ln_nonfinite_row_kept", "for (int64_t i = 0; i < H; ++i) yr[i] = ar[i] = 0x7FC0;",
+     "for (int64_t i = 0; i < H; ++i) yr[i] = ar[i] = xr[i];"),
+    ("ln_nan_negative", "        yr[i] = ar[i] = 0x7FC0;\n        continue;",
+     "        yr[i] = ar[i] = 0xFFC0;\n        continue;"),
+    ("ln_alt_never", "if (fabs(a - mid) <= w) ar[i]", "if (fabs(a - mid) < 0.0) ar[i]"),
     ("dequant_nan_unsigned", "uint32_t nan_bits = 0x7FC00000u | ((uint32_t)(src[i] & 0x80) << 24);",
      "uint32_t nan_bits = 0x7FC00000u;"),
 ]
