@@ -67,7 +67,7 @@ def _declare(lib):
     lib.oracle_gelu_bf16_array.restype = None
     lib.oracle_gelu_double.argtypes = [c.c_double]
     lib.oracle_gelu_double.restype = c.c_double
-    lib.oracle_layernorm_bf16.argtypes = [vp, vp, vp, c.c_float, i64, i64, vp, vp, vp, vp]
+    lib.oracle_layernorm_bf16.argtypes = [vp, vp, vp, c.c_float, i64, i64, vp, vp, vp, vp, vp]
     lib.oracle_layernorm_bf16.restype = None
     return lib
 
@@ -202,10 +202,11 @@ class Oracle:
 
     def layernorm_bf16(self, x: np.ndarray, gamma=None, beta=None, eps: float = 1e-6,
                        threads: int = 1):
-        """LayerNorm over the last axis of bf16 bits x (rows, H): returns (y, alt, mean,
-        rstd) -- y = RN_bf16 of the exact value, alt the admissible neighbour near a
-        rounding midpoint (else y), mean and rstd per row in double.  gamma/beta are
-        float32 arrays of length H or None.  Rows are split over `threads`."""
+        """LayerNorm over the last axis of bf16 bits x (rows, H): returns (y, y_lo, y_hi,
+        mean, rstd) -- y = RN_bf16 of the exact value, [y_lo, y_hi] the admissible range
+        of a binary32 evaluation (bf16 bits; y_lo == y == y_hi away from rounding
+        midpoints), mean and rstd per row in double.  gamma/beta are float32 arrays of
+        length H or None.  Rows are split over `threads`."""
         x = np.ascontiguousarray(x, np.uint16)
         H = x.shape[-1]
         x2 = x.reshape(-1, H)
@@ -215,7 +216,8 @@ class Oracle:
         assert g is None or g.size == H
         assert b is None or b.size == H
         y = np.empty_like(x2)
-        alt = np.empty_like(x2)
+        y_lo = np.empty_like(x2)
+        y_hi = np.empty_like(x2)
         mean = np.empty(rows, np.float64)
         rstd = np.empty(rows, np.float64)
 
@@ -224,8 +226,8 @@ class Oracle:
                 self.lib.oracle_layernorm_bf16(
                     x2[r0:].ctypes.data, None if g is None else g.ctypes.data,
                     None if b is None else b.ctypes.data, float(np.float32(eps)), r1 - r0, H,
-                    y[r0:].ctypes.data, alt[r0:].ctypes.data, mean[r0:].ctypes.data,
-                    rstd[r0:].ctypes.data)
+                    y[r0:].ctypes.data, y_lo[r0:].ctypes.data, y_hi[r0:].ctypes.data,
+                    mean[r0:].ctypes.data, rstd[r0:].ctypes.data)
 
         if threads <= 1 or rows < 64:
             run(0, rows)
@@ -233,23 +235,31 @@ class Oracle:
             bounds = np.linspace(0, rows, threads + 1).astype(np.int64)
             with ThreadPoolExecutor(threads) as ex:
                 list(ex.map(run, bounds[:-1], bounds[1:]))
-        return y.reshape(x.shape), alt.reshape(x.shape), mean, rstd
+        return (y.reshape(x.shape), y_lo.reshape(x.shape), y_hi.reshape(x.shape), mean, rstd)
 
     def layernorm_quantize_amax(self, x: np.ndarray, fmt: int, scale: float, gamma=None,
                                 beta=None, eps: float = 1e-6, amax_in: float = 0.0,
                                 threads: int = 1):
-        """Producer-fused quantize of LayerNorm(x): returns (codes, amax, codes_alt,
-        amax_lo, amax_hi, mean, rstd), as gelu_quantize_amax for the activation y."""
-        y, alt, mean, rstd = self.layernorm_bf16(x, gamma, beta, eps, threads=threads)
+        """Producer-fused quantize of LayerNorm(x): returns (codes, amax, codes_lo,
+        codes_hi, amax_lo, amax_hi, mean, rstd): codes/amax of y, the codes of the ends
+        of the admissible range (every admissible code lies between them in value, as
+        the quantize is monotone), and the bounds of the amax over every admissible
+        choice."""
+        y, y_lo, y_hi, mean, rstd = self.layernorm_bf16(x, gamma, beta, eps, threads=threads)
         codes, amax = self.quantize_amax(y, fmt, scale, amax_in=amax_in, threads=threads)
-        codes_alt, _ = self.quantize_amax(alt, fmt, scale, amax_in=amax_in, threads=threads)
-        my = y.astype(np.uint32) & 0x7FFF
-        ma = alt.astype(np.uint32) & 0x7FFF
+        codes_lo, _ = self.quantize_amax(y_lo, fmt, scale, amax_in=amax_in, threads=threads)
+        codes_hi, _ = self.quantize_amax(y_hi, fmt, scale, amax_in=amax_in, threads=threads)
+        ml = y_lo.astype(np.uint32) & 0x7FFF
+        mh = y_hi.astype(np.uint32) & 0x7FFF
+        crosses = ((y_lo & 0x8000) != 0) | (ml == 0)
+        crosses &= ((y_hi & 0x8000) == 0) | (mh == 0)
+        min_mag = np.where(crosses, 0, np.minimum(ml, mh))
         a_in = int(np.float32(amax_in).view(np.uint32))
-        lo = max(int(np.minimum(my, ma).max(initial=0)) << 16, a_in)
-        hi = max(int(np.maximum(my, ma).max(initial=0)) << 16, a_in)
-        return (codes.reshape(x.shape), amax, codes_alt.reshape(x.shape),
-                np.uint32(lo).view(np.float32), np.uint32(hi).view(np.float32), mean, rstd)
+        lo = max(int(min_mag.max(initial=0)) << 16, a_in)
+        hi = max(int(np.maximum(ml, mh).max(initial=0)) << 16, a_in)
+        return (codes.reshape(x.shape), amax, codes_lo.reshape(x.shape),
+                codes_hi.reshape(x.shape), np.uint32(lo).view(np.float32),
+                np.uint32(hi).view(np.float32), mean, rstd)
 
     def count_saturated(self, x: np.ndarray, fmt: int, scale: float) -> int:
         x, dt = self._src(x)

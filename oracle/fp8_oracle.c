@@ -336,17 +336,11 @@ double oracle_gelu_double(double x) { return gelu_tanh_d(x); }
  * divide and gamma r' add 3 ulps.  The window is twice that with L = ceil(log2 H) + 10
  * >= D + 4, plus 2^-147 for a subnormal y:
  *   w = 2^-23 (|gamma| r (|d| (L/2 + 7 + L^2 2^-24 A A_d r^2) + L A_d + L^2 2^-24 A)
- *              + |y|) + 2^-147;
- * where y lies within w of a bf16 rounding midpoint, the other neighbour is returned
- * in `alt` too (at an exact tie, the one RN did not pick). */
-static uint16_t other_bf16_neighbour(double v, double lo, double hi, uint16_t y) {
-  double picked = (double)u2f((uint32_t)(y & 0x7FFF) << 16);
-  double other = (picked == lo) ? hi : lo;
-  uint16_t sg = signbit(v) ? 0x8000 : 0;
-  if (other >= ldexp(1.0, 128)) return (uint16_t)(0x7F80 | sg);
-  return (uint16_t)((f2u((float)other) >> 16) | sg);
-}
-
+ *              + |y|) + 2^-147.
+ * Its absolute terms can exceed a bf16 spacing where |y| is small against the row's
+ * spread, so the admissible results form a range: every bf16 value from
+ * y_lo = RN_bf16(y - w) to y_hi = RN_bf16(y + w) (RN is monotone), which reduces to
+ * y alone away from rounding midpoints and holds both neighbours at an exact tie. */
 static int ceil_log2_i64(int64_t n) {
   int l = 0;
   while (((int64_t)1 << l) < n) ++l;
@@ -360,22 +354,23 @@ static void comp_add(double* s, double* c, double v) {
   *s = t;
 }
 
-/* rows x H bf16 inputs (row-major) -> y (RN_bf16 of the exact LayerNorm), alt (see
- * above), per-row mean and rstd = 1/sqrt(V + eps) in double (NaN for an undefined row).
- * gamma, beta: H binary32 values each, or NULL. */
+/* rows x H bf16 inputs (row-major) -> y (RN_bf16 of the exact LayerNorm), the
+ * admissible range [y_lo, y_hi] (see above), per-row mean and rstd = 1/sqrt(V + eps)
+ * in double (NaN for an undefined row).  gamma, beta: H binary32 values each, or NULL. */
 void oracle_layernorm_bf16(const uint16_t* x, const float* gamma, const float* beta,
-                           float eps, int64_t rows, int64_t H, uint16_t* y, uint16_t* alt,
-                           double* mean_out, double* rstd_out) {
+                           float eps, int64_t rows, int64_t H, uint16_t* y, uint16_t* y_lo,
+                           uint16_t* y_hi, double* mean_out, double* rstd_out) {
   const double L = (double)ceil_log2_i64(H) + 10.0;
   for (int64_t r = 0; r < rows; ++r) {
     const uint16_t* xr = x + r * H;
     uint16_t* yr = y + r * H;
-    uint16_t* ar = alt + r * H;
+    uint16_t* lr = y_lo + r * H;
+    uint16_t* hr = y_hi + r * H;
     int finite = 1;
     for (int64_t i = 0; i < H; ++i)
       if ((xr[i] & 0x7F80) == 0x7F80) finite = 0;
     if (!finite) {
-      for (int64_t i = 0; i < H; ++i) yr[i] = ar[i] = 0x7FC0;
+      for (int64_t i = 0; i < H; ++i) yr[i] = lr[i] = hr[i] = 0x7FC0;
       mean_out[r] = NAN;
       rstd_out[r] = NAN;
       continue;
@@ -404,13 +399,10 @@ void oracle_layernorm_bf16(const uint16_t* x, const float* gamma, const float* b
       const double d = (double)u2f((uint32_t)xr[i] << 16) - mu;
       const double v = g * d * rr + b;
       if (isnan(v)) {
-        yr[i] = ar[i] = 0x7FC0;
+        yr[i] = lr[i] = hr[i] = 0x7FC0;
         continue;
       }
-      double lo = 0.0, hi = 0.0;
-      const uint16_t yb = round_d_to_bf16(v, &lo, &hi);
-      yr[i] = ar[i] = yb;
-      if (isinf(v) || lo == hi) continue;
+      yr[i] = round_d_to_bf16(v, NULL, NULL);
       const double w =
           ldexp(fabs(g) * rr *
                         (fabs(d) * (L / 2 + 7 + L * L * ldexp(A * Ad * rr * rr, -24)) +
@@ -418,8 +410,8 @@ void oracle_layernorm_bf16(const uint16_t* x, const float* gamma, const float* b
                     fabs(v),
                 -23) +
           ldexp(1.0, -147);
-      const double a = fabs(v), mid = 0.5 * (lo + hi);
-      if (fabs(a - mid) <= w) ar[i] = other_bf16_neighbour(v, lo, hi, yb);
+      lr[i] = round_d_to_bf16(v - w, NULL, NULL);
+      hr[i] = round_d_to_bf16(v + w, NULL, NULL);
     }
   }
 }

@@ -15,6 +15,7 @@ oracle copies with planted mistakes and requires each mistake to fail at least o
 """
 from __future__ import annotations
 
+import math
 import os
 from fractions import Fraction
 
@@ -608,7 +609,7 @@ def pin_layernorm_vs_torch(o):
     for seed, rows, H, eps in ((61, 16, 4096, 1e-6), (62, 9, 1000, 1e-6), (63, 5, 8, 1e-3),
                                (64, 7, 768, 0.0)):
         x, gamma, beta = _ln_case(seed, rows, H)
-        y, alt, mean, rstd = o.layernorm_bf16(x, gamma, beta, eps)
+        y, _, _, mean, rstd = o.layernorm_bf16(x, gamma, beta, eps)
         xt = torch.from_numpy(bf16_to_f32(x.reshape(-1)).astype(np.float64).reshape(rows, H))
         e32 = float(np.float32(eps))
         ref = torch.nn.functional.layer_norm(xt, (H,), torch.from_numpy(gamma.astype(np.float64)),
@@ -636,56 +637,90 @@ def pin_layernorm_closed_forms(o):
     a = 3.0
     row = np.where(np.arange(H) % 2 == 0, a, -a).astype(np.float32)
     xb = f32_to_bf16_np(row).reshape(1, H)
-    y, alt, mean, rstd = o.layernorm_bf16(xb, None, None, 0.0)
+    y, _, _, mean, rstd = o.layernorm_bf16(xb, None, None, 0.0)
     assert (y == f32_to_bf16_np(np.where(np.arange(H) % 2 == 0, 1.0, -1.0).astype(np.float32))).all()
     assert mean[0] == 0.0 and rstd[0] == 1 / 3.0
     eps = float(np.float32(1e-2))
-    y, _, _, _ = o.layernorm_bf16(xb, None, None, 1e-2)
+    y = o.layernorm_bf16(xb, None, None, 1e-2)[0]
     v = a / np.sqrt(a * a + eps)
     assert (bf16_to_f32(y.reshape(-1))[::2] == bf16_to_f32(f32_to_bf16_np(np.float32([v])))[0]).all()
     const = np.full((2, 16), 0x4040, np.uint16)                 # 3.0
     beta = np.linspace(-2, 2, 16).astype(np.float32)
-    y, _, mean, rstd = o.layernorm_bf16(const, None, beta, 1e-6)
+    y, _, _, mean, rstd = o.layernorm_bf16(const, None, beta, 1e-6)
     assert (y == f32_to_bf16_np(beta)[None, :]).all() and mean[0] == 3.0
-    y, alt, _, _ = o.layernorm_bf16(const, None, beta, 0.0)
-    assert (y == 0x7FC0).all() and (alt == 0x7FC0).all()
+    y, y_lo, y_hi, _, _ = o.layernorm_bf16(const, None, beta, 0.0)
+    assert (y == 0x7FC0).all() and (y_lo == 0x7FC0).all() and (y_hi == 0x7FC0).all()
     bad = np.tile(np.uint16(0x3F80), (3, 8))
     bad[0, 3] = 0x7F80
     bad[1, 5] = 0xFFC1
     bad[2, 0] = 0xFF80
-    y, alt, mean, rstd = o.layernorm_bf16(bad, None, None, 1e-6)
+    y, _, _, mean, rstd = o.layernorm_bf16(bad, None, None, 1e-6)
     assert (y == 0x7FC0).all() and np.isnan(mean).all() and np.isnan(rstd).all()
-    y, _, _, _ = o.layernorm_bf16(np.array([[0x4000], [0xC2F6]], np.uint16), None,
-                                  np.array([0.75], np.float32), 1e-6)
+    y = o.layernorm_bf16(np.array([[0x4000], [0xC2F6]], np.uint16), None,
+                         np.array([0.75], np.float32), 1e-6)[0]
     assert list(y[:, 0]) == [0x3F40, 0x3F40]
     g = np.random.Generator(np.random.PCG64(65))
     ints = g.integers(0, 128, (4, 256)).astype(np.float32)
-    y1, _, _, _ = o.layernorm_bf16(f32_to_bf16_np(ints), None, None, 0.0)
-    y2, _, _, _ = o.layernorm_bf16(f32_to_bf16_np(ints + 128), None, None, 0.0)
-    y3, _, _, _ = o.layernorm_bf16(f32_to_bf16_np(ints * 2), None, None, 0.0)
+    y1 = o.layernorm_bf16(f32_to_bf16_np(ints), None, None, 0.0)[0]
+    y2 = o.layernorm_bf16(f32_to_bf16_np(ints + 128), None, None, 0.0)[0]
+    y3 = o.layernorm_bf16(f32_to_bf16_np(ints * 2), None, None, 0.0)[0]
     assert (y1 == y2).all() and (y1 == y3).all()
 
 
-def pin_layernorm_alternative(o):
-    """`alt` is y or an adjacent bf16 of the same sign, offered for a small fraction of
-    elements; an exact tie (a constant row, so y = beta, with beta a bf16 midpoint)
-    gives the even neighbour as y and the odd one as alt; the fused quantize equals the
-    plain quantize of y."""
+def _bf16_order(h: np.ndarray) -> np.ndarray:
+    """bf16 bits -> integers in value order (-0 and +0 equal)."""
+    h = h.astype(np.int64)
+    return np.where(h & 0x8000, -(h & 0x7FFF), h & 0x7FFF)
+
+
+def pin_layernorm_admissible_range(o):
+    """[y_lo, y_hi] holds y; it is y alone for most elements, a range wider than one
+    bf16 step only where |y| is small against the window's absolute terms; it equals
+    [y - w, y + w] rounded, checked against the window recomputed here from its formula
+    on a sample; an exact tie (a constant row gives y = beta exactly, beta a bf16
+    midpoint) has y even and the range holding both neighbours; the fused quantize
+    equals the plain quantize of y, and the amax bounds bracket it."""
     x, gamma, beta = _ln_case(66, 32, 2048)
-    y, alt, _, _ = o.layernorm_bf16(x, gamma, beta, 1e-6)
-    diff = y != alt
-    assert 0 < diff.mean() < 0.02
-    yd, ad = y[diff].astype(np.int32), alt[diff].astype(np.int32)
-    assert ((yd ^ ad) & 0x8000 == 0).all()
-    assert (np.abs((yd & 0x7FFF) - (ad & 0x7FFF)) == 1).all()
-    mids = np.array([1 + 2 ** -8, -(1 + 3 * 2 ** -8), 1.5 * 2 ** -9 + 2 ** -17], np.float32)
-    const = np.full((1, 3), 0x3F80, np.uint16)
-    y, alt, _, _ = o.layernorm_bf16(const, None, mids, 1e-6)
+    y, y_lo, y_hi, mean, rstd = o.layernorm_bf16(x, gamma, beta, 1e-6)
+    oy, ol, oh = _bf16_order(y), _bf16_order(y_lo), _bf16_order(y_hi)
+    assert (ol <= oy).all() and (oy <= oh).all()
+    assert 0 < (ol != oh).mean() < 0.05
+    # the window from its definition, on every element of row 3
+    H = 2048
+    L = math.ceil(math.log2(H)) + 10
+    xf = bf16_to_f32(x[3]).astype(np.float64)
+    mu = xf.mean()
+    d = xf - mu
+    r = 1 / np.sqrt((d * d).mean() + float(np.float32(1e-6)))
+    A, Ad = np.abs(xf).mean(), np.abs(d).mean()
+    g64, b64 = gamma.astype(np.float64), beta.astype(np.float64)
+    v = g64 * d * r + b64
+    w = 2.0 ** -23 * (np.abs(g64) * r * (np.abs(d) * (L / 2 + 7 + L * L * 2.0 ** -24 * A * Ad * r * r)
+                                       + L * Ad + L * L * 2.0 ** -24 * A) + np.abs(v)) + 2.0 ** -147
+    def rn_bf16_exact(val: float) -> float:
+        r = rn_binary(abs(Fraction(val)), 7, -126, 128)
+        return math.copysign(float("inf") if r is None else float(r), val)
+
+    for i in range(H):
+        lo_f = float(bf16_to_f32(y_lo[3, i:i + 1])[0])
+        hi_f = float(bf16_to_f32(y_hi[3, i:i + 1])[0])
+        # v and w carry double rounding (~2^-50 relative); the ends are compared where
+        # v -+ w is not within 2^-40 of a bf16 rounding midpoint
+        for end, val in ((lo_f, v[i] - w[i]), (hi_f, v[i] + w[i])):
+            near = rn_bf16_exact(val * (1 - 2.0 ** -40)) != rn_bf16_exact(val * (1 + 2.0 ** -40))
+            assert near or end == rn_bf16_exact(val), (i, end, val)
+    # ties with the even neighbour above and below, both signs
+    mids = np.array([1 + 2 ** -8, -(1 + 3 * 2 ** -8), 1.5 * 2 ** -9 + 2 ** -17, 1 + 3 * 2 ** -8,
+                     -(1 + 2 ** -8)], np.float32)
+    const = np.full((1, mids.size), 0x3F80, np.uint16)
+    y, y_lo, y_hi, _, _ = o.layernorm_bf16(const, None, mids, 1e-6)
     m = mids.view(np.uint32)
     lo = (m >> 16).astype(np.uint16)
-    assert ((y[0] & 1) == 0).all() and (np.abs(y[0].astype(int) - alt[0].astype(int)) == 1).all()
-    assert set(map(int, y[0])) | set(map(int, alt[0])) == set(map(int, lo)) | set(map(int, lo + 1))
-    codes, amax, codes_alt, a_lo, a_hi, _, _ = o.layernorm_quantize_amax(x, E4M3, 0.02, gamma,
+    assert ((y[0] & 1) == 0).all()
+    for k in range(mids.size):  # each range is exactly the two neighbours, in value order
+        assert {int(y_lo[0, k]), int(y_hi[0, k])} == {int(lo[k]), int(lo[k]) + 1}
+        assert _bf16_order(y_lo[0, k:k + 1])[0] < _bf16_order(y_hi[0, k:k + 1])[0]
+    codes, amax, c_lo, c_hi, a_lo, a_hi, _, _ = o.layernorm_quantize_amax(x, E4M3, 0.02, gamma,
                                                                          beta, 1e-6)
     c2, am2 = o.quantize_amax(o.layernorm_bf16(x, gamma, beta, 1e-6)[0], E4M3, 0.02)
     assert (codes == c2).all() and f2u(amax) == f2u(am2)

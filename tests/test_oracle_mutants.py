@@ -66,11 +66,14 @@ MUTANTS = [
     ("ln_gamma_dropped", "const double v = g * d * rr + b;", "const double v = d * rr + b;"),
     ("ln_mean_off_by_one", "const double mu = (s + c) / (double)H;",
      "const double mu = (s + c) / (double)(H + 1);"),
-    ("ln_nonfinite_row_kept", "for (int64_t i = 0; i < H; ++i) yr[i] = ar[i] = 0x7FC0;",
-     "for (int64_t i = 0; i < H; ++i) yr[i] = ar[i] = xr[i];"),
-    ("ln_nan_negative", "        yr[i] = ar[i] = 0x7FC0;\n        continue;",
-     "        yr[i] = ar[i] = 0xFFC0;\n        continue;"),
-    ("ln_alt_never", "if (fabs(a - mid) <= w) ar[i]", "if (fabs(a - mid) < 0.0) ar[i]"),
+    ("ln_nonfinite_row_kept", "for (int64_t i = 0; i < H; ++i) yr[i] = lr[i] = hr[i] = 0x7FC0;",
+     "for (int64_t i = 0; i < H; ++i) yr[i] = lr[i] = hr[i] = xr[i];"),
+    ("ln_nan_negative", "        yr[i] = lr[i] = hr[i] = 0x7FC0;\n        continue;",
+     "        yr[i] = lr[i] = hr[i] = 0xFFC0;\n        continue;"),
+    ("ln_window_dropped", "lr[i] = round_d_to_bf16(v - w, NULL, NULL);",
+     "lr[i] = round_d_to_bf16(v, NULL, NULL);"),
+    ("ln_window_one_sided", "hr[i] = round_d_to_bf16(v + w, NULL, NULL);",
+     "hr[i] = round_d_to_bf16(v, NULL, NULL);"),
     ("dequant_nan_unsigned", "uint32_t nan_bits = 0x7FC00000u | ((uint32_t)(src[i] & 0x80) << 24);",
      "uint32_t nan_bits = 0x7FC00000u;"),
 ]
