@@ -39,7 +39,7 @@ def log(msg):
 
 def kernel_hash() -> str:
     h = hashlib.sha256()
-    for name in ("quantize_amax.hip", "device_common.h", "host_common.h"):
+    for name in ("quantize_amax.hip", "quant_math.h", "device_common.h", "host_common.h"):
         with open(os.path.join(ROOT, "delayed_scaling_amax_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]

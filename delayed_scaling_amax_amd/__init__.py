@@ -7,6 +7,8 @@ the current HIP stream.  Functions carry the C names:
   fp8_quantize_amax(src, dst, scale, amax, format)          one tensor, fused amax
   fp8_multi_quantize_amax([(src, dst, scale, amax, format), ...])   one launch
   fp8_gelu_quantize_amax(src, dst, scale, amax, format)     gelu(bf16 src), quantized
+  fp8_layernorm_quantize_amax(x, dst, scale, amax, format, gamma=None, beta=None,
+                              eps=1e-6, mean=None, rstd=None)  LayerNorm(x), quantized
   fp8_dequantize(src, dst, scale, format)
   fp8_amax_and_scale_update(amax, amax_history, scale, scale_inv, formats,
                             algo=AMAX_MAX, margin=0, reset_amax=False)
@@ -54,12 +56,14 @@ def _load():
     lib.fp8_quantize_amax.argtypes = [vp, i32, vp, i64, i32, vp, vp, vp]
     lib.fp8_multi_quantize_amax.argtypes = [ctypes.POINTER(fp8q_tensor), i32, vp]
     lib.fp8_gelu_quantize_amax.argtypes = [vp, i32, vp, i64, i32, vp, vp, vp]
+    lib.fp8_layernorm_quantize_amax.argtypes = [vp, i32, vp, vp, ctypes.c_float, i64, i64, vp,
+                                                i32, vp, vp, vp, vp, vp]
     lib.fp8_dequantize.argtypes = [vp, i32, vp, i32, i64, vp, vp]
     lib.fp8_amax_and_scale_update.argtypes = [vp, vp, vp, vp, vp, i64, i64, i32, i32, i32, vp]
     lib.fp8_status_string.argtypes = [i32]
     lib.fp8_status_string.restype = ctypes.c_char_p
     for f in ("fp8_quantize_amax", "fp8_multi_quantize_amax", "fp8_gelu_quantize_amax",
-              "fp8_dequantize", "fp8_amax_and_scale_update"):
+              "fp8_layernorm_quantize_amax", "fp8_dequantize", "fp8_amax_and_scale_update"):
         getattr(lib, f).restype = i32
     return lib
 
@@ -114,6 +118,33 @@ def fp8_gelu_quantize_amax(src: torch.Tensor, dst: torch.Tensor, scale: torch.Te
             _stream(src.device)))
 
 
+def _opt_f32(t, n: int, name: str) -> int | None:
+    if t is None:
+        return None
+    if t.dtype != torch.float32 or t.numel() != n:
+        raise ValueError("%s must be a float32 tensor of %d elements" % (name, n))
+    return _dense(t, name)
+
+
+def fp8_layernorm_quantize_amax(x: torch.Tensor, dst: torch.Tensor, scale: torch.Tensor,
+                                amax: torch.Tensor, format: int, gamma=None, beta=None,
+                                eps: float = 1e-6, mean=None, rstd=None) -> None:
+    """LayerNorm over the last axis of x, quantized; mean/rstd (rows elements each) are
+    optional outputs."""
+    if x.dim() < 1:
+        raise ValueError("x must have a last axis")
+    hidden = x.shape[-1]
+    rows = x.numel() // hidden if hidden else 0
+    if dst.dtype != torch.uint8 or dst.numel() != x.numel():
+        raise ValueError("dst must be uint8 with x.numel() elements")
+    with torch.cuda.device(x.device):
+        _check("fp8_layernorm_quantize_amax", lib.fp8_layernorm_quantize_amax(
+            _dense(x, "x"), _DTYPE.get(x.dtype, -1), _opt_f32(gamma, hidden, "gamma"),
+            _opt_f32(beta, hidden, "beta"), float(eps), rows, hidden, _dense(dst, "dst"),
+            int(format), _one_float(scale, "scale"), _one_float(amax, "amax"),
+            _opt_f32(mean, rows, "mean"), _opt_f32(rstd, rows, "rstd"), _stream(x.device)))
+
+
 def fp8_multi_quantize_amax(entries) -> None:
     """entries: sequence of (src, dst, scale, amax, format)."""
     entries = list(entries)
@@ -164,6 +195,6 @@ def fp8_amax_and_scale_update(amax: torch.Tensor, amax_history: torch.Tensor,
 
 
 __all__ = ["fp8_quantize_amax", "fp8_multi_quantize_amax", "fp8_gelu_quantize_amax",
-           "fp8_dequantize",
+           "fp8_layernorm_quantize_amax", "fp8_dequantize",
            "fp8_amax_and_scale_update", "fp8_status_string", "fp8q_tensor", "Fp8qError",
            "E4M3", "E5M2", "BF16", "F32", "AMAX_MAX", "AMAX_MOST_RECENT", "LIB_PATH", "lib"]

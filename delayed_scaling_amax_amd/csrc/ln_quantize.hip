@@ -1,0 +1,363 @@
+// ln_quantize.hip -- LayerNorm output -> FP8 quantize + amax, the LayerNorm applied in
+// registers so its bf16 output is never written.
+//
+// What it computes: the transformer block of the reproducer in "Fusion of Fp8
+// quantization and amax reduction kernels" (test.py: BasicTransformer applies Flax
+// nn.LayerNorm() and feeds the result to the MLP's first dense, whose FP8 dot
+// quantizes it).  Per row of length H:
+//   mu = mean(x), V = mean((x - mu)^2), rstd = 1 / sqrt(V + eps),
+//   y = RN_bf16(gamma * (x - mu) * rstd + beta),
+// then code = FP8(saturate(RN32(y / scale))) and amax = max(amax, max|y|) exactly as
+// the plain quantize does ("User Guide on Native XLA-FP8", section "JAX").
+//
+// Design (gfx950; HBM-bound at 3 bytes/element plus 8 bytes per row of statistics):
+//  * One wavefront per row, persistent grid: the row (H <= 8192 bf16 = 16 KB) is
+//    loaded as 16-byte units into registers -- the wavefront's next row is loaded
+//    while the current one is reduced and written -- so every reduction is a
+//    wavefront butterfly, with no LDS round trip and no block barrier per row.
+//  * gamma and beta are staged once per block into LDS (zero-padded to the unit
+//    grid), read back per element.
+//  * Statistics in binary32 with tree sums (depth log2(8 kV) per lane + 6 across the
+//    wavefront) and a corrected second pass: mu' = RN(S/H); d' = RN(x - mu');
+//    e' = sum(d')/H and V' = sum(d'^2)/H - e'^2 remove the first mean's rounding
+//    error from both the deviations and the variance (rows whose mean is large
+//    against their spread lose no accuracy); y' = RN(fma(d' - e', RN(gamma rstd'),
+//    beta)).
+//  * Rows with inf/NaN inputs (or V + eps = 0) produce NaN, written as the positive
+//    default NaN 0x7FC0; its code is 0x7F.
+//  * The quantize of y' is the shared element math (corrected division by the scale,
+//    saturate, native OCP convert, fixed codes for huge quotients); the amax is the
+//    packed bf16 magnitude max -> wavefront -> LDS -> one global atomic per block.
+#include "device_common.h"
+#include "host_common.h"
+#include "quant_math.h"
+#include "fp8q.h"
+
+namespace fp8q {
+
+constexpr int kLBlock = 256;       // 4 wavefronts, one row each at a time
+constexpr int kLMaxH = 8192;       // 64 lanes x 16 units x 8 elements
+#ifndef FP8Q_LN_BLOCKS_PER_CU
+#define FP8Q_LN_BLOCKS_PER_CU 3
+#endif
+constexpr int kLBlocksPerCU = FP8Q_LN_BLOCKS_PER_CU;
+
+struct LnArgs {
+  const uint16_t* x;
+  const float* gamma;  // may be null: 1
+  const float* beta;   // may be null: 0
+  uint8_t* dst;
+  const float* scale;
+  uint32_t* amax;
+  float* mean_out;  // may be null
+  float* rstd_out;  // may be null
+  int64_t rows;
+  int32_t H;
+  int32_t nunits;  // H / 8
+  float eps;
+  int32_t pad;
+};
+
+typedef uint32_t ln_u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t ln_u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t ln_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+
+// Units u = lane + 64 k of one row; a unit past the row's end reads zeros (the
+// resource covers exactly the row).
+template <int kV>
+__device__ __forceinline__ void ln_load_row(uint4 (&w)[kV], __amdgpu_buffer_rsrc_t rs,
+                                            int lane) {
+#pragma unroll
+  for (int k = 0; k < kV; ++k) {
+    const ln_u32x4 v = __builtin_bit_cast(
+        ln_u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (uint32_t)(lane + 64 * k) * 16u, 0, 2));
+    w[k] = make_uint4(v[0], v[1], v[2], v[3]);
+  }
+}
+
+// Pairwise (tree) sum of N values in place; N a power of two.
+template <int N>
+__device__ __forceinline__ float tree_sum(float (&v)[N]) {
+#pragma unroll
+  for (int w = N / 2; w >= 1; w /= 2) {
+#pragma unroll
+    for (int i = 0; i < w; ++i) v[i] = v[i] + v[i + w];
+  }
+  return v[0];
+}
+
+// Sum over the 64 lanes by a butterfly: every lane ends with the same value (IEEE
+// addition is commutative, so partners compute identical sums at every step).
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v = v + __shfl_xor(v, off, 64);
+  return v;
+}
+
+__device__ __forceinline__ void wave_sum2(float& a, float& b) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    const float oa = __shfl_xor(a, off, 64), ob = __shfl_xor(b, off, 64);
+    a = a + oa;
+    b = b + ob;
+  }
+}
+
+__device__ __forceinline__ float lo_f32(uint32_t w) { return as_float(w << 16); }
+__device__ __forceinline__ float hi_f32(uint32_t w) { return as_float(w & 0xFFFF0000u); }
+
+struct LnQuant {
+  float s, r;
+  uint32_t xlim;
+  bool win;
+};
+
+// Make the packed row opaque to the compiler between passes (an empty asm that
+// rebinds the registers, emitting nothing): values derived from it are recomputed
+// rather than merged with, and kept live from, an earlier pass.
+template <int kV>
+__device__ __forceinline__ void rebind(uint4 (&w)[kV]) {
+#pragma unroll
+  for (int k = 0; k < kV; ++k)
+    __asm__ volatile("" : "+v"(w[k].x), "+v"(w[k].y), "+v"(w[k].z), "+v"(w[k].w));
+}
+
+// The 8 elements of a unit as binary32.
+__device__ __forceinline__ void unpack8(const uint4& w, float (&x)[8]) {
+  const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    x[2 * j] = lo_f32(u[j]);
+    x[2 * j + 1] = hi_f32(u[j]);
+  }
+}
+
+// Normalize, quantize and store one row held in w[] (units lane + 64 k).  The row
+// stays packed; each pass re-derives x (and d = RN(x - mu'), bit-identical every time)
+// unit by unit, so only the packed row and a few partial sums stay live.  Sums are
+// trees: 8 elements of a unit (depth 3), then the kV units (depth log2 kV), then the
+// wavefront (depth 6).
+template <int kFmt, int kV, bool kMasked>
+__device__ __forceinline__ void ln_row(uint4 (&w)[kV], const LnArgs& a, int64_t row,
+                                       int lane, const float* __restrict__ lg,
+                                       const float* __restrict__ lb, const LnQuant& q,
+                                       uint32_t& acc) {
+  const float Hf = (float)a.H;
+  // pass 1: mean (units past the row read as zeros)
+  float p1[kV];
+#pragma unroll
+  for (int k = 0; k < kV; ++k) {
+    float x[8];
+    unpack8(w[k], x);
+    p1[k] = tree_sum(x);
+  }
+  const float mu = wave_sum(tree_sum(p1)) / Hf;
+  // pass 2: deviations from mu', their sum and sum of squares
+  rebind(w);
+  float s1[kV], s2[kV];
+#pragma unroll
+  for (int k = 0; k < kV; ++k) {
+    float x[8], sq[8];
+    unpack8(w[k], x);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      x[j] = x[j] - mu;
+      sq[j] = x[j] * x[j];
+    }
+    s1[k] = tree_sum(x);
+    s2[k] = tree_sum(sq);
+    if (kMasked && lane + 64 * k >= a.nunits) s1[k] = s2[k] = 0.0f;
+  }
+  float t1 = tree_sum(s1), t2 = tree_sum(s2);
+  wave_sum2(t1, t2);
+  const float e = t1 / Hf;
+  float var = __builtin_fmaf(-e, e, t2 / Hf);
+  var = var < 0.0f ? 0.0f : var;  // rounding can dip below 0; a NaN stays NaN
+  const float rstd = 1.0f / __builtin_sqrtf(var + a.eps);
+  if (lane == 0) {
+    if (a.mean_out) a.mean_out[row] = mu + e;
+    if (a.rstd_out) a.rstd_out[row] = rstd;
+  }
+  // pass 3: y, its bf16 rounding, the codes and the amax
+  rebind(w);
+  const __amdgpu_buffer_rsrc_t out = ln_rsrc(a.dst + row * (int64_t)a.H, (uint32_t)a.H);
+#pragma unroll
+  for (int k = 0; k < kV; ++k) {
+    const int unit = lane + 64 * k;
+    const float4* g4 = (const float4*)(lg + 8 * unit);
+    const float4* b4 = (const float4*)(lb + 8 * unit);
+    const float4 g0 = g4[0], g1 = g4[1], b0 = b4[0], b1 = b4[1];
+    const float gv[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+    const float bv[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+    float x[8], y[8];
+    unpack8(w[k], x);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) y[j] = __builtin_fmaf((x[j] - mu) - e, gv[j] * rstd, bv[j]);
+    uint4 yw = make_uint4(pack_bf16_rne(y[0], y[1]), pack_bf16_rne(y[2], y[3]),
+                          pack_bf16_rne(y[4], y[5]), pack_bf16_rne(y[6], y[7]));
+    uint32_t mg = mag8_bf16(yw);
+    if (__builtin_amdgcn_ballot_w64(halves_nan(mg) != 0) != 0) {  // rare: NaN rows
+      uint32_t o[4] = {yw.x, yw.y, yw.z, yw.w};
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        const uint32_t l = (o[h] & 0x7FFFu) > 0x7F80u ? 0x7FC0u : (o[h] & 0xFFFFu);
+        const uint32_t u = ((o[h] >> 16) & 0x7FFFu) > 0x7F80u ? 0x7FC0u : (o[h] >> 16);
+        o[h] = l | (u << 16);
+      }
+      yw = make_uint4(o[0], o[1], o[2], o[3]);
+      mg = mag8_bf16(yw);
+    }
+    const bool valid = !kMasked || unit < a.nunits;
+    acc = pk_max_u16(acc, valid ? mg : 0u);
+    uint2 c;
+    if (q.win) {
+      c = codes8_bf16<kFmt>(yw, q.s, q.r);
+      if (max_halves(mg) >= q.xlim) c = patch8_bf16<kFmt>(c, yw, q.xlim);
+    } else {  // scale outside the corrected-division window: IEEE divide per element
+      const uint32_t u[4] = {yw.x, yw.y, yw.z, yw.w};
+      uint32_t cw[2] = {0, 0};
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float v = (j & 1) ? hi_f32(u[j >> 1]) : lo_f32(u[j >> 1]);
+        cw[j >> 2] |= code_ieee<kFmt>(v, q.s) << (8 * (j & 3));
+      }
+      c = make_uint2(cw[0], cw[1]);
+    }
+    __builtin_amdgcn_raw_buffer_store_b64(ln_u32x2{c.x, c.y}, out, (uint32_t)unit * 8u, 0, 0);
+    // keep each unit's work (LDS reads, arithmetic) from being hoisted into the
+    // previous one's, which would hold every unit's temporaries at once
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+template <int kFmt, int kV, bool kMasked>
+__global__ __launch_bounds__(kLBlock)
+void ln_quantize_kernel(const LnArgs a) {
+  extern __shared__ float lds[];  // gamma then beta, each 512 kV floats, zero-padded
+  __shared__ uint32_t block_amax;
+  constexpr int kPad = 512 * kV;
+  float* lg = lds;
+  float* lb = lds + kPad;
+  for (int i = threadIdx.x; i < kPad; i += kLBlock) {
+    const bool in = i < a.H;
+    lg[i] = in ? (a.gamma ? a.gamma[i] : 1.0f) : 0.0f;
+    lb[i] = in ? (a.beta ? a.beta[i] : 0.0f) : 0.0f;
+  }
+  if (threadIdx.x == 0) block_amax = 0;
+
+  LnQuant q;
+  q.s = uniform(*a.scale);
+  q.r = 1.0f / q.s;
+  q.win = (q.s >= 0x1p-80f) && (q.s <= 0x1p125f);
+  q.xlim = min(as_uint(q.s * 0x1p126f) >> 16, 0x7F80u);
+  __syncthreads();
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: SGPR
+  const int64_t nwaves = (int64_t)gridDim.x * (kLBlock / 64);
+  int64_t row = (int64_t)blockIdx.x * (kLBlock / 64) + wave;
+  const uint32_t row_bytes = (uint32_t)a.H * 2u;
+  uint32_t acc = 0;
+  uint4 wa[kV], wb[kV];
+  // two row buffers alternate so that the next row's loads are in flight while this
+  // row is reduced; the prefetch index is clamped so every load is unconditional
+  if (row < a.rows) ln_load_row<kV>(wa, ln_rsrc(a.x + row * a.H, row_bytes), lane);
+  while (row < a.rows) {
+    int64_t nxt = row + nwaves < a.rows ? row + nwaves : a.rows - 1;
+    ln_load_row<kV>(wb, ln_rsrc(a.x + nxt * a.H, row_bytes), lane);
+    ln_row<kFmt, kV, kMasked>(wa, a, row, lane, lg, lb, q, acc);
+    row += nwaves;
+    if (row >= a.rows) break;
+    nxt = row + nwaves < a.rows ? row + nwaves : a.rows - 1;
+    ln_load_row<kV>(wa, ln_rsrc(a.x + nxt * a.H, row_bytes), lane);
+    ln_row<kFmt, kV, kMasked>(wb, a, row, lane, lg, lb, q, acc);
+    row += nwaves;
+  }
+  // block amax: packed halves -> wavefront -> LDS -> one global atomic
+  uint32_t m = max_halves(acc) << 16;
+  m = wave_max_u32(m);
+  if (lane == 0 && m != 0) atomicMax(&block_amax, m);
+  __syncthreads();
+  if (threadIdx.x == 0 && block_amax != 0) atomicMax(a.amax, block_amax);
+}
+
+// ---------------------------------------------------------------- host side
+template <int kFmt, int kV, bool kMasked>
+static int ln_launch(const LnArgs& a, hipStream_t stream) {
+  const void* fn = (const void*)ln_quantize_kernel<kFmt, kV, kMasked>;
+  const size_t smem = (size_t)2 * 512 * kV * sizeof(float);
+  static std::atomic<int> fit{0};
+  int per_cu = fit.load(std::memory_order_relaxed);
+  if (per_cu <= 0) {
+    int occ = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, fn, kLBlock, smem) != hipSuccess)
+      return FP8Q_EHIP;
+    per_cu = occ < kLBlocksPerCU ? (occ > 0 ? occ : 1) : kLBlocksPerCU;
+    fit.store(per_cu, std::memory_order_relaxed);
+  }
+  int cus = 0;
+  const int st = current_device_cus(&cus);
+  if (st != FP8Q_OK) return st;
+  int64_t blocks = (a.rows + (kLBlock / 64) - 1) / (kLBlock / 64);
+  const int64_t cap = (int64_t)cus * per_cu;
+  if (blocks > cap) blocks = cap;
+  void* args[] = {(void*)&a};
+  return launch_status(
+      hipLaunchKernel(fn, dim3((unsigned)blocks), dim3(kLBlock), args, smem, stream));
+}
+
+template <int kFmt>
+static int ln_dispatch(const LnArgs& a, hipStream_t stream) {
+  const int need = (a.nunits + 63) / 64;  // units per lane
+  const int kv = need <= 1 ? 1 : need <= 2 ? 2 : need <= 4 ? 4 : need <= 8 ? 8 : 16;
+  const bool masked = a.nunits != 64 * kv;
+  switch (kv) {
+    case 1: return masked ? ln_launch<kFmt, 1, true>(a, stream) : ln_launch<kFmt, 1, false>(a, stream);
+    case 2: return masked ? ln_launch<kFmt, 2, true>(a, stream) : ln_launch<kFmt, 2, false>(a, stream);
+    case 4: return masked ? ln_launch<kFmt, 4, true>(a, stream) : ln_launch<kFmt, 4, false>(a, stream);
+    case 8: return masked ? ln_launch<kFmt, 8, true>(a, stream) : ln_launch<kFmt, 8, false>(a, stream);
+    default: return masked ? ln_launch<kFmt, 16, true>(a, stream) : ln_launch<kFmt, 16, false>(a, stream);
+  }
+}
+
+}  // namespace fp8q
+
+using namespace fp8q;
+
+extern "C" int fp8_layernorm_quantize_amax(const void* x, int x_dtype, const float* gamma,
+                                           const float* beta, float eps, int64_t rows,
+                                           int64_t hidden, uint8_t* dst, int format,
+                                           const float* scale, float* amax, float* mean,
+                                           float* rstd, void* stream) {
+  if (rows < 0 || hidden < 0) return FP8Q_EINVAL;
+  if (format != FP8Q_E4M3 && format != FP8Q_E5M2) return FP8Q_EINVAL;
+  if (x_dtype != FP8Q_BF16 && x_dtype != FP8Q_F32) return FP8Q_EINVAL;
+  if (scale == nullptr || amax == nullptr) return FP8Q_EINVAL;
+  if (!(eps >= 0.0f) || eps > 3.4e38f) return FP8Q_EINVAL;  // NaN, negative or inf
+  if (x_dtype != FP8Q_BF16) return FP8Q_EUNSUPPORTED;
+  if (rows == 0 || hidden == 0) return FP8Q_OK;
+  if (x == nullptr || dst == nullptr) return FP8Q_EINVAL;
+  if (hidden % 8 != 0 || hidden > kLMaxH) return FP8Q_EUNSUPPORTED;
+  if ((uintptr_t)x % 16 != 0 || (uintptr_t)dst % 8 != 0) return FP8Q_EUNSUPPORTED;
+  if (rows > INT64_MAX / hidden) return FP8Q_EINVAL;
+  LnArgs a;
+  a.x = (const uint16_t*)x;
+  a.gamma = gamma;
+  a.beta = beta;
+  a.dst = dst;
+  a.scale = scale;
+  a.amax = (uint32_t*)amax;
+  a.mean_out = mean;
+  a.rstd_out = rstd;
+  a.rows = rows;
+  a.H = (int32_t)hidden;
+  a.nunits = (int32_t)(hidden / 8);
+  a.eps = eps;
+  a.pad = 0;
+  return format == FP8Q_E4M3 ? ln_dispatch<FP8Q_E4M3>(a, (hipStream_t)stream)
+                             : ln_dispatch<FP8Q_E5M2>(a, (hipStream_t)stream);
+}

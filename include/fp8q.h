@@ -139,6 +139,42 @@ int fp8_gelu_quantize_amax(const void* src, int src_dtype, uint8_t* dst, int64_t
                            int format, const float* scale, float* amax, void* stream);
 
 /*
+ * fp8_layernorm_quantize_amax -- the LayerNorm in front of the MLP, quantized in the
+ * kernel that normalizes: each row of the bf16 input is normalized in registers and
+ * its bf16 result goes through fp8_quantize_amax's quantize and amax without being
+ * written ("Fusion of Fp8 quantization and amax reduction kernels": the reproducer's
+ * transformer block applies nn.LayerNorm() to its input and feeds the result to the
+ * MLP's first FP8 dense).  Per row r of `hidden` elements:
+ *   mu = mean(x), V = mean((x - mu)^2) (biased), rstd = 1 / sqrt(V + eps)
+ *   y[i]    = RN_bf16(gamma[i] * (x[i] - mu) * rstd + beta[i])
+ *   dst[i]  = FP8(saturate(RN32(y[i] / *scale)))
+ *   *amax   = max(*amax, max over all rows of |y[i]|)
+ *   mean[r] = mu, rstd[r] = rstd           (binary32; for the backward pass)
+ * Evaluated in binary32: tree sums and a corrected two-pass variance; y[i] is the bf16
+ * rounding of a value within (twice its first-order bound)
+ *   2^-23 (|gamma| rstd (|d| (L/2 + 7 + L^2 2^-24 A A_d rstd^2) + L A_d + L^2 2^-24 A) + |y|)
+ * of the exact one, L = ceil(log2 hidden) + 10, d = x - mu, A = mean|x|, A_d = mean|d|;
+ * so it is the correctly rounded bf16 of the exact LayerNorm except within that
+ * distance of a bf16 rounding midpoint.  mean and rstd are within a few ulps of the
+ * exact values.  A row containing inf or NaN (or with V + eps = 0) gives NaN outputs,
+ * written as the positive default NaN (code 0x7F), and NaN mean/rstd.
+ *   x          device, rows x hidden bf16, row-major, 16-byte aligned.
+ *   x_dtype    FP8Q_BF16 (FP8Q_F32 returns FP8Q_EUNSUPPORTED).
+ *   gamma,beta device, hidden binary32 each, or NULL for 1 / 0.
+ *   eps        finite, >= 0 (the layer's default is 1e-6).
+ *   rows       >= 0.   hidden: a multiple of 8 in [8, 8192] (else FP8Q_EUNSUPPORTED);
+ *              rows == 0 or hidden == 0 enqueues nothing.
+ *   dst        device, rows x hidden codes, 8-byte aligned (else FP8Q_EUNSUPPORTED).
+ *   format, scale, amax as fp8_quantize_amax.
+ *   mean,rstd  device, rows binary32 each, or NULL to skip.
+ * Returns FP8Q_OK, FP8Q_EINVAL, FP8Q_EUNSUPPORTED or FP8Q_EHIP.
+ */
+int fp8_layernorm_quantize_amax(const void* x, int x_dtype, const float* gamma,
+                                const float* beta, float eps, int64_t rows, int64_t hidden,
+                                uint8_t* dst, int format, const float* scale, float* amax,
+                                float* mean, float* rstd, void* stream);
+
+/*
  * fp8_dequantize -- y[i] = RN32(decode(src[i]) * *scale), written as fp32, or
  * rounded to nearest even into bf16 ("User Guide on Native XLA-FP8", section "JAX":
  * dequantization casts up and multiplies by the scale).  A NaN result is written as

@@ -20,7 +20,8 @@ def declared_functions():
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted([
         "fp8_quantize_amax", "fp8_multi_quantize_amax", "fp8_gelu_quantize_amax",
-        "fp8_dequantize", "fp8_amax_and_scale_update", "fp8_status_string"])
+        "fp8_layernorm_quantize_amax", "fp8_dequantize", "fp8_amax_and_scale_update",
+        "fp8_status_string"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -74,6 +75,33 @@ def test_quantize_rejects_invalid(args):
     import delayed_scaling_amax_amd as d
     assert d.lib.fp8_quantize_amax(*args, None) == d.EINVAL
     assert d.lib.fp8_gelu_quantize_amax(*args, None) == d.EINVAL
+
+
+def _ln(d, x=BAD, dt=0, g=None, b=None, eps=1e-6, rows=4, H=64, dst=BAD, fmt=0, s=BAD,
+        a=BAD):
+    return d.lib.fp8_layernorm_quantize_amax(x, dt, g, b, eps, rows, H, dst, fmt, s, a, None,
+                                             None, None)
+
+
+def test_layernorm_quantize_validation():
+    import delayed_scaling_amax_amd as d
+    assert _ln(d, rows=-1) == d.EINVAL
+    assert _ln(d, H=-8) == d.EINVAL
+    assert _ln(d, fmt=2) == d.EINVAL
+    assert _ln(d, dt=2) == d.EINVAL
+    assert _ln(d, s=None) == d.EINVAL and _ln(d, a=None) == d.EINVAL
+    assert _ln(d, eps=-1.0) == d.EINVAL and _ln(d, eps=float("nan")) == d.EINVAL
+    assert _ln(d, eps=float("inf")) == d.EINVAL
+    assert _ln(d, x=None) == d.EINVAL and _ln(d, dst=None) == d.EINVAL
+    assert _ln(d, dt=d.F32) == d.EUNSUPPORTED
+    assert _ln(d, H=12) == d.EUNSUPPORTED          # not a multiple of 8
+    assert _ln(d, H=8200) == d.EUNSUPPORTED        # longer rows than the kernel holds
+    assert _ln(d, x=BAD + 8) == d.EUNSUPPORTED     # x not 16-byte aligned
+    assert _ln(d, dst=BAD + 4) == d.EUNSUPPORTED   # dst not 8-byte aligned
+    assert _ln(d, rows=2 ** 62, H=8) == d.EINVAL   # rows * hidden overflows
+    # empty is a no-op that touches nothing
+    assert _ln(d, x=None, dst=None, rows=0) == d.OK
+    assert _ln(d, x=None, dst=None, H=0) == d.OK
 
 
 def test_gelu_quantize_takes_bf16_only():
