@@ -74,6 +74,32 @@ def alg_bytes_update(n: int, H: int) -> int:
     return 2 * H * n * 4 + n * 4 * 2 + n * 4 * 2 + n * 4 + n
 
 
+def timed_launches(fn, reps=20):
+    """Median time (us) of fn(i) between HIP events on the current stream, after 3
+    untimed calls; fn(i) picks its buffers by i."""
+    import torch
+    for i in range(3):
+        fn(i)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(reps)]
+    for i, (a, b) in enumerate(ev):
+        a.record()
+        fn(i)
+        b.record()
+    torch.cuda.synchronize()
+    return 1e3 * float(np.median([a.elapsed_time(b) for a, b in ev]))
+
+
+def w_ln_input(workloads, threads, w=None):
+    """The LayerNorm input: the mlp_4096 activation (2048,4,4096) as (8192, 4096) bf16
+    (taken from w when that is the mlp_4096 workload already generated)."""
+    if w is None or w.name != "mlp_4096":
+        w = workloads.mlp_4096(threads=threads)
+    act = w.tensors[0].data
+    return act.reshape(-1, act.shape[-1]).view(np.int16)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -84,6 +110,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-gelu", action="store_true",
                     help="skip the gelu-fused quantize measurement")
+    ap.add_argument("--no-ln", action="store_true",
+                    help="skip the layernorm-fused quantize measurement")
     ap.add_argument("--update-calls", type=int, default=200)
     ap.add_argument("--rotate", type=int, default=3,
                     help="input/output sets used in turn by successive steps")
@@ -287,21 +315,8 @@ def main():
             torch.ops.aten.gelu.out(gsets[i % 2], approximate="tanh", out=gy)
             d.fp8_quantize_amax(gy, gdst, gscale, gamax, 0)
 
-        def timed(fn, reps=20):
-            for i in range(3):
-                fn(i)
-            torch.cuda.synchronize()
-            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                  for _ in range(reps)]
-            for i, (a, b) in enumerate(ev):
-                a.record()
-                fn(i)
-                b.record()
-            torch.cuda.synchronize()
-            return 1e3 * float(np.median([a.elapsed_time(b) for a, b in ev]))
-
-        f_us = timed(fused)
-        u_us = timed(unfused)
+        f_us = timed_launches(fused)
+        u_us = timed_launches(unfused)
         g_bytes = 3 * gn + 8
         gelu_out = {"workload": gw.name, "elements": gn, "format": "e4m3",
                     "fused_events_median_us": round(f_us, 3),
@@ -313,6 +328,51 @@ def main():
         log("gelu fused %.2f us (%.1f GB/s), unfused %.2f us" % (
             f_us, g_bytes / (f_us * 1e-6) / 1e9, u_us))
         del gsets, gdst, gy
+
+    # ------------------------------------------------------------ layernorm-fused quantize
+    # (not in the step) the transformer block's LayerNorm in front of the MLP: bf16 input
+    # (2048,4,4096) (the mlp_4096 activation) -> LayerNorm (gamma, beta, eps 1e-6) ->
+    # E4M3 + amax + per-row mean/rstd in one kernel, against torch's layer_norm writing
+    # the bf16 output followed by the plain quantize.  Four input copies rotate so the
+    # 67 MB input streams from HBM rather than the MALL.
+    ln_out = None
+    if not args.no_ln:
+        lx0 = torch.from_numpy(w_ln_input(workloads, threads, w)).view(torch.bfloat16).to(dev)
+        lsets = [lx0] + [lx0.clone() for _ in range(3)]
+        lrows, lH = lx0.shape
+        ln_ = lrows * lH
+        gen = torch.Generator(device="cpu").manual_seed(12)
+        lg = (1 + 0.1 * torch.randn(lH, generator=gen)).to(dev)
+        lb = (0.1 * torch.randn(lH, generator=gen)).to(dev)
+        lg16, lb16 = lg.to(torch.bfloat16), lb.to(torch.bfloat16)
+        ldst = [torch.empty(ln_, dtype=torch.uint8, device=dev) for _ in range(2)]
+        lmean = torch.empty(lrows, dtype=torch.float32, device=dev)
+        lrstd = torch.empty(lrows, dtype=torch.float32, device=dev)
+        lscale = torch.tensor([1 / 64], dtype=torch.float32, device=dev)
+        lamax = torch.zeros(1, dtype=torch.float32, device=dev)
+
+        def ln_fused(i):
+            d.fp8_layernorm_quantize_amax(lsets[i % 4], ldst[i % 2], lscale, lamax, 0,
+                                          gamma=lg, beta=lb, eps=1e-6, mean=lmean, rstd=lrstd)
+
+        def ln_unfused(i):
+            y = torch.nn.functional.layer_norm(lsets[i % 4], (lH,), lg16, lb16, 1e-6)
+            d.fp8_quantize_amax(y, ldst[i % 2], lscale, lamax, 0)
+
+        lf_us = timed_launches(ln_fused)
+        lu_us = timed_launches(ln_unfused)
+        l_bytes = 3 * ln_ + 8 * lrows + 8 * lH + 8
+        ln_out = {"workload": "mlp_4096 activation (2048,4,4096) as the LayerNorm input",
+                  "elements": ln_, "hidden": lH, "format": "e4m3",
+                  "fused_events_median_us": round(lf_us, 3),
+                  "fused_gbps": round(l_bytes / (lf_us * 1e-6) / 1e9, 1),
+                  "fused_alg_bytes": l_bytes,
+                  "unfused_events_median_us": round(lu_us, 3),
+                  "unfused": "torch layer_norm bf16 out + fp8_quantize_amax",
+                  "speedup": round(lu_us / lf_us, 3)}
+        log("layernorm fused %.2f us (%.1f GB/s), unfused %.2f us" % (
+            lf_us, l_bytes / (lf_us * 1e-6) / 1e9, lu_us))
+        del lsets, ldst
 
     # ------------------------------------------------------------ copy context
     cbuf = torch.empty(1 << 27, dtype=torch.float32, device=dev)  # 512 MiB
@@ -356,6 +416,7 @@ def main():
                        "out": "bf16", "events_median_us": round(dq_us, 3),
                        "gbps": round(dq_bytes / (dq_us * 1e-6) / 1e9, 1)},
         "gelu_quantize": gelu_out,
+        "layernorm_quantize": ln_out,
         "copy_d2d_gbps": round(copy_gbps, 1),
         "roofline": {"bound": "hbm", "achieved": round(q_gbps, 1), "peak": PEAK_HBM_GBPS,
                      "unit": "GB/s", "frac": round(q_gbps / PEAK_HBM_GBPS, 4),

@@ -18,7 +18,7 @@
 //  * gamma and beta are staged once per block into LDS (zero-padded to the unit
 //    grid), read back per element.
 //  * Statistics in binary32 with tree sums (depth log2(8 kV) per lane + 6 across the
-//    wavefront) and a corrected second pass: mu' = RN(S/H); d' = RN(x - mu');
+//    wavefront, the latter on the DPP network) and a corrected second pass: mu' = RN(S/H); d' = RN(x - mu');
 //    e' = sum(d')/H and V' = sum(d'^2)/H - e'^2 remove the first mean's rounding
 //    error from both the deviations and the variance (rows whose mean is large
 //    against their spread lose no accuracy); y' = RN(fma(d' - e', RN(gamma rstd'),
@@ -38,7 +38,13 @@ namespace fp8q {
 constexpr int kLBlock = 256;       // 4 wavefronts, one row each at a time
 constexpr int kLMaxH = 8192;       // 64 lanes x 16 units x 8 elements
 #ifndef FP8Q_LN_BLOCKS_PER_CU
-#define FP8Q_LN_BLOCKS_PER_CU 3
+#define FP8Q_LN_BLOCKS_PER_CU 4
+#endif
+#ifndef FP8Q_LN_PREFETCH
+#define FP8Q_LN_PREFETCH 0
+#endif
+#ifndef FP8Q_LN_UNIT_BARRIER
+#define FP8Q_LN_UNIT_BARRIER 1
 #endif
 constexpr int kLBlocksPerCU = FP8Q_LN_BLOCKS_PER_CU;
 
@@ -55,6 +61,8 @@ struct LnArgs {
   int32_t H;
   int32_t nunits;  // H / 8
   float eps;
+  int32_t vec_affine;  // gamma and beta (where given) are 16-byte aligned
+  float inv_h;         // RN(1/H)
   int32_t pad;
 };
 
@@ -90,21 +98,44 @@ __device__ __forceinline__ float tree_sum(float (&v)[N]) {
   return v[0];
 }
 
-// Sum over the 64 lanes by a butterfly: every lane ends with the same value (IEEE
-// addition is commutative, so partners compute identical sums at every step).
+// Sum over the 64 lanes of a wavefront as a pairwise tree on the DPP network (no LDS
+// round trips): xor-1 and xor-2 within quads, rotations by 4 and 8 within each 16-lane
+// row, then row 0 + row 1 and row 2 + row 3 (row_bcast15), and their sum (row_bcast31)
+// into lane 63, whose value is returned to every lane through a scalar register.
+template <int kCtrl, int kRowMask>
+__device__ __forceinline__ float dpp_add(float v) {
+  // lanes of rows outside kRowMask read 0 and keep v
+  const float t = __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), kCtrl, kRowMask, 0xF,
+                                         false));
+  return v + t;
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v = v + __shfl_xor(v, off, 64);
-  return v;
+  v = dpp_add<0xB1, 0xF>(v);   // quad_perm [1,0,3,2]
+  v = dpp_add<0x4E, 0xF>(v);   // quad_perm [2,3,0,1]
+  v = dpp_add<0x124, 0xF>(v);  // row_ror:4
+  v = dpp_add<0x128, 0xF>(v);  // row_ror:8
+  v = dpp_add<0x142, 0xA>(v);  // row_bcast:15 into rows 1 and 3
+  v = dpp_add<0x143, 0xC>(v);  // row_bcast:31 into rows 2 and 3
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
 }
 
 __device__ __forceinline__ void wave_sum2(float& a, float& b) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) {
-    const float oa = __shfl_xor(a, off, 64), ob = __shfl_xor(b, off, 64);
-    a = a + oa;
-    b = b + ob;
-  }
+  a = dpp_add<0xB1, 0xF>(a);
+  b = dpp_add<0xB1, 0xF>(b);
+  a = dpp_add<0x4E, 0xF>(a);
+  b = dpp_add<0x4E, 0xF>(b);
+  a = dpp_add<0x124, 0xF>(a);
+  b = dpp_add<0x124, 0xF>(b);
+  a = dpp_add<0x128, 0xF>(a);
+  b = dpp_add<0x128, 0xF>(b);
+  a = dpp_add<0x142, 0xA>(a);
+  b = dpp_add<0x142, 0xA>(b);
+  a = dpp_add<0x143, 0xC>(a);
+  b = dpp_add<0x143, 0xC>(b);
+  a = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, a), 63));
+  b = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, b), 63));
 }
 
 __device__ __forceinline__ float lo_f32(uint32_t w) { return as_float(w << 16); }
@@ -146,7 +177,7 @@ __device__ __forceinline__ void ln_row(uint4 (&w)[kV], const LnArgs& a, int64_t 
                                        int lane, const float* __restrict__ lg,
                                        const float* __restrict__ lb, const LnQuant& q,
                                        uint32_t& acc) {
-  const float Hf = (float)a.H;
+  const float invH = a.inv_h;  // RN(1/H), exact for a power-of-two H
   // pass 1: mean (units past the row read as zeros)
   float p1[kV];
 #pragma unroll
@@ -155,7 +186,7 @@ __device__ __forceinline__ void ln_row(uint4 (&w)[kV], const LnArgs& a, int64_t 
     unpack8(w[k], x);
     p1[k] = tree_sum(x);
   }
-  const float mu = wave_sum(tree_sum(p1)) / Hf;
+  const float mu = wave_sum(tree_sum(p1)) * invH;
   // pass 2: deviations from mu', their sum and sum of squares
   rebind(w);
   float s1[kV], s2[kV];
@@ -174,10 +205,13 @@ __device__ __forceinline__ void ln_row(uint4 (&w)[kV], const LnArgs& a, int64_t 
   }
   float t1 = tree_sum(s1), t2 = tree_sum(s2);
   wave_sum2(t1, t2);
-  const float e = t1 / Hf;
-  float var = __builtin_fmaf(-e, e, t2 / Hf);
+  const float e = t1 * invH;
+  float var = __builtin_fmaf(-e, e, t2 * invH);
   var = var < 0.0f ? 0.0f : var;  // rounding can dip below 0; a NaN stays NaN
-  const float rstd = 1.0f / __builtin_sqrtf(var + a.eps);
+  const float ve = var + a.eps;
+  // hardware reciprocal square root (1 ulp) where its input is normal; the IEEE
+  // square root and divide for a subnormal (or zero) V + eps
+  const float rstd = ve >= 0x1p-126f ? __builtin_amdgcn_rsqf(ve) : 1.0f / __builtin_sqrtf(ve);
   if (lane == 0) {
     if (a.mean_out) a.mean_out[row] = mu + e;
     if (a.rstd_out) a.rstd_out[row] = rstd;
@@ -228,24 +262,60 @@ __device__ __forceinline__ void ln_row(uint4 (&w)[kV], const LnArgs& a, int64_t 
       c = make_uint2(cw[0], cw[1]);
     }
     __builtin_amdgcn_raw_buffer_store_b64(ln_u32x2{c.x, c.y}, out, (uint32_t)unit * 8u, 0, 0);
+#if FP8Q_LN_UNIT_BARRIER
     // keep each unit's work (LDS reads, arithmetic) from being hoisted into the
     // previous one's, which would hold every unit's temporaries at once
     __builtin_amdgcn_sched_barrier(0);
+#endif
   }
 }
 
 template <int kFmt, int kV, bool kMasked>
 __global__ __launch_bounds__(kLBlock)
 void ln_quantize_kernel(const LnArgs a) {
-  extern __shared__ float lds[];  // gamma then beta, each 512 kV floats, zero-padded
+  // gamma then beta, each 512 kV floats, zero-padded; 16-byte aligned for the b128 reads
+  extern __shared__ __attribute__((aligned(16))) float lds[];
   __shared__ uint32_t block_amax;
   constexpr int kPad = 512 * kV;
   float* lg = lds;
   float* lb = lds + kPad;
-  for (int i = threadIdx.x; i < kPad; i += kLBlock) {
-    const bool in = i < a.H;
-    lg[i] = in ? (a.gamma ? a.gamma[i] : 1.0f) : 0.0f;
-    lb[i] = in ? (a.beta ? a.beta[i] : 0.0f) : 0.0f;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: SGPR
+  const int64_t nwaves = (int64_t)gridDim.x * (kLBlock / 64);
+  int64_t row = (int64_t)blockIdx.x * (kLBlock / 64) + wave;
+  const uint32_t row_bytes = (uint32_t)a.H * 2u;
+#if FP8Q_LN_PREFETCH
+  // the first row's loads go out before the staging below, which they overlap
+  uint4 wa[kV], wb[kV];
+  if (row < a.rows) ln_load_row<kV>(wa, ln_rsrc(a.x + row * a.H, row_bytes), lane);
+#endif
+  // stage gamma/beta: 16-byte loads, all issued before any is used
+  if (a.vec_affine) {
+    float4 gs[kPad / 4 / kLBlock > 0 ? kPad / 4 / kLBlock : 1];
+    float4 bs[kPad / 4 / kLBlock > 0 ? kPad / 4 / kLBlock : 1];
+    constexpr int kIt = (kPad / 4 + kLBlock - 1) / kLBlock;
+#pragma unroll
+    for (int it = 0; it < kIt; ++it) {
+      const int i4 = threadIdx.x + it * kLBlock;  // float4 index
+      const bool in = 4 * i4 < a.H;
+      gs[it] = in && a.gamma ? ((const float4*)a.gamma)[i4] : make_float4(1.f, 1.f, 1.f, 1.f);
+      bs[it] = in && a.beta ? ((const float4*)a.beta)[i4] : make_float4(0.f, 0.f, 0.f, 0.f);
+      if (!in) gs[it] = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+    for (int it = 0; it < kIt; ++it) {
+      const int i4 = threadIdx.x + it * kLBlock;
+      if (4 * i4 < kPad) {
+        ((float4*)lg)[i4] = gs[it];
+        ((float4*)lb)[i4] = bs[it];
+      }
+    }
+  } else {
+    for (int i = threadIdx.x; i < kPad; i += kLBlock) {
+      const bool in = i < a.H;
+      lg[i] = in ? (a.gamma ? a.gamma[i] : 1.0f) : 0.0f;
+      lb[i] = in ? (a.beta ? a.beta[i] : 0.0f) : 0.0f;
+    }
   }
   if (threadIdx.x == 0) block_amax = 0;
 
@@ -256,27 +326,31 @@ void ln_quantize_kernel(const LnArgs a) {
   q.xlim = min(as_uint(q.s * 0x1p126f) >> 16, 0x7F80u);
   __syncthreads();
 
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: SGPR
-  const int64_t nwaves = (int64_t)gridDim.x * (kLBlock / 64);
-  int64_t row = (int64_t)blockIdx.x * (kLBlock / 64) + wave;
-  const uint32_t row_bytes = (uint32_t)a.H * 2u;
   uint32_t acc = 0;
-  uint4 wa[kV], wb[kV];
+#if FP8Q_LN_PREFETCH
   // two row buffers alternate so that the next row's loads are in flight while this
   // row is reduced; the prefetch index is clamped so every load is unconditional
-  if (row < a.rows) ln_load_row<kV>(wa, ln_rsrc(a.x + row * a.H, row_bytes), lane);
   while (row < a.rows) {
     int64_t nxt = row + nwaves < a.rows ? row + nwaves : a.rows - 1;
     ln_load_row<kV>(wb, ln_rsrc(a.x + nxt * a.H, row_bytes), lane);
+    __builtin_amdgcn_sched_barrier(0);
     ln_row<kFmt, kV, kMasked>(wa, a, row, lane, lg, lb, q, acc);
     row += nwaves;
     if (row >= a.rows) break;
     nxt = row + nwaves < a.rows ? row + nwaves : a.rows - 1;
     ln_load_row<kV>(wa, ln_rsrc(a.x + nxt * a.H, row_bytes), lane);
+    __builtin_amdgcn_sched_barrier(0);
     ln_row<kFmt, kV, kMasked>(wb, a, row, lane, lg, lb, q, acc);
     row += nwaves;
   }
+#else
+  // one row at a time: latency is hidden by the other resident wavefronts
+  for (; row < a.rows; row += nwaves) {
+    uint4 w[kV];
+    ln_load_row<kV>(w, ln_rsrc(a.x + row * a.H, row_bytes), lane);
+    ln_row<kFmt, kV, kMasked>(w, a, row, lane, lg, lb, q, acc);
+  }
+#endif
   // block amax: packed halves -> wavefront -> LDS -> one global atomic
   uint32_t m = max_halves(acc) << 16;
   m = wave_max_u32(m);
@@ -357,6 +431,8 @@ extern "C" int fp8_layernorm_quantize_amax(const void* x, int x_dtype, const flo
   a.H = (int32_t)hidden;
   a.nunits = (int32_t)(hidden / 8);
   a.eps = eps;
+  a.vec_affine = ((uintptr_t)gamma % 16 == 0) && ((uintptr_t)beta % 16 == 0);
+  a.inv_h = 1.0f / (float)hidden;
   a.pad = 0;
   return format == FP8Q_E4M3 ? ln_dispatch<FP8Q_E4M3>(a, (hipStream_t)stream)
                              : ln_dispatch<FP8Q_E5M2>(a, (hipStream_t)stream);
