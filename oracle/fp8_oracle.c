@@ -415,3 +415,79 @@ void oracle_layernorm_bf16(const uint16_t* x, const float* gamma, const float* b
     }
   }
 }
+
+/* ------------------------------------------------------------------------------
+ * FP8 GEMM consumer ("User Guide on Native XLA-FP8", section "JAX": the FP8 operands are
+ * cast up and multiplied by their scales, then the dot; the page's matmul takes two FP8
+ * tensors and two binary32 scalar scales).  Readings:
+ *  M1 C[m][n] = sa * sb * sum_k decode(A[m][k]) * decode(B[n][k]) with both operands
+ *     K-contiguous (A: M x K, B: N x K, row-major): the layout FP8 matmuls require.
+ *  M2 the sum is the exact value (every FP8 product is an integer times a power of two,
+ *     accumulated here exactly in 128-bit fixed point), converted to double (relative
+ *     error below 2^-51) and multiplied by the scales in double (sa * sb is exact in
+ *     double); a binary32 evaluation is judged against it by the error bound of its
+ *     accumulation, so the oracle also returns sum_k |a_k b_k| (times |sa sb|).
+ *  M3 IEEE specials: a NaN operand, inf * 0, or inf - inf gives NaN; an inf operand
+ *     times a finite nonzero one gives +-inf (E5M2 codes only; the quantize never
+ *     produces inf).
+ */
+typedef struct { int64_t m; int e; int special; } fp8_parts; /* value = m * 2^e */
+
+static fp8_parts fp8_split(int fmt, uint8_t code) {
+  fp8_parts p = {0, 0, 0};
+  const int mbits = fmt_mbits(fmt), bias = fmt_bias(fmt);
+  const int ebits = 7 - mbits;
+  const int sign = code >> 7, ex = (code >> mbits) & ((1 << ebits) - 1);
+  const int man = code & ((1 << mbits) - 1);
+  double v = oracle_fp8_decode(fmt, code);
+  if (isnan(v)) { p.special = 2; return p; }
+  if (isinf(v)) { p.special = v > 0 ? 1 : -1; return p; }
+  if (ex == 0) { p.m = man; p.e = 1 - bias - mbits; }
+  else { p.m = (1 << mbits) | man; p.e = ex - bias - mbits; }
+  if (sign) p.m = -p.m;
+  return p;
+}
+
+/* C_exact[m*N+n] and C_abs[m*N+n] (both including the scales), double. */
+void oracle_fp8_gemm(const uint8_t* A, int a_fmt, const uint8_t* B, int b_fmt, int64_t M,
+                     int64_t N, int64_t K, float sa, float sb, double* C_exact, double* C_abs) {
+  /* products m_a m_b 2^(e_a + e_b); every exponent is >= 2 * (1 - 15 - 2) = -32 */
+  const int e0 = -40;
+  const double s = (double)sa * (double)sb;
+  for (int64_t m = 0; m < M; ++m)
+    for (int64_t n = 0; n < N; ++n) {
+      __int128 acc = 0, acc_abs = 0;
+      int nan = 0, pinf = 0, ninf = 0;
+      for (int64_t k = 0; k < K; ++k) {
+        fp8_parts a = fp8_split(a_fmt, A[m * K + k]), b = fp8_split(b_fmt, B[n * K + k]);
+        if (a.special == 2 || b.special == 2) { nan = 1; continue; }
+        if (a.special || b.special) {
+          const int sa_ = a.special ? a.special : (a.m > 0 ? 1 : a.m < 0 ? -1 : 0);
+          const int sb_ = b.special ? b.special : (b.m > 0 ? 1 : b.m < 0 ? -1 : 0);
+          if (sa_ == 0 || sb_ == 0) nan = 1;            /* inf * 0 */
+          else if (sa_ * sb_ > 0) pinf = 1;
+          else ninf = 1;
+          continue;
+        }
+        const __int128 t = (__int128)(a.m * b.m) << (a.e + b.e - e0);
+        acc += t;
+        acc_abs += t < 0 ? -t : t;
+      }
+      double v, va;
+      if (nan || (pinf && ninf)) { v = NAN; va = NAN; }
+      else if (pinf) { v = INFINITY; va = INFINITY; }
+      else if (ninf) { v = -INFINITY; va = INFINITY; }
+      else {
+        /* the exact fixed-point sum in double (two roundings at most) */
+        const int neg = acc < 0;
+        unsigned __int128 u = neg ? (unsigned __int128)(-acc) : (unsigned __int128)acc;
+        const double hi = (double)(uint64_t)(u >> 64), lo = (double)(uint64_t)u;
+        v = ldexp(ldexp(hi, 64) + lo, e0);
+        if (neg) v = -v;
+        const unsigned __int128 ua = (unsigned __int128)acc_abs;
+        va = ldexp(ldexp((double)(uint64_t)(ua >> 64), 64) + (double)(uint64_t)ua, e0);
+      }
+      C_exact[m * N + n] = v * s;
+      C_abs[m * N + n] = va * fabs(s);
+    }
+}

@@ -727,6 +727,90 @@ def pin_layernorm_admissible_range(o):
     assert f2u(a_lo) <= f2u(amax) <= f2u(a_hi)
 
 
+def _torch_decode(codes: np.ndarray, fmt: int) -> np.ndarray:
+    """FP8 codes -> float64 through torch's CPU float8 types (independent of the oracle)."""
+    dt = torch.float8_e4m3fn if fmt == E4M3 else torch.float8_e5m2
+    return torch.from_numpy(np.ascontiguousarray(codes, np.uint8)).view(dt).to(torch.float64).numpy()
+
+
+def _finite_codes(g, shape, fmt):
+    c = g.integers(0, 256, shape).astype(np.uint8)
+    if fmt == E4M3:
+        c[(c & 0x7F) == 0x7F] = 0x38
+    else:
+        c[(c & 0x7C) == 0x7C] = 0x3C
+    return c
+
+
+def pin_gemm_vs_float64_matmul(o):
+    """E4M3 x E4M3 with K <= 64: every partial sum of decoded products fits a double (the
+    products span 2^-18 .. 2^17.6), so numpy's float64 matmul of torch-decoded operands is
+    exact and the oracle must equal it bit for bit (times the scales). Pairings with E5M2
+    span too many binades for that: there the oracle is compared with the exact rational
+    sum (Python Fractions) to its stated 2^-51. C_abs is the matmul of |.| in all cases."""
+    g = np.random.Generator(np.random.PCG64(81))
+    sa, sb = float(np.float32(0.37)), float(np.float32(3.5e-3))
+    for fa, fb, M, N, K in ((E4M3, E4M3, 7, 5, 64), (E4M3, E4M3, 3, 2, 17), (E5M2, E4M3, 3, 4, 48),
+                            (E4M3, E5M2, 4, 4, 33), (E5M2, E5M2, 5, 6, 16)):
+        A = _finite_codes(g, (M, K), fa)
+        B = _finite_codes(g, (N, K), fb)
+        C, Cabs = o.fp8_gemm(A, fa, B, fb, sa, sb)
+        da, db = _torch_decode(A, fa), _torch_decode(B, fb)
+        if fa == E4M3 and fb == E4M3:
+            ref = (da @ db.T) * (sa * sb)
+            assert (C == ref).all(), np.max(np.abs(C - ref))
+        else:
+            for m in range(M):
+                for n in range(N):
+                    ex = sum(Fraction(float(da[m, k])) * Fraction(float(db[n, k])) for k in range(K))
+                    want = float(ex * Fraction(sa) * Fraction(sb))
+                    assert abs(C[m, n] - want) <= 2.0 ** -50 * abs(want) + 1e-300, (m, n)
+        assert np.allclose(Cabs, (np.abs(da) @ np.abs(db).T) * abs(sa * sb), rtol=1e-14, atol=0)
+        assert (Cabs >= np.abs(C) * (1 - 1e-15)).all()
+
+
+def pin_gemm_exact_large_k(o):
+    """Sums that do not fit a double: E5M2 extremes (57344^2 against 2^-16 * 2^-16 terms)
+    over K = 4096, against Python integers; identity operands return the other operand."""
+    g = np.random.Generator(np.random.PCG64(82))
+    K = 4096
+    A = np.full((2, K), 0x01, np.uint8)              # 2^-16 (smallest E5M2 subnormal)
+    B = np.full((2, K), 0x01, np.uint8)
+    A[0, 0] = B[0, 0] = 0x7B                          # 57344
+    A[1, 5] = 0xFB                                    # -57344 against +2^-16
+    C, _ = o.fp8_gemm(A, E5M2, B, E5M2)
+    exact00 = Fraction(57344) ** 2 + (K - 1) * Fraction(1, 2 ** 32)
+    assert C[0, 0] == float(exact00)
+    exact10 = sum(Fraction(_torch_decode(A[1:2, k:k + 1], E5M2)[0, 0]) *
+                  Fraction(_torch_decode(B[0:1, k:k + 1], E5M2)[0, 0]) for k in range(K))
+    assert C[1, 0] == float(exact10)
+    # identity: A = I (codes of 1.0), C = decode(B) as rows
+    n = 16
+    I = np.zeros((n, n), np.uint8)
+    I[np.arange(n), np.arange(n)] = 0x38           # E4M3 1.0
+    Bc = _finite_codes(g, (5, n), E4M3)
+    C, _ = o.fp8_gemm(I, E4M3, Bc, E4M3)
+    assert (C == _torch_decode(Bc, E4M3).T).all()
+
+
+def pin_gemm_specials(o):
+    """NaN operands, inf * 0 and inf - inf give NaN; inf times a nonzero finite value
+    gives a signed inf (E5M2 has inf codes); finite rows elsewhere are unaffected."""
+    A = np.full((4, 4), 0x3C, np.uint8)              # E5M2 1.0
+    B = np.full((3, 4), 0x3C, np.uint8)
+    A[0, 1] = 0x7F                                    # NaN
+    A[1, 2] = 0x7C                                    # +inf
+    A[2, 2] = 0x7C
+    A[2, 3] = 0xFC                                    # +inf and -inf in one dot
+    B[1, 2] = 0x00                                    # 0 against row 1's inf
+    B[2, :] = 0xBC                                    # -1.0
+    C, _ = o.fp8_gemm(A, E5M2, B, E5M2)
+    assert np.isnan(C[0]).all()
+    assert C[1, 0] == np.inf and np.isnan(C[1, 1]) and C[1, 2] == -np.inf
+    assert np.isnan(C[2]).all()
+    assert (C[3] == np.array([4.0, 3.0, -4.0])).all()     # B row 1 has one zero
+
+
 def f32_to_bf16_np(v: np.ndarray) -> np.ndarray:
     u = v.view(np.uint32)
     return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)

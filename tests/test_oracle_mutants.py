@@ -74,6 +74,15 @@ MUTANTS = [
      "lr[i] = round_d_to_bf16(v, NULL, NULL);"),
     ("ln_window_one_sided", "hr[i] = round_d_to_bf16(v + w, NULL, NULL);",
      "hr[i] = round_d_to_bf16(v, NULL, NULL);"),
+    ("gemm_b_transposed", "fp8_parts a = fp8_split(a_fmt, A[m * K + k]), b = fp8_split(b_fmt, B[n * K + k]);",
+     "fp8_parts a = fp8_split(a_fmt, A[m * K + k]), b = fp8_split(b_fmt, B[k * N + n]);"),
+    ("gemm_scale_dropped", "C_exact[m * N + n] = v * s;", "C_exact[m * N + n] = v;"),
+    ("gemm_subnormal_exponent", "if (ex == 0) { p.m = man; p.e = 1 - bias - mbits; }",
+     "if (ex == 0) { p.m = man; p.e = -bias - mbits; }"),
+    ("gemm_sign_dropped", "  if (sign) p.m = -p.m;\n  return p;", "  return p;"),
+    ("gemm_inf_times_zero", "if (sa_ == 0 || sb_ == 0) nan = 1;", "if (sa_ == 0 || sb_ == 0) continue;"),
+    ("gemm_nan_ignored", "if (a.special == 2 || b.special == 2) { nan = 1; continue; }",
+     "if (a.special == 2 || b.special == 2) { continue; }"),
     ("dequant_nan_unsigned", "uint32_t nan_bits = 0x7FC00000u | ((uint32_t)(src[i] & 0x80) << 24);",
      "uint32_t nan_bits = 0x7FC00000u;"),
 ]
