@@ -10,6 +10,7 @@ the current HIP stream.  Functions carry the C names:
   fp8_layernorm_quantize_amax(x, dst, scale, amax, format, gamma=None, beta=None,
                               eps=1e-6, mean=None, rstd=None)  LayerNorm(x), quantized
   fp8_dequantize(src, dst, scale, format)
+  fp8_gemm(A, a_format, B, b_format, a_scale, b_scale, C)   C = sa sb A @ B.T (FP8)
   fp8_amax_and_scale_update(amax, amax_history, scale, scale_inv, formats,
                             algo=AMAX_MAX, margin=0, reset_amax=False)
   fp8_status_string(status)
@@ -59,11 +60,13 @@ def _load():
     lib.fp8_layernorm_quantize_amax.argtypes = [vp, i32, vp, vp, ctypes.c_float, i64, i64, vp,
                                                 i32, vp, vp, vp, vp, vp]
     lib.fp8_dequantize.argtypes = [vp, i32, vp, i32, i64, vp, vp]
+    lib.fp8_gemm.argtypes = [vp, i32, vp, i32, i64, i64, i64, vp, vp, vp, i32, vp]
     lib.fp8_amax_and_scale_update.argtypes = [vp, vp, vp, vp, vp, i64, i64, i32, i32, i32, vp]
     lib.fp8_status_string.argtypes = [i32]
     lib.fp8_status_string.restype = ctypes.c_char_p
     for f in ("fp8_quantize_amax", "fp8_multi_quantize_amax", "fp8_gelu_quantize_amax",
-              "fp8_layernorm_quantize_amax", "fp8_dequantize", "fp8_amax_and_scale_update"):
+              "fp8_layernorm_quantize_amax", "fp8_gemm", "fp8_dequantize", "fp8_amax_and_scale_update",
+              "fp8_gemm"):
         getattr(lib, f).restype = i32
     return lib
 
@@ -145,6 +148,25 @@ def fp8_layernorm_quantize_amax(x: torch.Tensor, dst: torch.Tensor, scale: torch
             _opt_f32(mean, rows, "mean"), _opt_f32(rstd, rows, "rstd"), _stream(x.device)))
 
 
+def fp8_gemm(A: torch.Tensor, a_format: int, B: torch.Tensor, b_format: int,
+             a_scale: torch.Tensor, b_scale: torch.Tensor, C: torch.Tensor) -> None:
+    """C (M, N) bf16/fp32 = a_scale * b_scale * decode(A) @ decode(B).T for uint8 code
+    tensors A (M, K) and B (N, K)."""
+    if A.dim() != 2 or B.dim() != 2 or C.dim() != 2:
+        raise ValueError("A, B and C must be 2-D")
+    M, K = A.shape
+    N, K2 = B.shape
+    if K2 != K or tuple(C.shape) != (M, N):
+        raise ValueError("shapes: A (M, K), B (N, K), C (M, N)")
+    if A.dtype != torch.uint8 or B.dtype != torch.uint8:
+        raise ValueError("A and B hold FP8 codes as uint8")
+    with torch.cuda.device(A.device):
+        _check("fp8_gemm", lib.fp8_gemm(
+            _dense(A, "A"), int(a_format), _dense(B, "B"), int(b_format), M, N, K,
+            _one_float(a_scale, "a_scale"), _one_float(b_scale, "b_scale"), _dense(C, "C"),
+            _DTYPE.get(C.dtype, -1), _stream(A.device)))
+
+
 def fp8_multi_quantize_amax(entries) -> None:
     """entries: sequence of (src, dst, scale, amax, format)."""
     entries = list(entries)
@@ -195,6 +217,6 @@ def fp8_amax_and_scale_update(amax: torch.Tensor, amax_history: torch.Tensor,
 
 
 __all__ = ["fp8_quantize_amax", "fp8_multi_quantize_amax", "fp8_gelu_quantize_amax",
-           "fp8_layernorm_quantize_amax", "fp8_dequantize",
+           "fp8_layernorm_quantize_amax", "fp8_gemm", "fp8_dequantize",
            "fp8_amax_and_scale_update", "fp8_status_string", "fp8q_tensor", "Fp8qError",
            "E4M3", "E5M2", "BF16", "F32", "AMAX_MAX", "AMAX_MOST_RECENT", "LIB_PATH", "lib"]

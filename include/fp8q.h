@@ -11,7 +11,11 @@
  *   - the amax-history scale update for many tensors in one launch ("Implement
  *     fused kernel for FP8 scale update", TransformerEngine PR 593: roll the amax
  *     history in place, take the amax from it, compute the new scale);
- *   - dequantize (FP8 code times scale).
+ *   - dequantize (FP8 code times scale);
+ *   - the quantize fused into the kernel that produces the tensor, for the MLP's gelu
+ *     activation and the LayerNorm in front of it (the reproducer's transformer block
+ *     in that issue), so the bf16 activation is never written;
+ *   - the consumer: an FP8 matrix product with per-tensor scales on the matrix cores.
  * The formulas are those of "User Guide on Native XLA-FP8" (NVIDIA JAX-Toolbox),
  * section "JAX": quantize A_fp8 = cast(A / A_scale); dequantize cast_up(a_fp8) *
  * a_scale; delayed scaling A_scale = max|A| / E4M3_MAX.
@@ -29,9 +33,11 @@
  *               launch returns FP8Q_EHIP.  Faults during kernel execution surface at
  *               the caller's next synchronisation, as in HIP.
  *   Layout.     Tensors are dense and contiguous, element i at byte offset
- *               i * sizeof(element).  Any alignment is accepted: when source and
- *               destination are aligned alike the body runs with 16-byte vector
- *               loads, otherwise (or for the few head/tail elements) element-wise.
+ *               i * sizeof(element).  The quantize, dequantize and update entry points
+ *               accept any alignment: when source and destination are aligned alike
+ *               the body runs with 16-byte vector loads, otherwise (or for the few
+ *               head/tail elements) element-wise.  The LayerNorm-fused quantize and
+ *               the GEMM state their alignment requirements.
  *   Aliasing.   Sources and destinations of one call must not overlap.
  *   Numerics.   Binary32 throughout: the quotient x/scale is one IEEE division
  *               rounded to nearest even, then saturated to +-FP8_MAX (448 for E4M3,
@@ -173,6 +179,33 @@ int fp8_layernorm_quantize_amax(const void* x, int x_dtype, const float* gamma,
                                 const float* beta, float eps, int64_t rows, int64_t hidden,
                                 uint8_t* dst, int format, const float* scale, float* amax,
                                 float* mean, float* rstd, void* stream);
+
+/*
+ * fp8_gemm -- the consumer of the quantized tensors: an FP8 matrix product with
+ * per-tensor scales on the matrix cores ("User Guide on Native XLA-FP8", section "JAX":
+ * the FP8 operands are cast up and multiplied by their scales before the dot; the matmul
+ * the page names takes two FP8 tensors and two binary32 scalar scales).
+ *   C[m][n] = *a_scale * *b_scale * sum_k decode(A[m][k]) * decode(B[n][k])
+ * A is M x K and B is N x K, both row-major (K contiguous: a weight stored K x N is
+ * quantized from its transpose); C is M x N row-major.  The FP8 products are exact; the
+ * gfx950 matrix core sums each aligned group of 8 consecutive products in fixed point
+ * 13 bits below the group's largest (smaller products truncate toward zero; measured)
+ * and accumulates the group sums in binary32, so before the final rounding to c_dtype
+ * (bf16: round to nearest even)
+ *   |C - exact| <= (2^-10 G + 2^-24 (ceil(K/8) + 2) S) |sa sb|,
+ *   G = sum over k-groups [8q, 8q+8) of max |a_k b_k|,  S = sum_k |a_k b_k|.
+ * NaN operands propagate.  K == 0 gives C = 0.
+ *   a_format, b_format  FP8Q_E4M3 or FP8Q_E5M2 (any pairing).
+ *   M, N, K     >= 0; M == 0 or N == 0 enqueues nothing.  K a multiple of 16 and at most
+ *               2^23 (else FP8Q_EUNSUPPORTED).
+ *   A, B        device, 16-byte aligned (else FP8Q_EUNSUPPORTED); non-NULL when K > 0.
+ *   a_scale, b_scale  device, 1 float each (the delayed-scaling scales of A and B).
+ *   C           device, M x N of c_dtype (FP8Q_BF16 or FP8Q_F32), naturally aligned.
+ * Returns FP8Q_OK, FP8Q_EINVAL, FP8Q_EUNSUPPORTED or FP8Q_EHIP.
+ */
+int fp8_gemm(const uint8_t* A, int a_format, const uint8_t* B, int b_format, int64_t M,
+             int64_t N, int64_t K, const float* a_scale, const float* b_scale, void* C,
+             int c_dtype, void* stream);
 
 /*
  * fp8_dequantize -- y[i] = RN32(decode(src[i]) * *scale), written as fp32, or

@@ -70,7 +70,7 @@ def _declare(lib):
     lib.oracle_layernorm_bf16.argtypes = [vp, vp, vp, c.c_float, i64, i64, vp, vp, vp, vp, vp]
     lib.oracle_layernorm_bf16.restype = None
     lib.oracle_fp8_gemm.argtypes = [vp, c.c_int, vp, c.c_int, i64, i64, i64, c.c_float, c.c_float,
-                                    vp, vp]
+                                    vp, vp, vp]
     lib.oracle_fp8_gemm.restype = None
     return lib
 
@@ -267,8 +267,9 @@ class Oracle:
     def fp8_gemm(self, A: np.ndarray, a_fmt: int, B: np.ndarray, b_fmt: int, sa: float = 1.0,
                  sb: float = 1.0, threads: int = 1):
         """C = sa*sb * decode(A) @ decode(B).T for FP8 codes A (M, K) and B (N, K): returns
-        (C_exact, C_abs) in float64, C_abs = |sa*sb| * sum_k |a_k b_k| (the scale of an
-        accumulation's error bound).  Rows of C are split over `threads`."""
+        (C_exact, C_abs, C_gmax) in float64: C_abs = |sa*sb| * sum_k |a_k b_k| and C_gmax =
+        |sa*sb| * sum over k-groups [8q, 8q+8) of the group's largest |a_k b_k| (the scales
+        of an accumulation's error bound).  Rows of C are split over `threads`."""
         A = np.ascontiguousarray(A, np.uint8)
         B = np.ascontiguousarray(B, np.uint8)
         M, K = A.shape
@@ -276,12 +277,13 @@ class Oracle:
         assert K == K2
         C = np.empty((M, N), np.float64)
         Cabs = np.empty((M, N), np.float64)
+        Cg = np.empty((M, N), np.float64)
 
         def run(r0, r1):
             if r1 > r0:
                 self.lib.oracle_fp8_gemm(A[r0:].ctypes.data, a_fmt, B.ctypes.data, b_fmt,
                                          r1 - r0, N, K, float(sa), float(sb), C[r0:].ctypes.data,
-                                         Cabs[r0:].ctypes.data)
+                                         Cabs[r0:].ctypes.data, Cg[r0:].ctypes.data)
 
         if threads <= 1 or M < 2 * threads:
             run(0, M)
@@ -289,7 +291,7 @@ class Oracle:
             bounds = np.linspace(0, M, threads + 1).astype(np.int64)
             with ThreadPoolExecutor(threads) as ex:
                 list(ex.map(run, bounds[:-1], bounds[1:]))
-        return C, Cabs
+        return C, Cabs, Cg
 
     def count_saturated(self, x: np.ndarray, fmt: int, scale: float) -> int:
         x, dt = self._src(x)

@@ -425,8 +425,11 @@ void oracle_layernorm_bf16(const uint16_t* x, const float* gamma, const float* b
  *  M2 the sum is the exact value (every FP8 product is an integer times a power of two,
  *     accumulated here exactly in 128-bit fixed point), converted to double (relative
  *     error below 2^-51) and multiplied by the scales in double (sa * sb is exact in
- *     double); a binary32 evaluation is judged against it by the error bound of its
- *     accumulation, so the oracle also returns sum_k |a_k b_k| (times |sa sb|).
+ *     double).  A hardware evaluation is judged against it by the error bound of its
+ *     accumulation, so the oracle also returns sum_k |a_k b_k| and, for accumulators
+ *     that sum aligned groups of 8 consecutive products with limited precision, the sum
+ *     over those groups (k in [8q, 8q + 8)) of the group's largest |a_k b_k|, both times
+ *     |sa sb|.
  *  M3 IEEE specials: a NaN operand, inf * 0, or inf - inf gives NaN; an inf operand
  *     times a finite nonzero one gives +-inf (E5M2 codes only; the quantize never
  *     produces inf).
@@ -448,9 +451,10 @@ static fp8_parts fp8_split(int fmt, uint8_t code) {
   return p;
 }
 
-/* C_exact[m*N+n] and C_abs[m*N+n] (both including the scales), double. */
+/* C_exact[m*N+n], C_abs[m*N+n] and C_gmax[m*N+n] (all including the scales), double. */
 void oracle_fp8_gemm(const uint8_t* A, int a_fmt, const uint8_t* B, int b_fmt, int64_t M,
-                     int64_t N, int64_t K, float sa, float sb, double* C_exact, double* C_abs) {
+                     int64_t N, int64_t K, float sa, float sb, double* C_exact, double* C_abs,
+                     double* C_gmax) {
   /* products m_a m_b 2^(e_a + e_b); every exponent is >= 2 * (1 - 15 - 2) = -32 */
   const int e0 = -40;
   const double s = (double)sa * (double)sb;
@@ -458,7 +462,9 @@ void oracle_fp8_gemm(const uint8_t* A, int a_fmt, const uint8_t* B, int b_fmt, i
     for (int64_t n = 0; n < N; ++n) {
       __int128 acc = 0, acc_abs = 0;
       int nan = 0, pinf = 0, ninf = 0;
+      double gsum = 0.0, gmax = 0.0;   /* sum over groups of 8 of the largest |a b| */
       for (int64_t k = 0; k < K; ++k) {
+        if (k % 8 == 0) { gsum += gmax; gmax = 0.0; }
         fp8_parts a = fp8_split(a_fmt, A[m * K + k]), b = fp8_split(b_fmt, B[n * K + k]);
         if (a.special == 2 || b.special == 2) { nan = 1; continue; }
         if (a.special || b.special) {
@@ -472,7 +478,10 @@ void oracle_fp8_gemm(const uint8_t* A, int a_fmt, const uint8_t* B, int b_fmt, i
         const __int128 t = (__int128)(a.m * b.m) << (a.e + b.e - e0);
         acc += t;
         acc_abs += t < 0 ? -t : t;
+        const double pa = fabs(ldexp((double)(a.m * b.m), a.e + b.e));
+        if (pa > gmax) gmax = pa;
       }
+      gsum += gmax;
       double v, va;
       if (nan || (pinf && ninf)) { v = NAN; va = NAN; }
       else if (pinf) { v = INFINITY; va = INFINITY; }
@@ -489,5 +498,6 @@ void oracle_fp8_gemm(const uint8_t* A, int a_fmt, const uint8_t* B, int b_fmt, i
       }
       C_exact[m * N + n] = v * s;
       C_abs[m * N + n] = va * fabs(s);
+      if (C_gmax) C_gmax[m * N + n] = (isnan(va) || isinf(va)) ? va : gsum * fabs(s);
     }
 }

@@ -754,8 +754,13 @@ def pin_gemm_vs_float64_matmul(o):
                             (E4M3, E5M2, 4, 4, 33), (E5M2, E5M2, 5, 6, 16)):
         A = _finite_codes(g, (M, K), fa)
         B = _finite_codes(g, (N, K), fb)
-        C, Cabs = o.fp8_gemm(A, fa, B, fb, sa, sb)
+        C, Cabs, Cg = o.fp8_gemm(A, fa, B, fb, sa, sb)
         da, db = _torch_decode(A, fa), _torch_decode(B, fb)
+        # group maxima over k in [8q, 8q + 8), from the decoded products
+        P = np.abs(da[:, None, :] * db[None, :, :])
+        pad = (-K) % 8
+        Pg = np.pad(P, ((0, 0), (0, 0), (0, pad))).reshape(M, N, -1, 8).max(axis=3).sum(axis=2)
+        assert np.allclose(Cg, Pg * abs(sa * sb), rtol=1e-14, atol=0)
         if fa == E4M3 and fb == E4M3:
             ref = (da @ db.T) * (sa * sb)
             assert (C == ref).all(), np.max(np.abs(C - ref))
@@ -778,7 +783,7 @@ def pin_gemm_exact_large_k(o):
     B = np.full((2, K), 0x01, np.uint8)
     A[0, 0] = B[0, 0] = 0x7B                          # 57344
     A[1, 5] = 0xFB                                    # -57344 against +2^-16
-    C, _ = o.fp8_gemm(A, E5M2, B, E5M2)
+    C = o.fp8_gemm(A, E5M2, B, E5M2)[0]
     exact00 = Fraction(57344) ** 2 + (K - 1) * Fraction(1, 2 ** 32)
     assert C[0, 0] == float(exact00)
     exact10 = sum(Fraction(_torch_decode(A[1:2, k:k + 1], E5M2)[0, 0]) *
@@ -789,7 +794,7 @@ def pin_gemm_exact_large_k(o):
     I = np.zeros((n, n), np.uint8)
     I[np.arange(n), np.arange(n)] = 0x38           # E4M3 1.0
     Bc = _finite_codes(g, (5, n), E4M3)
-    C, _ = o.fp8_gemm(I, E4M3, Bc, E4M3)
+    C = o.fp8_gemm(I, E4M3, Bc, E4M3)[0]
     assert (C == _torch_decode(Bc, E4M3).T).all()
 
 
@@ -804,7 +809,7 @@ def pin_gemm_specials(o):
     A[2, 3] = 0xFC                                    # +inf and -inf in one dot
     B[1, 2] = 0x00                                    # 0 against row 1's inf
     B[2, :] = 0xBC                                    # -1.0
-    C, _ = o.fp8_gemm(A, E5M2, B, E5M2)
+    C = o.fp8_gemm(A, E5M2, B, E5M2)[0]
     assert np.isnan(C[0]).all()
     assert C[1, 0] == np.inf and np.isnan(C[1, 1]) and C[1, 2] == -np.inf
     assert np.isnan(C[2]).all()

@@ -21,7 +21,7 @@ def test_header_declares_the_boundary():
     assert declared_functions() == sorted([
         "fp8_quantize_amax", "fp8_multi_quantize_amax", "fp8_gelu_quantize_amax",
         "fp8_layernorm_quantize_amax", "fp8_dequantize", "fp8_amax_and_scale_update",
-        "fp8_status_string"])
+        "fp8_gemm", "fp8_status_string"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -102,6 +102,27 @@ def test_layernorm_quantize_validation():
     # empty is a no-op that touches nothing
     assert _ln(d, x=None, dst=None, rows=0) == d.OK
     assert _ln(d, x=None, dst=None, H=0) == d.OK
+
+
+def _gemm(d, A=BAD, fa=0, B=BAD, fb=0, M=4, N=4, K=32, sa=BAD, sb=BAD, C=BAD, ct=0):
+    return d.lib.fp8_gemm(A, fa, B, fb, M, N, K, sa, sb, C, ct, None)
+
+
+def test_gemm_validation():
+    import delayed_scaling_amax_amd as d
+    assert _gemm(d, M=-1) == d.EINVAL and _gemm(d, N=-1) == d.EINVAL and _gemm(d, K=-16) == d.EINVAL
+    assert _gemm(d, fa=2) == d.EINVAL and _gemm(d, fb=-1) == d.EINVAL
+    assert _gemm(d, ct=2) == d.EINVAL
+    assert _gemm(d, sa=None) == d.EINVAL and _gemm(d, sb=None) == d.EINVAL
+    assert _gemm(d, C=None) == d.EINVAL
+    assert _gemm(d, A=None) == d.EINVAL and _gemm(d, B=None) == d.EINVAL
+    assert _gemm(d, K=24) == d.EUNSUPPORTED                    # K not a multiple of 16
+    assert _gemm(d, K=(1 << 23) + 16) == d.EUNSUPPORTED
+    assert _gemm(d, A=BAD + 8) == d.EUNSUPPORTED and _gemm(d, B=BAD + 4) == d.EUNSUPPORTED
+    assert _gemm(d, C=BAD + 1, ct=0) == d.EINVAL              # bf16 C misaligned
+    assert _gemm(d, C=BAD + 2, ct=1) == d.EINVAL              # fp32 C misaligned
+    assert _gemm(d, A=None, B=None, C=None, M=0) == d.OK      # empty: nothing enqueued
+    assert _gemm(d, A=None, B=None, C=None, N=0) == d.OK
 
 
 def test_gelu_quantize_takes_bf16_only():

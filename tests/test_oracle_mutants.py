@@ -83,6 +83,8 @@ MUTANTS = [
     ("gemm_inf_times_zero", "if (sa_ == 0 || sb_ == 0) nan = 1;", "if (sa_ == 0 || sb_ == 0) continue;"),
     ("gemm_nan_ignored", "if (a.special == 2 || b.special == 2) { nan = 1; continue; }",
      "if (a.special == 2 || b.special == 2) { continue; }"),
+    ("gemm_group_of_four", "if (k % 8 == 0) { gsum += gmax; gmax = 0.0; }",
+     "if (k % 4 == 0) { gsum += gmax; gmax = 0.0; }"),
     ("dequant_nan_unsigned", "uint32_t nan_bits = 0x7FC00000u | ((uint32_t)(src[i] & 0x80) << 24);",
      "uint32_t nan_bits = 0x7FC00000u;"),
 ]
