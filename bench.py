@@ -10,7 +10,8 @@ E4M3, history 16).  Prints one JSON line.
 Also measured in the same run: the batched update of 1152 tensors with history 1024
 (kernel time warm and cold, host wall time per call), dequantize, the gelu-fused
 quantize of the MLP's FFN activation against the unfused gelu-then-quantize sequence,
-a device-to-device copy as the achievable-bandwidth context, and the CPU oracle on the same step (cpu_baseline), whose
+the LayerNorm-fused quantize against LayerNorm-then-quantize, the FP8 GEMM consumer
+on the MLP's two dense shapes against torch._scaled_mm, a device-to-device copy as the achievable-bandwidth context, and the CPU oracle on the same step (cpu_baseline), whose
 output is compared byte for byte with the GPU's first step.
 """
 from __future__ import annotations
@@ -28,6 +29,7 @@ sys.path.insert(0, ROOT)
 import numpy as np  # noqa: E402
 
 PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E, published
+PEAK_FP8_TFLOPS = 5000.0  # MI355X dense FP8 matrix throughput, published
 METRIC = "fused quantize+amax GB/s & % HBM peak; µs per batched scale update"
 KERNEL_SOURCE = os.path.join(ROOT, "delayed_scaling_amax_amd", "csrc", "quantize_amax.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "quantize_amax_mlp_4096_traffic.txt")
@@ -112,6 +114,8 @@ def main():
                     help="skip the gelu-fused quantize measurement")
     ap.add_argument("--no-ln", action="store_true",
                     help="skip the layernorm-fused quantize measurement")
+    ap.add_argument("--no-gemm", action="store_true",
+                    help="skip the FP8 GEMM consumer comparison")
     ap.add_argument("--update-calls", type=int, default=200)
     ap.add_argument("--rotate", type=int, default=3,
                     help="input/output sets used in turn by successive steps")
@@ -374,6 +378,46 @@ def main():
             lf_us, l_bytes / (lf_us * 1e-6) / 1e9, lu_us))
         del lsets, ldst
 
+    # ------------------------------------------------------------ FP8 GEMM consumer
+    # (not in the step) the MLP's two dense layers on the codes the step produced: the
+    # activation (8192 x 4096 E4M3) times wi (its 16384 x 4096 codes read K-contiguous),
+    # and an (8192 x 16384) E4M3 activation (seeded N(0,1) x 40) times wo (its 4096 x
+    # 16384 codes); per-tensor scale_inv of the step as the operand scales, bf16 out.
+    # torch._scaled_mm (hipBLASLt) on the same operands alongside.
+    gemm_out = None
+    if not args.no_gemm and w.name == "mlp_4096":
+        gen = torch.Generator(device=dev).manual_seed(12)
+        h_codes = (torch.randn(8192, 16384, device=dev, generator=gen) * 40).to(
+            torch.float8_e4m3fn).view(torch.uint8)
+        cases = [("wi", dsts[0].view(8192, 4096), dsts[1].view(16384, 4096), 0, 1),
+                 ("wo", h_codes, dsts[2].view(4096, 16384), 0, 2)]
+        gemm_out = {"peak_tflops": PEAK_FP8_TFLOPS, "out": "bf16", "shapes": []}
+        for name, A, B, ia, ib in cases:
+            M, K = A.shape
+            N = B.shape[0]
+            C = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
+            sa, sb = scale_inv[ia:ia + 1], scale_inv[ib:ib + 1]
+            g_us = timed_launches(lambda i: d.fp8_gemm(A, 0, B, 0, sa, sb, C))
+            flops = 2.0 * M * N * K
+            rec = {"layer": name, "M": M, "N": N, "K": K, "events_median_us": round(g_us, 3),
+                   "tflops": round(flops / g_us / 1e6, 1),
+                   "frac_fp8_peak": round(flops / g_us / 1e6 / PEAK_FP8_TFLOPS, 4)}
+            try:
+                A8, B8 = A.view(torch.float8_e4m3fn), B.view(torch.float8_e4m3fn)
+                t_us = timed_launches(lambda i: torch._scaled_mm(
+                    A8, B8.t(), scale_a=sa, scale_b=sb, out_dtype=torch.bfloat16))
+                rec["torch_scaled_mm_us"] = round(t_us, 3)
+                rec["torch_scaled_mm_tflops"] = round(flops / t_us / 1e6, 1)
+            except (RuntimeError, TypeError) as e:
+                rec["torch_scaled_mm"] = "unavailable: %s" % str(e)[:80]
+            gemm_out["shapes"].append(rec)
+            log("gemm %s %dx%dx%d: %.1f us (%.0f TFLOP/s)%s" % (
+                name, M, N, K, g_us, flops / g_us / 1e6,
+                ", torch._scaled_mm %.1f us" % rec["torch_scaled_mm_us"]
+                if "torch_scaled_mm_us" in rec else ""))
+            del C
+        del h_codes
+
     # ------------------------------------------------------------ copy context
     cbuf = torch.empty(1 << 27, dtype=torch.float32, device=dev)  # 512 MiB
     cdst = torch.empty_like(cbuf)
@@ -417,6 +461,7 @@ def main():
                        "gbps": round(dq_bytes / (dq_us * 1e-6) / 1e9, 1)},
         "gelu_quantize": gelu_out,
         "layernorm_quantize": ln_out,
+        "fp8_gemm": gemm_out,
         "copy_d2d_gbps": round(copy_gbps, 1),
         "roofline": {"bound": "hbm", "achieved": round(q_gbps, 1), "peak": PEAK_HBM_GBPS,
                      "unit": "GB/s", "frac": round(q_gbps / PEAK_HBM_GBPS, 4),
