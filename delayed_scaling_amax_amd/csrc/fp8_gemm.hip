@@ -27,12 +27,23 @@
 //    set.
 //  * Edges: rows past M or N and 16-byte chunks past K are loaded through offsets outside
 //    the buffer resource, which the hardware returns as zeros; stores are masked.
-//  * Epilogue: bf16 output with N a multiple of 8 goes through LDS (the ring is free by
-//    then) and leaves as 16-byte row-contiguous stores; otherwise element stores.
-//  * Tile order: row-major over the tile grid (block b is tile b).  A and B of the MLP
-//    shapes (tens of MB) stay in the 256 MB MALL, so re-reads of a slice by blocks on
-//    other XCDs rarely reach HBM; a remap giving each XCD a contiguous tile range measured
-//    slower on the large shapes.
+//  * Registers: 256 accumulators in AGPRs, two fragment sets (128 VGPRs); lane-derived
+//    offsets are rebuilt per tile so nothing spills.
+//  * Epilogue: B is the MFMA's first operand, so each lane holds four consecutive
+//    columns of a C row per register quad.  With C 16-byte aligned and N a multiple of
+//    8 (bf16) or 4 (fp32), lanes l and l + 32 exchange quads (v_permlane32_swap) so that
+//    each holds 8 consecutive bf16 columns, and every lane issues 16-byte buffer stores,
+//    the same number per tile whatever the edges (masked elements use an offset past the
+//    resource).  Otherwise element stores.
+//  * Persistent blocks, one per compute unit, walk the tiles in row-major order with a
+//    stride of the grid size (so the blocks in flight cover 256 consecutive tiles, as a
+//    plain grid would).  The last two ring refills of a tile fetch the next tile's first
+//    two stages, so the epilogue's stores overlap those loads and the next tile's first
+//    MFMAs.  A and B of the MLP shapes (tens of MB) stay in the 256 MB MALL, so re-reads
+//    of a slice by blocks on other XCDs rarely reach HBM; a remap giving each XCD a
+//    contiguous tile range measured slower.
+#include <type_traits>
+
 #include "device_common.h"
 #include "host_common.h"
 #include "quant_math.h"
@@ -47,6 +58,14 @@ constexpr int kGThreads = 256;
 constexpr int kGStages = 2;    // LDS ring: stage t + 2 loads while t + 1 waits
 constexpr int kGTileBytes = kGBM * kGBK;  // 32 KB per operand per stage
 constexpr int kGDmaPerWave = kGTileBytes / 1024 / (kGThreads / 64);  // 1 KB DMA ops per wave
+constexpr int kGEpiStores = 32;  // 16-byte stores per wave of a bf16 tile (vector path)
+#ifndef FP8Q_GEMM_ST_AUX
+#define FP8Q_GEMM_ST_AUX 0
+#endif
+// C store cache policy: the default.  The epilogue writes each 128-byte line of C in
+// quarter-line pieces over a few consecutive stores, which merge in L2; non-temporal
+// stores bypass that merge and measured 20-25% slower on the MLP shapes.
+constexpr int kGStAux = FP8Q_GEMM_ST_AUX;
 
 struct GemmArgs {
   const uint8_t* A;
@@ -55,12 +74,14 @@ struct GemmArgs {
   const float* sa;
   const float* sb;
   int64_t M, N, K;
-  int64_t nbn;    // column tiles
-  int32_t vec_c;  // bf16 C with N % 8 == 0 and 16-byte alignment: 16-byte row stores
+  uint32_t nbn;     // column tiles
+  uint32_t ntiles;  // row tiles x column tiles (< 2^31)
+  int32_t vec_c;   // 16-byte C stores (see fp8_gemm below)
   int32_t pad;
 };
 
 typedef int g_v8i __attribute__((ext_vector_type(8)));
+typedef uint32_t g_u32x4 __attribute__((ext_vector_type(4)));
 typedef float g_v16f __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) void g_lds_t;
 
@@ -79,22 +100,21 @@ __device__ __forceinline__ int g_swz(int r) { return (r >> 1) & 7; }
 // 8 (w kGDmaPerWave + j) .. +7) writes lane l's 16 bytes to row 8 j' + l / 8, slot
 // l mod 8, loading the logical chunk held there.  A and B tiles have the same shape, so
 // one offset serves both.  Rows past the resource (M or N) and chunks past K load zeros
-// (offset 0xFFFFFFF0 is past every resource; K is a multiple of 16, so in-range offsets
-// have their low 4 bits clear and the OR below yields that offset).
+// (offset 0xFFFFFFF0 is past every resource).
 __device__ __forceinline__ void g_stage_dma(g_lds_t* ta, g_lds_t* tb, __amdgpu_buffer_rsrc_t ra,
-                                            __amdgpu_buffer_rsrc_t rb, int64_t K, int64_t k0,
+                                            __amdgpu_buffer_rsrc_t rb, uint32_t K, uint32_t k0,
                                             int wave, int lane) {
+  // 32-bit offsets: rows < 256, K <= 2^23, k0 < K + 512
+  const uint32_t rl = lane >> 3, rlK = rl * K;
 #pragma unroll
   for (int j = 0; j < kGDmaPerWave; ++j) {
-    const int blk = wave * kGDmaPerWave + j;
-    const int row = 8 * blk + (lane >> 3);
-    const int c = (lane & 7) ^ g_swz(row);
-    const int64_t k = k0 + 16 * c;
-    const uint32_t past = 0u - (uint32_t)(k >= K);
-    const uint32_t voff = (uint32_t)(row * K + k) | (past & 0xFFFFFFF0u);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (g_lds_t*)((__attribute__((address_space(3))) uint8_t*)ta + 1024 * blk),
+    const uint32_t row0 = 8 * (wave * kGDmaPerWave + j);  // wave-uniform
+    const uint32_t c = (lane & 7) ^ (((row0 + rl) >> 1) & 7);
+    const uint32_t k = k0 + 16 * c;
+    const uint32_t voff = k < K ? rlK + row0 * K + k : 0xFFFFFFF0u;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (g_lds_t*)((__attribute__((address_space(3))) uint8_t*)ta + 1024 * (row0 / 8)),
                                              16, voff, 0, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (g_lds_t*)((__attribute__((address_space(3))) uint8_t*)tb + 1024 * blk),
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (g_lds_t*)((__attribute__((address_space(3))) uint8_t*)tb + 1024 * (row0 / 8)),
                                              16, voff, 0, 0, 0);
   }
 }
@@ -112,162 +132,242 @@ __device__ __forceinline__ g_v8i g_frag(const uint8_t* tile, int row, int ch) {
 #define G_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 0xF) | (0x7 << 4) | (0xF << 8) | (((n) >> 4) << 14))
 #define G_WAIT_VMCNT_LGKM0(n) __builtin_amdgcn_s_waitcnt(((n) & 0xF) | (0x7 << 4) | (((n) >> 4) << 14))
 
+// Buffer resource over the block rows of tile `tile` (whole K); a tile index past the
+// grid gives an empty resource, whose loads return zeros without touching memory.
+__device__ __forceinline__ void g_tile_rsrc(const GemmArgs& g, uint32_t tile,
+                                            __amdgpu_buffer_rsrc_t& ra,
+                                            __amdgpu_buffer_rsrc_t& rb) {
+  const bool live = tile < g.ntiles;
+  const uint32_t bm = live ? tile / g.nbn : 0, bn = live ? tile % g.nbn : 0;
+  const int64_t m0 = (int64_t)bm * kGBM, n0 = (int64_t)bn * kGBN;
+  const int64_t rows_a = live ? (g.M - m0 < kGBM ? g.M - m0 : kGBM) : 0;
+  const int64_t rows_b = live ? (g.N - n0 < kGBN ? g.N - n0 : kGBN) : 0;
+  ra = g_rsrc(g.A + m0 * g.K, (uint32_t)(rows_a * g.K));
+  rb = g_rsrc(g.B + n0 * g.K, (uint32_t)(rows_b * g.K));
+}
+
 template <int kFa, int kFb, bool kBf16Out>
 __global__ __launch_bounds__(kGThreads) void fp8_gemm_kernel(const GemmArgs g) {
   // one LDS object per stage and operand: the compiler tracks the DMA writes of each
-  // separately and waits only for the stage being read
+  // separately
   __shared__ __attribute__((aligned(16))) uint8_t a0[kGTileBytes], a1[kGTileBytes],
       b0[kGTileBytes], b1[kGTileBytes];
   uint8_t* const sa_[kGStages] = {a0, a1};
   uint8_t* const sb_[kGStages] = {b0, b1};
   const int tid = threadIdx.x;
-  const int lane = tid & 63;
+  const int lane0 = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
-  const int64_t tile = blockIdx.x;
-  const int64_t bm = tile / g.nbn, bn = tile % g.nbn;
-  const int64_t m0 = bm * kGBM, n0 = bn * kGBN;
-  const int64_t rows_a = g.M - m0 < kGBM ? g.M - m0 : kGBM;
-  const int64_t rows_b = g.N - n0 < kGBN ? g.N - n0 : kGBN;
-  // resources over exactly the block's rows (whole K): rows past M / N read as zeros
-  const __amdgpu_buffer_rsrc_t ra = g_rsrc(g.A + m0 * g.K, (uint32_t)(rows_a * g.K));
-  const __amdgpu_buffer_rsrc_t rb = g_rsrc(g.B + n0 * g.K, (uint32_t)(rows_b * g.K));
+  const float s = uniform(*g.sa) * uniform(*g.sb);
 
-  g_v16f acc[4][4];
+  // Persistent blocks: block b computes tiles b, b + G, b + 2G, ... (G = grid size), in
+  // row-major order over the tile grid.  Per tile, K is consumed in stages t of 128
+  // bytes (ring slot t mod 2), each in two sub-steps of 64 bytes.  Sub-step (t, 0): the
+  // 16 MFMAs on the fragments of (t, 0) run while those of (t, 1) are read from the same
+  // slot.  Sub-step (t, 1): a wave waits for its own DMA of stage t + 1 (the only one in
+  // flight) and its LDS reads; after the barrier (every wave's DMA of stage t + 1 has
+  // landed, every wave has finished reading slot t) it refills slot t with stage t + 2,
+  // or, for the last two stages, with stage 0 or 1 of its next tile, and reads (t + 1, 0)
+  // while the MFMAs of (t, 1) run.  So a tile's epilogue overlaps the loads of the next.
+  // Stages are rounded up to a multiple of the ring size; stages past K load zeros (and
+  // touch no memory).
+  const int64_t nk0 = ((g.K + kGBK - 1) / kGBK + kGStages - 1) / kGStages * kGStages;
+  const int64_t nk = nk0 > kGStages ? nk0 : kGStages;  // at least one round (K = 0 too)
+  uint32_t tile = blockIdx.x;  // wave-uniform throughout
+  __amdgpu_buffer_rsrc_t ra, rb, rna, rnb;
+  g_tile_rsrc(g, tile, ra, rb);
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = g_v16f{};
-
-  // Software pipeline over K stages t (128 bytes each, ring slot t mod 2), each consumed
-  // in two sub-steps of 64 bytes.  Sub-step (t, 0): the 16 MFMAs on the fragments of
-  // (t, 0) run while those of (t, 1) are read from the same slot.  Sub-step (t, 1): a
-  // wave waits for its own DMA of stage t + 1 (the only one in flight) and its LDS reads,
-  // and after the barrier (every wave's DMA of stage t + 1 has landed, every wave has
-  // finished reading slot t) refills slot t with stage t + 2 and reads (t + 1, 0) while
-  // the MFMAs of (t, 1) run.  Stages are rounded up to a multiple of the ring size;
-  // stages past K load zeros (and touch no memory).
-  const int64_t nk = ((g.K + kGBK - 1) / kGBK + kGStages - 1) / kGStages * kGStages;
-  const int frow = lane & 31, fch = 2 * (lane >> 5);
-  const int ra0 = wm * 128 + frow, rb0 = wn * 128 + frow;
-#pragma unroll
-  for (int s = 0; s < kGStages; ++s)
-    g_stage_dma((g_lds_t*)sa_[s], (g_lds_t*)sb_[s], ra, rb, g.K, s * kGBK, wave, lane);
+  for (int st = 0; st < kGStages; ++st)
+    g_stage_dma((g_lds_t*)sa_[st], (g_lds_t*)sb_[st], ra, rb, (uint32_t)g.K, st * kGBK, wave,
+                lane0);
   g_v8i af[2][4], bf[2][4];
-  G_WAIT_VMCNT(2 * kGDmaPerWave);
+  // both stages: the first round's first wait allows kGEpiStores younger ops in flight
+  G_WAIT_VMCNT(0);
   __builtin_amdgcn_s_barrier();
 #pragma unroll
-  for (int i = 0; i < 4; ++i) af[0][i] = g_frag(sa_[0], ra0 + 32 * i, fch);
+  for (int i = 0; i < 4; ++i) af[0][i] = g_frag(sa_[0], wm * 128 + (lane0 & 31) + 32 * i, 2 * (lane0 >> 5));
 #pragma unroll
-  for (int j = 0; j < 4; ++j) bf[0][j] = g_frag(sb_[0], rb0 + 32 * j, fch);
-  for (int64_t kt = 0; kt < nk; kt += kGStages) {
-#pragma unroll
-    for (int s = 0; s < kGStages; ++s) {
-      // sub-step (t, 0)
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) af[1][i] = g_frag(sa_[s], ra0 + 32 * i, fch + 4);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) bf[1][j] = g_frag(sb_[s], rb0 + 32 * j, fch + 4);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[0][i], bf[0][j],
-                                                                     acc[i][j], kFa, kFb, 0, 127,
-                                                                     0, 127);
-#pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      }
-      // sub-step (t, 1)
-      G_WAIT_VMCNT_LGKM0(0);
-      __builtin_amdgcn_s_barrier();
-      __builtin_amdgcn_sched_barrier(0);
-      g_stage_dma((g_lds_t*)sa_[s], (g_lds_t*)sb_[s], ra, rb, g.K, (kt + s + kGStages) * kGBK,
-                  wave, lane);
-      const int s1 = (s + 1) % kGStages;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) af[0][i] = g_frag(sa_[s1], ra0 + 32 * i, fch);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) bf[0][j] = g_frag(sb_[s1], rb0 + 32 * j, fch);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[1][i], bf[1][j],
-                                                                     acc[i][j], kFa, kFb, 0, 127,
-                                                                     0, 127);
-      // each MFMA is followed by one fragment read and one DMA issue
-#pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-      }
-    }
-  }
-  // no LDS DMA may still be in flight when the ring is reused or the block exits
-  G_WAIT_VMCNT(0);
+  for (int j = 0; j < 4; ++j) bf[0][j] = g_frag(sb_[0], wn * 128 + (lane0 & 31) + 32 * j, 2 * (lane0 >> 5));
 
-  // epilogue: C = acc * (sa * sb); accumulator r of a 32 x 32 tile holds row
-  // (r mod 4) + 8 (r / 4) + 4 (lane / 32), column lane mod 32
-  const float s = uniform(*g.sa) * uniform(*g.sb);
-  if constexpr (kBf16Out) {
-    if (g.vec_c) {
-      // through LDS (the ring is free now): each wave writes its 128 x 128 bf16 tile
-      // into one 32 KB object (128 rows of 256 bytes) and stores it back row by row, 16
-      // bytes per lane
-      __syncthreads();
-      uint8_t* const e = wave == 0 ? a0 : wave == 1 ? a1 : wave == 2 ? b0 : b1;
+  while (tile < g.ntiles) {
+    // Lane-derived offsets are rebuilt per tile from an opaque copy of the lane index:
+    // hoisted to the kernel start they would stay live across the whole tile loop and
+    // spill (each reload then waits for every memory op in flight).
+    int lane = lane0;
+    asm volatile("" : "+v"(lane));
+    const int frow = lane & 31, fch = 2 * (lane >> 5);
+    const int ra0 = wm * 128 + frow, rb0 = wn * 128 + frow;
+    const uint32_t next = __builtin_amdgcn_readfirstlane(tile + gridDim.x);
+    g_tile_rsrc(g, next, rna, rnb);
+    g_v16f acc[4][4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < 4; ++j) acc[i][j] = g_v16f{};
+    // One round = kGStages stages.  The first round of a tile differs only in its first
+    // wait: the previous tile's epilogue may have left up to kGEpiStores stores per wave
+    // in flight, issued after the DMA of stage 1; vmcnt drains in issue order, so waiting
+    // down to that many suffices (more in flight only makes the wait stricter, and every
+    // other case has fewer ops in flight: see the prologue and the element-store path).
+    auto round = [&](auto first_round, int64_t kt) {
+      constexpr bool kFirst = decltype(first_round)::value;
+      // refills of this round: stages kt + 2, kt + 3 of this tile, or the next tile's
+      // first two stages when this is the tile's last round
+      const bool last = kt + kGStages >= nk;
+      const __amdgpu_buffer_rsrc_t qa = last ? rna : ra, qb = last ? rnb : rb;
+      const int64_t qk = last ? 0 : (kt + kGStages) * kGBK;
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int rl = i * 32 + (r & 3) + 8 * (r >> 2) + 4 * (lane >> 5);
-            const int cl = j * 32 + (lane & 31);
-            uint8_t* o = e + rl * 256 + 2 * cl;
-            *(uint16_t*)o = (uint16_t)(pack_bf16_rne(acc[i][j][r] * s, 0.0f) & 0xFFFFu);
-          }
-#pragma unroll 4
-      for (int c = 0; c < 32; ++c) {
-        const int qi = lane + 64 * c;  // 16-byte chunk of the wave tile
-        const int rl = qi >> 4, cl = 8 * (qi & 15);
-        const uint4 v = *(const uint4*)(e + rl * 256 + 2 * cl);
-        const int64_t row = m0 + wm * 128 + rl, col = n0 + wn * 128 + cl;
-        if (row < g.M && col < g.N) *(uint4*)((uint16_t*)g.C + row * g.N + col) = v;
-      }
-      return;
-    }
-  }
+      for (int st = 0; st < kGStages; ++st) {
+        // sub-step (t, 0)
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < 4; ++i) af[1][i] = g_frag(sa_[st], ra0 + 32 * i, fch + 4);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int64_t col = n0 + wn * 128 + j * 32 + (lane & 31);
+        for (int j = 0; j < 4; ++j) bf[1][j] = g_frag(sb_[st], rb0 + 32 * j, fch + 4);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int64_t row = m0 + wm * 128 + i * 32 + (r & 3) + 8 * (r >> 2) + 4 * (lane >> 5);
-        if (row < g.M && col < g.N) {
-          const float v = acc[i][j][r] * s;
-          if constexpr (kBf16Out)
-            ((uint16_t*)g.C)[row * g.N + col] = (uint16_t)(pack_bf16_rne(v, 0.0f) & 0xFFFFu);
-          else
-            ((float*)g.C)[row * g.N + col] = v;
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                bf[0][j], af[0][i], acc[i][j], kFb, kFa, 0, 127, 0, 127);
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        // sub-step (t, 1)
+        if (kFirst && st == 0)
+          G_WAIT_VMCNT_LGKM0(kGEpiStores);
+        else
+          G_WAIT_VMCNT_LGKM0(0);
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        g_stage_dma((g_lds_t*)sa_[st], (g_lds_t*)sb_[st], qa, qb, (uint32_t)g.K,
+                    (uint32_t)(qk + st * kGBK), wave, lane);
+        const int s1 = (st + 1) % kGStages;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) af[0][i] = g_frag(sa_[s1], ra0 + 32 * i, fch);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) bf[0][j] = g_frag(sb_[s1], rb0 + 32 * j, fch);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                bf[1][j], af[1][i], acc[i][j], kFb, kFa, 0, 127, 0, 127);
+        // each MFMA is followed by one fragment read and one DMA issue
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
         }
       }
+    };
+    round(std::true_type{}, 0);
+    for (int64_t kt = kGStages; kt < nk; kt += kGStages) round(std::false_type{}, kt);
+
+    // epilogue: C = acc * (sa * sb).  With B as the MFMA's first operand, accumulator r
+    // of the 32 x 32 tile (i, j) holds C row i * 32 + lane mod 32, column
+    // j * 32 + (r mod 4) + 8 (r / 4) + 4 h (h = lane / 32): register quad q holds four
+    // consecutive columns 8 q + 4 h.
+    const int64_t m0 = (int64_t)(tile / g.nbn) * kGBM, n0 = (int64_t)(tile % g.nbn) * kGBN;
+    if (g.vec_c) {
+      // Buffer stores through a resource over C from (m0, n0) on; masked elements use an
+      // offset past it (dropped by the hardware), so every wave issues the same number
+      // of stores per tile.
+      constexpr int kElt = kBf16Out ? 2 : 4;
+      const int64_t rem = ((g.M - m0) * g.N - n0) * kElt;
+      const __amdgpu_buffer_rsrc_t rc =
+          g_rsrc((uint8_t*)g.C + (m0 * g.N + n0) * kElt,
+                 (uint32_t)(rem < 0x7FFFFFF0 ? rem : 0x7FFFFFF0));
+      const int h = lane >> 5;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int rl = wm * 128 + i * 32 + (lane & 31);
+        const bool row_ok = m0 + rl < g.M;
+        const uint32_t rbase = (uint32_t)(rl * g.N) * kElt;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          // one 32 x 32 tile at a time: keeps the accumulator reads from being hoisted
+          __builtin_amdgcn_sched_barrier(0);
+          if constexpr (kBf16Out) {
+            // quads 2 p and 2 p + 1 of the lane pair (l, l + 32) are exchanged so that
+            // lane l holds columns 16 p .. + 7 and lane l + 32 columns 16 p + 8 .. + 15
+#pragma unroll
+            for (int p = 0; p < 2; ++p) {
+              const uint32_t x0 = pack_bf16_rne(acc[i][j][8 * p] * s, acc[i][j][8 * p + 1] * s);
+              const uint32_t x1 = pack_bf16_rne(acc[i][j][8 * p + 2] * s, acc[i][j][8 * p + 3] * s);
+              const uint32_t y0 = pack_bf16_rne(acc[i][j][8 * p + 4] * s, acc[i][j][8 * p + 5] * s);
+              const uint32_t y1 = pack_bf16_rne(acc[i][j][8 * p + 6] * s, acc[i][j][8 * p + 7] * s);
+              const auto w0 = __builtin_amdgcn_permlane32_swap(x0, y0, false, false);
+              const auto w1 = __builtin_amdgcn_permlane32_swap(x1, y1, false, false);
+              const int cl = wn * 128 + j * 32 + 16 * p + 8 * h;
+              const bool ok = row_ok && n0 + cl < g.N;
+              const uint32_t voff = ok ? rbase + (uint32_t)cl * 2 : 0x80000000u;
+              __builtin_amdgcn_raw_buffer_store_b128(
+                  g_u32x4{(uint32_t)w0[0], (uint32_t)w1[0], (uint32_t)w0[1], (uint32_t)w1[1]}, rc,
+                  voff, 0, kGStAux);
+            }
+          } else {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const int cl = wn * 128 + j * 32 + 8 * q + 4 * h;
+              const bool ok = row_ok && n0 + cl < g.N;
+              const uint32_t voff = ok ? rbase + (uint32_t)cl * 4 : 0x80000000u;
+              __builtin_amdgcn_raw_buffer_store_b128(
+                  g_u32x4{__float_as_uint(acc[i][j][4 * q] * s),
+                        __float_as_uint(acc[i][j][4 * q + 1] * s),
+                        __float_as_uint(acc[i][j][4 * q + 2] * s),
+                        __float_as_uint(acc[i][j][4 * q + 3] * s)},
+                  rc, voff, 0, kGStAux);
+            }
+          }
+        }
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int64_t row = m0 + wm * 128 + i * 32 + (lane & 31);
+        if (row < g.M) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const int64_t col = n0 + wn * 128 + j * 32 + 8 * q + 4 * (lane >> 5);
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                if (col + e < g.N) {
+                  const float v = acc[i][j][4 * q + e] * s;
+                  if constexpr (kBf16Out)
+                    ((uint16_t*)g.C)[row * g.N + col + e] =
+                        (uint16_t)(pack_bf16_rne(v, 0.0f) & 0xFFFFu);
+                  else
+                    ((float*)g.C)[row * g.N + col + e] = v;
+                }
+            }
+        }
+      }
+      // element stores are not counted: drain them before the next tile's first wait
+      G_WAIT_VMCNT(0);
     }
+    tile = next;
+    ra = rna;
+    rb = rnb;
+  }
+  // no LDS DMA may still be in flight when the block exits
+  G_WAIT_VMCNT(0);
 }
 
 template <int kFa, int kFb>
 static int gemm_launch(const GemmArgs& g, bool bf16_out, hipStream_t stream) {
   const void* fn = bf16_out ? (const void*)fp8_gemm_kernel<kFa, kFb, true>
                             : (const void*)fp8_gemm_kernel<kFa, kFb, false>;
-  const int64_t nbm = (g.M + kGBM - 1) / kGBM;
-  const int64_t blocks = nbm * g.nbn;
+  int cus = 0;
+  const int rc = current_device_cus(&cus);
+  if (rc != FP8Q_OK) return rc;
+  // one block per compute unit (the 128 KB ring and 512 registers per lane allow one)
+  const int64_t blocks = (int64_t)g.ntiles < cus ? (int64_t)g.ntiles : cus;
   void* args[] = {(void*)&g};
   return launch_status(hipLaunchKernel(fn, dim3((unsigned)blocks), dim3(kGThreads), args, 0, stream));
 }
@@ -303,8 +403,11 @@ extern "C" int fp8_gemm(const uint8_t* A, int a_format, const uint8_t* B, int b_
   g.M = M;
   g.N = N;
   g.K = K;
-  g.nbn = nbn;
-  g.vec_c = c_dtype == FP8Q_BF16 && N % 8 == 0 && (uintptr_t)C % 16 == 0;
+  g.nbn = (uint32_t)nbn;
+  g.ntiles = (uint32_t)(nbm * nbn);
+  // vector path: 16-byte stores of 8 bf16 / 4 fp32 columns, tile offsets within 2^31
+  const int64_t elt = c_dtype == FP8Q_BF16 ? 2 : 4;
+  g.vec_c = N % (16 / elt) == 0 && (uintptr_t)C % 16 == 0 && kGBM * N * elt < ((int64_t)1 << 31);
   g.pad = 0;
   const bool bf16 = c_dtype == FP8Q_BF16;
   const hipStream_t st = (hipStream_t)stream;
