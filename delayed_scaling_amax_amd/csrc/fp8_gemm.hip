@@ -42,8 +42,6 @@
 //    MFMAs.  A and B of the MLP shapes (tens of MB) stay in the 256 MB MALL, so re-reads
 //    of a slice by blocks on other XCDs rarely reach HBM; a remap giving each XCD a
 //    contiguous tile range measured slower.
-#include <type_traits>
-
 #include "device_common.h"
 #include "host_common.h"
 #include "quant_math.h"
@@ -58,7 +56,6 @@ constexpr int kGThreads = 256;
 constexpr int kGStages = 2;    // LDS ring: stage t + 2 loads while t + 1 waits
 constexpr int kGTileBytes = kGBM * kGBK;  // 32 KB per operand per stage
 constexpr int kGDmaPerWave = kGTileBytes / 1024 / (kGThreads / 64);  // 1 KB DMA ops per wave
-constexpr int kGEpiStores = 32;  // 16-byte stores per wave of a bf16 tile (vector path)
 #ifndef FP8Q_GEMM_ST_AUX
 #define FP8Q_GEMM_ST_AUX 0
 #endif
@@ -181,8 +178,7 @@ __global__ __launch_bounds__(kGThreads) void fp8_gemm_kernel(const GemmArgs g) {
     g_stage_dma((g_lds_t*)sa_[st], (g_lds_t*)sb_[st], ra, rb, (uint32_t)g.K, st * kGBK, wave,
                 lane0);
   g_v8i af[2][4], bf[2][4];
-  // both stages: the first round's first wait allows kGEpiStores younger ops in flight
-  G_WAIT_VMCNT(0);
+  G_WAIT_VMCNT(2 * kGDmaPerWave);  // stage 0 (stage 1 stays in flight)
   __builtin_amdgcn_s_barrier();
 #pragma unroll
   for (int i = 0; i < 4; ++i) af[0][i] = g_frag(sa_[0], wm * 128 + (lane0 & 31) + 32 * i, 2 * (lane0 >> 5));
@@ -204,13 +200,10 @@ __global__ __launch_bounds__(kGThreads) void fp8_gemm_kernel(const GemmArgs g) {
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j) acc[i][j] = g_v16f{};
-    // One round = kGStages stages.  The first round of a tile differs only in its first
-    // wait: the previous tile's epilogue may have left up to kGEpiStores stores per wave
-    // in flight, issued after the DMA of stage 1; vmcnt drains in issue order, so waiting
-    // down to that many suffices (more in flight only makes the wait stricter, and every
-    // other case has fewer ops in flight: see the prologue and the element-store path).
-    auto round = [&](auto first_round, int64_t kt) {
-      constexpr bool kFirst = decltype(first_round)::value;
+    // One round = kGStages stages.  The first round of a tile is peeled off the loop: the
+    // same code, but the register allocation of the peeled form measured free of spills
+    // (the plain loop spilled ~100 VGPRs).
+    auto round = [&](int64_t kt) {
       // refills of this round: stages kt + 2, kt + 3 of this tile, or the next tile's
       // first two stages when this is the tile's last round
       const bool last = kt + kGStages >= nk;
@@ -235,11 +228,10 @@ __global__ __launch_bounds__(kGThreads) void fp8_gemm_kernel(const GemmArgs g) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
           __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         }
-        // sub-step (t, 1)
-        if (kFirst && st == 0)
-          G_WAIT_VMCNT_LGKM0(kGEpiStores);
-        else
-          G_WAIT_VMCNT_LGKM0(0);
+        // sub-step (t, 1).  A full drain: with loads and the previous tile's epilogue
+        // stores both outstanding, vmcnt is not guaranteed to drain in issue order, and
+        // the barrier below publishes this wave's DMA of stage t + 1 to the others.
+        G_WAIT_VMCNT_LGKM0(0);
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_sched_barrier(0);
         g_stage_dma((g_lds_t*)sa_[st], (g_lds_t*)sb_[st], qa, qb, (uint32_t)g.K,
@@ -264,8 +256,8 @@ __global__ __launch_bounds__(kGThreads) void fp8_gemm_kernel(const GemmArgs g) {
         }
       }
     };
-    round(std::true_type{}, 0);
-    for (int64_t kt = kGStages; kt < nk; kt += kGStages) round(std::false_type{}, kt);
+    round(0);
+    for (int64_t kt = kGStages; kt < nk; kt += kGStages) round(kt);
 
     // epilogue: C = acc * (sa * sb).  With B as the MFMA's first operand, accumulator r
     // of the 32 x 32 tile (i, j) holds C row i * 32 + lane mod 32, column
@@ -274,8 +266,7 @@ __global__ __launch_bounds__(kGThreads) void fp8_gemm_kernel(const GemmArgs g) {
     const int64_t m0 = (int64_t)(tile / g.nbn) * kGBM, n0 = (int64_t)(tile % g.nbn) * kGBN;
     if (g.vec_c) {
       // Buffer stores through a resource over C from (m0, n0) on; masked elements use an
-      // offset past it (dropped by the hardware), so every wave issues the same number
-      // of stores per tile.
+      // offset past it (dropped by the hardware).
       constexpr int kElt = kBf16Out ? 2 : 4;
       const int64_t rem = ((g.M - m0) * g.N - n0) * kElt;
       const __amdgpu_buffer_rsrc_t rc =
@@ -348,8 +339,6 @@ __global__ __launch_bounds__(kGThreads) void fp8_gemm_kernel(const GemmArgs g) {
             }
         }
       }
-      // element stores are not counted: drain them before the next tile's first wait
-      G_WAIT_VMCNT(0);
     }
     tile = next;
     ra = rna;
