@@ -35,13 +35,12 @@
 //    each holds 8 consecutive bf16 columns, and every lane issues 16-byte buffer stores,
 //    the same number per tile whatever the edges (masked elements use an offset past the
 //    resource).  Otherwise element stores.
-//  * Persistent blocks, one per compute unit, walk the tiles in row-major order with a
-//    stride of the grid size (so the blocks in flight cover 256 consecutive tiles, as a
-//    plain grid would).  The last two ring refills of a tile fetch the next tile's first
-//    two stages, so the epilogue's stores overlap those loads and the next tile's first
-//    MFMAs.  A and B of the MLP shapes (tens of MB) stay in the 256 MB MALL, so re-reads
-//    of a slice by blocks on other XCDs rarely reach HBM; a remap giving each XCD a
-//    contiguous tile range measured slower.
+//  * Persistent blocks, one per compute unit, walk the tiles with a stride of the grid
+//    size.  The last two ring refills of a tile fetch the next tile's first two stages,
+//    so the epilogue's stores overlap those loads.  Tile order: the 32 blocks of one XCD
+//    (blocks are dealt to the 8 XCDs in turn) work on one super-tile of 4 x 8 tiles at a
+//    time, so per stage they read 4 A and 8 B slices through their shared L2; A and B of
+//    the MLP shapes (tens of MB) stay in the 256 MB MALL behind it.
 #include "device_common.h"
 #include "host_common.h"
 #include "quant_math.h"
@@ -71,8 +70,10 @@ struct GemmArgs {
   const float* sa;
   const float* sb;
   int64_t M, N, K;
+  uint32_t nbm;     // row tiles
   uint32_t nbn;     // column tiles
   uint32_t ntiles;  // row tiles x column tiles (< 2^31)
+  uint32_t pad2;
   int32_t vec_c;   // 16-byte C stores (see fp8_gemm below)
   int32_t pad;
 };
@@ -129,13 +130,31 @@ __device__ __forceinline__ g_v8i g_frag(const uint8_t* tile, int row, int ch) {
 #define G_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 0xF) | (0x7 << 4) | (0xF << 8) | (((n) >> 4) << 14))
 #define G_WAIT_VMCNT_LGKM0(n) __builtin_amdgcn_s_waitcnt(((n) & 0xF) | (0x7 << 4) | (((n) >> 4) << 14))
 
-// Buffer resource over the block rows of tile `tile` (whole K); a tile index past the
-// grid gives an empty resource, whose loads return zeros without touching memory.
-__device__ __forceinline__ void g_tile_rsrc(const GemmArgs& g, uint32_t tile,
+// Tile order: super-tiles of 4 row tiles x 8 column tiles (smaller at the edges), in
+// row-major order, row-major inside.  When the column-tile count is a multiple of 8, the
+// 8 columns of super-tile column group G are G, G + S, ..., G + 7 S (S = count / 8)
+// rather than 8 G .. 8 G + 7: same L2 sharing, measured 4% faster on the 64-column MLP
+// grid.  Linear index L -> tile (bm, bn); a bijection of [0, ntiles) onto the grid.
+__device__ __forceinline__ void g_tile_coords(const GemmArgs& g, uint32_t L, uint32_t& bm,
+                                              uint32_t& bn) {
+  const uint32_t R = L / (4 * g.nbn);
+  const uint32_t hR = g.nbm - 4 * R < 4 ? g.nbm - 4 * R : 4;
+  const uint32_t Lr = L - R * 4 * g.nbn;
+  const uint32_t G = Lr / (hR * 8);
+  const uint32_t wG = g.nbn - 8 * G < 8 ? g.nbn - 8 * G : 8;
+  const uint32_t loc = Lr - G * hR * 8;
+  bm = 4 * R + loc / wG;
+  bn = g.nbn % 8 == 0 ? G + (g.nbn / 8) * (loc % 8) : 8 * G + loc % wG;
+}
+
+// Buffer resources over the block rows of the tile at linear index L (whole K); an index
+// past the grid gives empty resources, whose loads return zeros without touching memory.
+__device__ __forceinline__ void g_tile_rsrc(const GemmArgs& g, uint32_t L,
                                             __amdgpu_buffer_rsrc_t& ra,
                                             __amdgpu_buffer_rsrc_t& rb) {
-  const bool live = tile < g.ntiles;
-  const uint32_t bm = live ? tile / g.nbn : 0, bn = live ? tile % g.nbn : 0;
+  const bool live = L < g.ntiles;
+  uint32_t bm = 0, bn = 0;
+  if (live) g_tile_coords(g, L, bm, bn);
   const int64_t m0 = (int64_t)bm * kGBM, n0 = (int64_t)bn * kGBN;
   const int64_t rows_a = live ? (g.M - m0 < kGBM ? g.M - m0 : kGBM) : 0;
   const int64_t rows_b = live ? (g.N - n0 < kGBN ? g.N - n0 : kGBN) : 0;
@@ -170,7 +189,12 @@ __global__ __launch_bounds__(kGThreads) void fp8_gemm_kernel(const GemmArgs g) {
   // touch no memory).
   const int64_t nk0 = ((g.K + kGBK - 1) / kGBK + kGStages - 1) / kGStages * kGStages;
   const int64_t nk = nk0 > kGStages ? nk0 : kGStages;  // at least one round (K = 0 too)
-  uint32_t tile = blockIdx.x;  // wave-uniform throughout
+  // Block b takes linear indices L = w G + pos(b), w = 0, 1, ... (G = grid size).  Blocks
+  // are dealt to the 8 XCDs in turn, so pos gives the G / 8 blocks of one XCD consecutive
+  // indices: one super-tile per XCD per wave of G tiles.
+  const uint32_t gsz = gridDim.x;
+  const uint32_t pos = gsz % 8 == 0 ? (blockIdx.x % 8) * (gsz / 8) + blockIdx.x / 8 : blockIdx.x;
+  uint32_t tile = pos;  // linear index, wave-uniform throughout
   __amdgpu_buffer_rsrc_t ra, rb, rna, rnb;
   g_tile_rsrc(g, tile, ra, rb);
 #pragma unroll
@@ -263,7 +287,9 @@ __global__ __launch_bounds__(kGThreads) void fp8_gemm_kernel(const GemmArgs g) {
     // of the 32 x 32 tile (i, j) holds C row i * 32 + lane mod 32, column
     // j * 32 + (r mod 4) + 8 (r / 4) + 4 h (h = lane / 32): register quad q holds four
     // consecutive columns 8 q + 4 h.
-    const int64_t m0 = (int64_t)(tile / g.nbn) * kGBM, n0 = (int64_t)(tile % g.nbn) * kGBN;
+    uint32_t tbm, tbn;
+    g_tile_coords(g, tile, tbm, tbn);
+    const int64_t m0 = (int64_t)tbm * kGBM, n0 = (int64_t)tbn * kGBN;
     if (g.vec_c) {
       // Buffer stores through a resource over C from (m0, n0) on; masked elements use an
       // offset past it (dropped by the hardware).
@@ -392,8 +418,10 @@ extern "C" int fp8_gemm(const uint8_t* A, int a_format, const uint8_t* B, int b_
   g.M = M;
   g.N = N;
   g.K = K;
+  g.nbm = (uint32_t)nbm;
   g.nbn = (uint32_t)nbn;
   g.ntiles = (uint32_t)(nbm * nbn);
+  g.pad2 = 0;
   // vector path: 16-byte stores of 8 bf16 / 4 fp32 columns, tile offsets within 2^31
   const int64_t elt = c_dtype == FP8Q_BF16 ? 2 : 4;
   g.vec_c = N % (16 / elt) == 0 && (uintptr_t)C % 16 == 0 && kGBM * N * elt < ((int64_t)1 << 31);

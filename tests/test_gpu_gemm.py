@@ -197,3 +197,16 @@ def test_gemm_mlp_wi_sampled(orc):
     tol = acc_tol + 2.0 ** -8 * (np.abs(exact) + acc_tol)
     assert (np.abs(sub - exact) <= tol).all(), float(np.max(np.abs(sub - exact) / tol))
     print("gemm wi sampled: max |err| / bound = %.3f" % float(np.max(np.abs(sub - exact) / tol)))
+
+
+@pytest.mark.parametrize("M,N,K", [(4200, 4096, 64), (6000, 2600, 32)])
+def test_gemm_tile_order_full(orc, M, N, K):
+    """Every output of grids with more than 256 tiles (so persistent blocks take a second
+    tile and prefetch it during the first one's epilogue) and a ragged last row of 4 x 8
+    super-tiles: 17 x 16 tiles (column count a multiple of 8: strided super-tile columns)
+    and 24 x 11 tiles (contiguous super-tile columns, a narrower last group)."""
+    g = np.random.Generator(np.random.PCG64(M + N + K))
+    A = random_codes(g, (M, K), E4M3, spread=False)
+    B = random_codes(g, (N, K), E4M3, spread=False)
+    note("gemm tile order M=%d N=%d K=%d" % (M, N, K))
+    check(orc, A, E4M3, B, E4M3, 0.05, 0.02, torch.bfloat16, threads=16)
