@@ -382,7 +382,8 @@ def main():
     # (not in the step) the MLP's two dense layers on the codes the step produced: the
     # activation (8192 x 4096 E4M3) times wi (its 16384 x 4096 codes read K-contiguous),
     # and an (8192 x 16384) E4M3 activation (seeded N(0,1) x 40) times wo (its 4096 x
-    # 16384 codes); per-tensor scale_inv of the step as the operand scales, bf16 out.
+    # 16384 codes); the step's per-tensor scales (the dequantization multipliers) as the
+    # operand scales, bf16 out.
     # torch._scaled_mm (hipBLASLt) on the same operands alongside.
     gemm_out = None
     if not args.no_gemm and w.name == "mlp_4096":
@@ -396,7 +397,7 @@ def main():
             M, K = A.shape
             N = B.shape[0]
             C = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
-            sa, sb = scale_inv[ia:ia + 1], scale_inv[ib:ib + 1]
+            sa, sb = scale[ia:ia + 1], scale[ib:ib + 1]
             g_us = timed_launches(lambda i: d.fp8_gemm(A, 0, B, 0, sa, sb, C))
             flops = 2.0 * M * N * K
             rec = {"layer": name, "M": M, "N": N, "K": K, "events_median_us": round(g_us, 3),
