@@ -210,3 +210,33 @@ def test_gemm_tile_order_full(orc, M, N, K):
     B = random_codes(g, (N, K), E4M3, spread=False)
     note("gemm tile order M=%d N=%d K=%d" % (M, N, K))
     check(orc, A, E4M3, B, E4M3, 0.05, 0.02, torch.bfloat16, threads=16)
+
+
+def test_gemm_inf_operands(orc):
+    """E5M2 +-inf codes (M3): inf times a finite nonzero value gives a signed inf, inf
+    times zero and inf - inf give NaN, rows and columns without an inf are unaffected."""
+    g = np.random.Generator(np.random.PCG64(990))
+    M, N, K = 64, 48, 128
+    A = random_codes(g, (M, K), E5M2, spread=False)
+    B = random_codes(g, (N, K), E5M2, spread=False)
+    A[A == 0] = 0x3C  # no accidental zeros: placed zeros below decide inf * 0
+    B[B == 0] = 0x3C
+    A[2, 5] = 0x7C                      # +inf against column 5 of every B row
+    A[7, 40] = 0xFC                     # -inf
+    A[11, 3] = 0x7C
+    A[11, 90] = 0xFC                    # +inf and -inf in one row: NaN where the products differ in sign
+    A[20, 64] = 0x7C
+    B[4, 64] = 0x00                     # inf * 0 -> NaN at C[20, 4]
+    B[9, 70] = 0x7C                     # column 9 of C: +inf against row 30's entry
+    A[30, 70] = 0x80                    # -0 * inf -> NaN at C[30, 9]
+    note("gemm inf operands")
+    got = run_gemm(A, E5M2, B, E5M2, 0.5, 0.25, torch.float32)
+    exact, cabs, cg = orc.fp8_gemm(A, E5M2, B, E5M2, 0.5, 0.25)
+    nan = np.isnan(exact)
+    inf = np.isinf(exact)
+    assert nan.sum() > 0 and inf.sum() > 0
+    assert (np.isnan(got) == nan).all(), np.argwhere(np.isnan(got) != nan)[:8]
+    assert (got[inf] == exact[inf]).all(), np.argwhere(inf & (got != exact))[:8]
+    fin = ~(nan | inf)
+    tol = acc_bound(K, cabs, cg) + 2.0 ** -23 * np.abs(exact) + 2.0 ** -149
+    assert (np.abs(got[fin] - exact[fin]) <= tol[fin]).all()
