@@ -175,6 +175,9 @@ def main():
     first_codes = [x.cpu().numpy() for x in dsts]
     first_amax = amax.cpu().numpy().copy()
     update()
+    torch.cuda.synchronize()
+    first_meta = {"hist": hist.cpu().numpy().copy(), "scale": scale.cpu().numpy().copy(),
+                  "scale_inv": scale_inv.cpu().numpy().copy(), "amax": amax.cpu().numpy().copy()}
 
     for _ in range(args.warmup):
         quantize()
@@ -282,6 +285,39 @@ def main():
     log("update 1152x%d: graph-replay %s us/call, events warm %.2f us, cold %.2f us, host "
         "wall %.2f us/call" % (uH, "%.2f" % graph_us if graph_us else "n/a", warm_us, cold_us,
                                wall_us))
+    # (e) context only, never in the library: the same update as a sequence of small torch
+    #     ops per module call (roll, insert, max, divide, guard, reciprocal, reset: ~10
+    #     launches for the module's 3 tensors), the per-call pattern the fused kernel
+    #     replaces; 384 module calls, host wall time for all of them
+    fmax = torch.where(u_fmt == 0, torch.tensor(448.0, device=dev),
+                       torch.tensor(57344.0, device=dev))
+    u_hist_t = u_hist.clone()
+    u_amax_t = u_amax.clone()
+    u_scale_t = u_scale.clone()
+
+    def update_torch_ops():
+        for m in range(un // 3):
+            cs = slice(3 * m, 3 * m + 3)
+            h = torch.roll(u_hist_t[:, cs], 1, 0)
+            h[0] = u_amax_t[cs]
+            u_hist_t[:, cs] = h
+            sel = h.max(0).values
+            sc = sel / fmax[cs]
+            ok = torch.isfinite(sc) & (sc > 0)
+            u_scale_t[cs] = torch.where(ok, sc, u_scale_t[cs])
+            u_sinv[cs] = 1.0 / u_scale_t[cs]
+            u_amax_t[cs] = 0.0
+
+    update_torch_ops()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(3):
+        update_torch_ops()
+    torch.cuda.synchronize()
+    torch_ops_us = (time.perf_counter() - t0) * 1e6 / 3
+    del u_hist_t, u_amax_t, u_scale_t
+    log("update 1152x%d as small torch ops per module call: %.0f us per update" % (
+        uH, torch_ops_us))
 
     # ------------------------------------------------------------ dequantize (not in the step)
     # codes of the largest tensor of the step back to bf16 with its scale
@@ -460,6 +496,7 @@ def main():
                             "events_warm_us": round(warm_us, 3),
                             "events_cold_us": round(cold_us, 3),
                             "host_wall_us_per_call": round(wall_us, 3),
+                            "torch_ops_per_module_us_per_update": round(torch_ops_us, 1),
                             "alg_bytes": alg_bytes_update(un, uH),
                             "step_update_and_gap_events_us": round(1e3 * float(np.mean(u_ms)),
                                                                    3)},
@@ -487,18 +524,21 @@ def main():
                 c, amax_o[i] = orc.quantize_amax(t.data, fmts[i], float(w.first_scale[i]),
                                                  threads=threads)
                 codes_o.append(c)
-            orc.amax_and_scale_update(amax_o, np.zeros((w.history_len, n), np.float32),
-                                      np.asarray(w.first_scale, np.float32),
-                                      np.array(fmts, np.uint8), reset_amax=True)
-            return codes_o, amax_o
+            meta = orc.amax_and_scale_update(amax_o, np.zeros((w.history_len, n), np.float32),
+                                             np.asarray(w.first_scale, np.float32),
+                                             np.array(fmts, np.uint8), reset_amax=True)
+            return codes_o, amax_o, meta
 
-        # the first step is compared with the GPU's; whole steps are repeated until at
-        # least 10 s of oracle work have been timed (at most 100 steps)
+        # the first step is compared with the GPU's (codes, amax, and after the update
+        # the history, scale, scale_inv and reset amax, all bit for bit); whole steps are
+        # repeated until at least 10 s of oracle work have been timed (at most 100 steps)
         t0 = time.perf_counter()
-        codes_o, o_amax = oracle_step()
+        codes_o, o_amax, o_meta = oracle_step()
         reps = 1
         same = all(np.array_equal(c.reshape(-1), first_codes[i]) for i, c in enumerate(codes_o))
         same &= bool((o_amax.view(np.uint32) == first_amax.view(np.uint32)).all())
+        same &= all(np.array_equal(o_meta[k].view(np.uint32), first_meta[k].view(np.uint32))
+                    for k in ("hist", "scale", "scale_inv", "amax"))
         del codes_o
         while time.perf_counter() - t0 < 10.0 and reps < 100:
             oracle_step()
@@ -510,6 +550,16 @@ def main():
                                          "step's inputs and prior scales), %d threads over "
                                          "contiguous chunks, %.1f s" % (
                                              reps, w.name, w.numel, threads, dt)}
+        # the same oracle on one thread, on the activation tensor alone (33.5 M elements)
+        t1 = time.perf_counter()
+        orc.quantize_amax(w.tensors[0].data, fmts[0], float(w.first_scale[0]), threads=1)
+        dt1 = time.perf_counter() - t1
+        e1 = int(w.tensors[0].data.size)
+        out["cpu_baseline_one_thread"] = {
+            "value": round(3 * e1 / dt1 / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "ns_per_element": round(dt1 * 1e9 / e1, 3),
+            "sample": "quantize+amax of %s (%d elements), one thread, %.2f s" % (
+                w.tensors[0].name, e1, dt1)}
         out["parity_first_step"] = "bit-exact" if same else "MISMATCH"
     print(json.dumps(out), flush=True)
 
