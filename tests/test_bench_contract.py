@@ -1,0 +1,43 @@
+"""bench.py's contract on the CPU: one GPU only (N > 1 exits with a message before touching
+a device), and the algorithmic byte counts the roofline divides by."""
+import importlib.util
+import os
+import subprocess
+import sys
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _bench():
+    spec = importlib.util.spec_from_file_location("bench_mod", os.path.join(ROOT, "bench.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod
+
+
+def test_more_than_one_gpu_exits_with_message():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr and r.stdout == ""
+
+
+def test_algorithmic_bytes():
+    b = _bench()
+
+    class T:
+        def __init__(self, shape):
+            self.data = np.zeros(shape, np.uint16)  # bf16 bits
+
+    class W:
+        tensors = [T((2048, 4, 4096)), T((4096, 16384)), T((16384, 4096))]
+
+    # 2 B read + 1 B written per bf16 element, plus 12 B per tensor (scale read, amax
+    # read and write): 167,772,160 elements -> 503,316,480 + 36
+    assert b.alg_bytes_quantize(W) == 3 * 167772160 + 36
+    # history read + in-place write, amax read + reset write, scale read + write,
+    # scale_inv write, one format byte per tensor
+    n, H = 1152, 1024
+    assert b.alg_bytes_update(n, H) == 2 * H * n * 4 + 8 * n + 8 * n + 4 * n + n == 9461376
