@@ -313,6 +313,16 @@ def pin_amax(o):
     y[17] = np.nan
     _, a = o.quantize_amax(y, E4M3, 1.0)
     assert np.isnan(a)
+    # the NaN payload (R5: the largest sign-cleared bit pattern): among NaNs of both signs
+    # the largest payload wins, and any NaN beats inf; quiet NaNs, so no conversion on
+    # the way can change them; bf16 sources count by their binary32 upcast
+    zb = np.concatenate([np.array([1.0, -np.inf, 3.0, 0.0], np.float32).view(np.uint32),
+                         np.array([0xFFE12345, 0x7FC00001, 0xFFC00100], np.uint32)])
+    _, a = o.quantize_amax(zb.view(np.float32), E4M3, 1.0)
+    assert np.float32(a).view(np.uint32) == (zb & 0x7FFFFFFF).max() == 0x7FE12345
+    hb = np.array([0x3F80, 0xFFE1, 0x7FC3, 0xFF80], np.uint16)  # 1, -NaN, +NaN, -inf
+    _, a = o.quantize_amax(hb, E5M2, 1.0)
+    assert np.float32(a).view(np.uint32) == 0x7FE10000
 
 
 def pin_saturation_count(o):

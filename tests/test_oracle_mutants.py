@@ -85,6 +85,8 @@ MUTANTS = [
      "if (a.special == 2 || b.special == 2) { continue; }"),
     ("gemm_group_of_four", "if (k % 8 == 0) { gsum += gmax; gmax = 0.0; }",
      "if (k % 4 == 0) { gsum += gmax; gmax = 0.0; }"),
+    ("amax_nan_canonical", "  *amax = u2f(acc);\n}\n\n/* Amax only",
+     "  *amax = isnan(u2f(acc)) ? NAN : u2f(acc);\n}\n\n/* Amax only"),
     ("dequant_nan_unsigned", "uint32_t nan_bits = 0x7FC00000u | ((uint32_t)(src[i] & 0x80) << 24);",
      "uint32_t nan_bits = 0x7FC00000u;"),
 ]
