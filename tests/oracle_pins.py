@@ -258,6 +258,50 @@ def pin_quantize_exact_quotient(o):
             assert got == want, (fmt, x, s, hex(got), hex(want))
 
 
+def pin_quantize_extreme_scales(o):
+    """R12: a scale outside the normal range, negative, zero, infinite or NaN still gives
+    the IEEE quotient x / scale, then R2-R4.  Finite nonzero scales (subnormal, the
+    largest finite, negative) against the exact rational RN32 of x / s (overflow to inf,
+    underflow to a zero signed by sign(x) xor sign(s)); zero, infinite and NaN scales
+    against IEEE's special cases written out: x/0 = inf (0/0 NaN), x/inf = 0 (inf/inf
+    NaN), NaN anything = NaN; a NaN quotient encodes as 0x7F with x's sign (R4)."""
+    xb = np.array([0x0000, 0x8000, 0x0001, 0x8001, 0x007F, 0x0080, 0x3E80, 0x3F80, 0xBF80,
+                   0x43E0, 0xC2F6, 0x4780, 0x7F7F, 0xFF7F, 0x7F80, 0xFF80, 0x7FC0, 0xFFC0],
+                  np.uint16)
+    xs = [float(v) for v in bf16_to_f32(xb)]
+    f32 = lambda v: float(np.float32(v))
+    finite = [f32(2.0 ** -149), f32(3 * 2.0 ** -149), f32(2.0 ** -130), f32(2.0 ** -126),
+              f32(1e-30), 1.5, -1.5, f32(-(2.0 ** -140)), f32(1e20), f32(-3e30),
+              f32(1.5 * 2.0 ** 127), f32(3.4028234663852886e38), f32(-3.4028234663852886e38)]
+    special = [0.0, -0.0, float("inf"), float("-inf"), float("nan")]
+    for fmt in (E4M3, E5M2):
+        mx = o.fp8_max(fmt)
+        for x in xs:
+            sx = bool(np.signbit(x))
+            for sc in finite + special:
+                ss = bool(np.signbit(sc))
+                if np.isnan(x) or np.isnan(sc):
+                    q = float("nan")
+                elif sc == 0.0:
+                    q = float("nan") if x == 0.0 else (-1.0 if sx != ss else 1.0) * float("inf")
+                elif np.isinf(sc):
+                    q = float("nan") if np.isinf(x) else (-0.0 if sx != ss else 0.0)
+                elif np.isinf(x):
+                    q = (-1.0 if sx != ss else 1.0) * float("inf")
+                else:
+                    q = None                               # finite / finite: exact rational
+                if q is None:
+                    want = _exact_quantize(o, fmt, x, sc)
+                elif np.isnan(q):
+                    want = 0x7F | (0x80 if sx else 0x00)
+                elif q == 0.0:
+                    want = 0x80 if np.signbit(q) else 0x00
+                else:
+                    want = int(brute_encode(fmt, np.array([max(min(q, mx), -mx)]))[0])
+                got = o.quantize_element(fmt, x, sc)
+                assert got == want, (fmt, x, sc, hex(got), hex(want))
+
+
 def pin_quantize_f32_matches_encode_at_scale_one(o):
     g = np.random.Generator(np.random.PCG64(3))
     v = (np.exp2(g.uniform(-30, 20, 3000)) * np.where(g.random(3000) < .5, -1, 1)).astype(

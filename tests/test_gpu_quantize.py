@@ -23,8 +23,8 @@ def scales_grid():
 
 
 # scales outside the fast window or degenerate: IEEE path, NaN, inf, sign flips
-ODD_SCALES = [2.0 ** -90, 2.0 ** -126, 1e-40, 2.0 ** 126, 3.0e38, 0.0, -0.0, -1.5,
-              float("inf"), float("nan")]
+ODD_SCALES = [2.0 ** -90, 2.0 ** -126, 1e-40, 2.0 ** -149, 2.0 ** 126, 3.0e38, -3.0e30, 0.0,
+              -0.0, -1.5, float("inf"), float("-inf"), float("nan")]
 
 
 def test_worked_tensor(orc):
