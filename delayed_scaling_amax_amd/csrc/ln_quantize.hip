@@ -11,7 +11,7 @@
 // the plain quantize does ("User Guide on Native XLA-FP8", section "JAX").
 //
 // Design (gfx950; HBM-bound at 3 bytes/element plus 8 bytes per row of statistics):
-//  * One wavefront per row, persistent grid: the row (H <= 8192 bf16 = 16 KB) is
+//  * One wavefront per row, persistent grid: the row (H <= 16384 bf16 = 32 KB) is
 //    loaded as 16-byte units into registers -- the wavefront's next row is loaded
 //    while the current one is reduced and written -- so every reduction is a
 //    wavefront butterfly, with no LDS round trip and no block barrier per row.
@@ -36,7 +36,7 @@
 namespace fp8q {
 
 constexpr int kLBlock = 256;       // 4 wavefronts, one row each at a time
-constexpr int kLMaxH = 8192;       // 64 lanes x 16 units x 8 elements
+constexpr int kLMaxH = 16384;      // 64 lanes x 32 units x 8 elements
 #ifndef FP8Q_LN_BLOCKS_PER_CU
 #define FP8Q_LN_BLOCKS_PER_CU 4
 #endif
@@ -87,15 +87,26 @@ __device__ __forceinline__ void ln_load_row(uint4 (&w)[kV], __amdgpu_buffer_rsrc
   }
 }
 
-// Pairwise (tree) sum of N values in place; N a power of two.
+constexpr int ln_pow2_ceil(int n) { return n <= 1 ? 1 : 2 * ln_pow2_ceil((n + 1) / 2); }
+
+// Pairwise (tree) sum of N values, depth ceil(log2 N): a count that is not a power of two
+// is padded with exact zeros.
 template <int N>
 __device__ __forceinline__ float tree_sum(float (&v)[N]) {
+  constexpr int P = ln_pow2_ceil(N);
+  if constexpr (P == N) {
 #pragma unroll
-  for (int w = N / 2; w >= 1; w /= 2) {
+    for (int w = N / 2; w >= 1; w /= 2) {
 #pragma unroll
-    for (int i = 0; i < w; ++i) v[i] = v[i] + v[i + w];
+      for (int i = 0; i < w; ++i) v[i] = v[i] + v[i + w];
+    }
+    return v[0];
+  } else {
+    float t[P];
+#pragma unroll
+    for (int i = 0; i < P; ++i) t[i] = i < N ? v[i] : 0.0f;
+    return tree_sum(t);
   }
-  return v[0];
 }
 
 // Sum over the 64 lanes of a wavefront as a pairwise tree on the DPP network (no LDS
@@ -367,6 +378,11 @@ static int ln_launch(const LnArgs& a, hipStream_t stream) {
   static std::atomic<int> fit{0};
   int per_cu = fit.load(std::memory_order_relaxed);
   if (per_cu <= 0) {
+    // gamma/beta staging beyond 64 KB (24 and 32 units per lane: 96 and 128 KB)
+    if (smem > 65536 &&
+        hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem) !=
+            hipSuccess)
+      return FP8Q_EHIP;
     int occ = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, fn, kLBlock, smem) != hipSuccess)
       return FP8Q_EHIP;
@@ -387,14 +403,18 @@ static int ln_launch(const LnArgs& a, hipStream_t stream) {
 template <int kFmt>
 static int ln_dispatch(const LnArgs& a, hipStream_t stream) {
   const int need = (a.nunits + 63) / 64;  // units per lane
-  const int kv = need <= 1 ? 1 : need <= 2 ? 2 : need <= 4 ? 4 : need <= 8 ? 8 : 16;
+  const int kv = need <= 1 ? 1 : need <= 2 ? 2 : need <= 4 ? 4 : need <= 8 ? 8 : need <= 16 ? 16
+                 : need <= 24 ? 24 : 32;
   const bool masked = a.nunits != 64 * kv;
   switch (kv) {
     case 1: return masked ? ln_launch<kFmt, 1, true>(a, stream) : ln_launch<kFmt, 1, false>(a, stream);
     case 2: return masked ? ln_launch<kFmt, 2, true>(a, stream) : ln_launch<kFmt, 2, false>(a, stream);
     case 4: return masked ? ln_launch<kFmt, 4, true>(a, stream) : ln_launch<kFmt, 4, false>(a, stream);
     case 8: return masked ? ln_launch<kFmt, 8, true>(a, stream) : ln_launch<kFmt, 8, false>(a, stream);
-    default: return masked ? ln_launch<kFmt, 16, true>(a, stream) : ln_launch<kFmt, 16, false>(a, stream);
+    case 16: return masked ? ln_launch<kFmt, 16, true>(a, stream) : ln_launch<kFmt, 16, false>(a, stream);
+    // hidden 8200 .. 12288 (12288: the hidden-12288 MLP) and 12296 .. 16384
+    case 24: return masked ? ln_launch<kFmt, 24, true>(a, stream) : ln_launch<kFmt, 24, false>(a, stream);
+    default: return masked ? ln_launch<kFmt, 32, true>(a, stream) : ln_launch<kFmt, 32, false>(a, stream);
   }
 }
 

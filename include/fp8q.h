@@ -168,7 +168,7 @@ int fp8_gelu_quantize_amax(const void* src, int src_dtype, uint8_t* dst, int64_t
  *   x_dtype    FP8Q_BF16 (FP8Q_F32 returns FP8Q_EUNSUPPORTED).
  *   gamma,beta device, hidden binary32 each, or NULL for 1 / 0.
  *   eps        finite, >= 0 (the layer's default is 1e-6).
- *   rows       >= 0.   hidden: a multiple of 8 in [8, 8192] (else FP8Q_EUNSUPPORTED);
+ *   rows       >= 0.   hidden: a multiple of 8 in [8, 16384] (else FP8Q_EUNSUPPORTED);
  *              rows == 0 or hidden == 0 enqueues nothing.
  *   dst        device, rows x hidden codes, 8-byte aligned (else FP8Q_EUNSUPPORTED).
  *   format, scale, amax as fp8_quantize_amax.

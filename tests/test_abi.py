@@ -95,7 +95,7 @@ def test_layernorm_quantize_validation():
     assert _ln(d, x=None) == d.EINVAL and _ln(d, dst=None) == d.EINVAL
     assert _ln(d, dt=d.F32) == d.EUNSUPPORTED
     assert _ln(d, H=12) == d.EUNSUPPORTED          # not a multiple of 8
-    assert _ln(d, H=8200) == d.EUNSUPPORTED        # longer rows than the kernel holds
+    assert _ln(d, H=16392) == d.EUNSUPPORTED       # longer rows than the kernel holds
     assert _ln(d, x=BAD + 8) == d.EUNSUPPORTED     # x not 16-byte aligned
     assert _ln(d, dst=BAD + 4) == d.EUNSUPPORTED   # dst not 8-byte aligned
     assert _ln(d, rows=2 ** 62, H=8) == d.EINVAL   # rows * hidden overflows

@@ -106,10 +106,11 @@ def affine(seed, H):
             (0.3 * g.standard_normal(H)).astype(np.float32))
 
 
-@pytest.mark.parametrize("H", [8, 64, 512, 520, 768, 1000, 2048, 4096, 8192])
+@pytest.mark.parametrize("H", [8, 64, 512, 520, 768, 1000, 2048, 4096, 8192, 10000, 12288,
+                               12296, 16384])
 def test_ln_row_lengths(orc, H):
-    """Every kernel instance (units per lane 1-16, full and masked) over several rows,
-    affine gamma/beta, both formats."""
+    """Every kernel instance (units per lane 1-32, full and masked) over several rows,
+    affine gamma/beta, both formats; 12288 is the hidden size of the hidden-12288 MLP."""
     for rows, fmt, scale in ((1, E4M3, 0.02), (37, E5M2, 1e-3), (131, E4M3, 0.013)):
         x = ln_input(700 + H + rows, rows, H, offset=0.3)
         gamma, beta = affine(800 + H, H)
