@@ -36,6 +36,10 @@
 namespace fp8q {
 
 constexpr int kLBlock = 256;       // 4 wavefronts, one row each at a time
+// 24 units per lane: 8 wavefronts share one block's 96 KB of gamma/beta, two per SIMD
+// (232-240 registers each); 32 units need more than 256 registers, so one per SIMD.
+template <int kV>
+constexpr int ln_block() { return kV == 24 ? 512 : kLBlock; }
 constexpr int kLMaxH = 16384;      // 64 lanes x 32 units x 8 elements
 #ifndef FP8Q_LN_BLOCKS_PER_CU
 #define FP8Q_LN_BLOCKS_PER_CU 4
@@ -282,8 +286,9 @@ __device__ __forceinline__ void ln_row(uint4 (&w)[kV], const LnArgs& a, int64_t 
 }
 
 template <int kFmt, int kV, bool kMasked>
-__global__ __launch_bounds__(kLBlock)
+__global__ __launch_bounds__(ln_block<kV>())
 void ln_quantize_kernel(const LnArgs a) {
+  constexpr int kBlk = ln_block<kV>();
   // gamma then beta, each 512 kV floats, zero-padded; 16-byte aligned for the b128 reads
   extern __shared__ __attribute__((aligned(16))) float lds[];
   __shared__ uint32_t block_amax;
@@ -292,8 +297,8 @@ void ln_quantize_kernel(const LnArgs a) {
   float* lb = lds + kPad;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: SGPR
-  const int64_t nwaves = (int64_t)gridDim.x * (kLBlock / 64);
-  int64_t row = (int64_t)blockIdx.x * (kLBlock / 64) + wave;
+  const int64_t nwaves = (int64_t)gridDim.x * (kBlk / 64);
+  int64_t row = (int64_t)blockIdx.x * (kBlk / 64) + wave;
   const uint32_t row_bytes = (uint32_t)a.H * 2u;
 #if FP8Q_LN_PREFETCH
   // the first row's loads go out before the staging below, which they overlap
@@ -302,12 +307,12 @@ void ln_quantize_kernel(const LnArgs a) {
 #endif
   // stage gamma/beta: 16-byte loads, all issued before any is used
   if (a.vec_affine) {
-    float4 gs[kPad / 4 / kLBlock > 0 ? kPad / 4 / kLBlock : 1];
-    float4 bs[kPad / 4 / kLBlock > 0 ? kPad / 4 / kLBlock : 1];
-    constexpr int kIt = (kPad / 4 + kLBlock - 1) / kLBlock;
+    float4 gs[kPad / 4 / kBlk > 0 ? kPad / 4 / kBlk : 1];
+    float4 bs[kPad / 4 / kBlk > 0 ? kPad / 4 / kBlk : 1];
+    constexpr int kIt = (kPad / 4 + kBlk - 1) / kBlk;
 #pragma unroll
     for (int it = 0; it < kIt; ++it) {
-      const int i4 = threadIdx.x + it * kLBlock;  // float4 index
+      const int i4 = threadIdx.x + it * kBlk;  // float4 index
       const bool in = 4 * i4 < a.H;
       gs[it] = in && a.gamma ? ((const float4*)a.gamma)[i4] : make_float4(1.f, 1.f, 1.f, 1.f);
       bs[it] = in && a.beta ? ((const float4*)a.beta)[i4] : make_float4(0.f, 0.f, 0.f, 0.f);
@@ -315,14 +320,14 @@ void ln_quantize_kernel(const LnArgs a) {
     }
 #pragma unroll
     for (int it = 0; it < kIt; ++it) {
-      const int i4 = threadIdx.x + it * kLBlock;
+      const int i4 = threadIdx.x + it * kBlk;
       if (4 * i4 < kPad) {
         ((float4*)lg)[i4] = gs[it];
         ((float4*)lb)[i4] = bs[it];
       }
     }
   } else {
-    for (int i = threadIdx.x; i < kPad; i += kLBlock) {
+    for (int i = threadIdx.x; i < kPad; i += kBlk) {
       const bool in = i < a.H;
       lg[i] = in ? (a.gamma ? a.gamma[i] : 1.0f) : 0.0f;
       lb[i] = in ? (a.beta ? a.beta[i] : 0.0f) : 0.0f;
@@ -373,6 +378,7 @@ void ln_quantize_kernel(const LnArgs a) {
 // ---------------------------------------------------------------- host side
 template <int kFmt, int kV, bool kMasked>
 static int ln_launch(const LnArgs& a, hipStream_t stream) {
+  constexpr int kBlk = ln_block<kV>();
   const void* fn = (const void*)ln_quantize_kernel<kFmt, kV, kMasked>;
   const size_t smem = (size_t)2 * 512 * kV * sizeof(float);
   static std::atomic<int> fit{0};
@@ -384,7 +390,7 @@ static int ln_launch(const LnArgs& a, hipStream_t stream) {
             hipSuccess)
       return FP8Q_EHIP;
     int occ = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, fn, kLBlock, smem) != hipSuccess)
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, fn, kBlk, smem) != hipSuccess)
       return FP8Q_EHIP;
     per_cu = occ < kLBlocksPerCU ? (occ > 0 ? occ : 1) : kLBlocksPerCU;
     fit.store(per_cu, std::memory_order_relaxed);
@@ -392,12 +398,12 @@ static int ln_launch(const LnArgs& a, hipStream_t stream) {
   int cus = 0;
   const int st = current_device_cus(&cus);
   if (st != FP8Q_OK) return st;
-  int64_t blocks = (a.rows + (kLBlock / 64) - 1) / (kLBlock / 64);
+  int64_t blocks = (a.rows + (kBlk / 64) - 1) / (kBlk / 64);
   const int64_t cap = (int64_t)cus * per_cu;
   if (blocks > cap) blocks = cap;
   void* args[] = {(void*)&a};
   return launch_status(
-      hipLaunchKernel(fn, dim3((unsigned)blocks), dim3(kLBlock), args, smem, stream));
+      hipLaunchKernel(fn, dim3((unsigned)blocks), dim3(kBlk), args, smem, stream));
 }
 
 template <int kFmt>
