@@ -6,6 +6,8 @@ the current HIP stream.  Functions carry the C names:
 
   fp8_quantize_amax(src, dst, scale, amax, format)          one tensor, fused amax
   fp8_multi_quantize_amax([(src, dst, scale, amax, format), ...])   one launch
+  fp8_multi_quantize_amax_timed(entries, start_event, stop_event)  the same, with
+                            torch.cuda.Events set to the kernel's own start/stop
   fp8_gelu_quantize_amax(src, dst, scale, amax, format)     gelu(bf16 src), quantized
   fp8_layernorm_quantize_amax(x, dst, scale, amax, format, gamma=None, beta=None,
                               eps=1e-6, mean=None, rstd=None)  LayerNorm(x), quantized
@@ -13,6 +15,8 @@ the current HIP stream.  Functions carry the C names:
   fp8_gemm(A, a_format, B, b_format, a_scale, b_scale, C)   C = sa sb A @ B.T (FP8)
   fp8_amax_and_scale_update(amax, amax_history, scale, scale_inv, formats,
                             algo=AMAX_MAX, margin=0, reset_amax=False)
+  fp8_quantize_amax_and_update(entries, amax, amax_history, scale, scale_inv, formats,
+                               workspace, ...)   both of the above, one launch
   fp8_status_string(status)
 
 `scale` / `amax` are 1-element float32 device tensors (or 1-element views into a
@@ -56,17 +60,22 @@ def _load():
     vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
     lib.fp8_quantize_amax.argtypes = [vp, i32, vp, i64, i32, vp, vp, vp]
     lib.fp8_multi_quantize_amax.argtypes = [ctypes.POINTER(fp8q_tensor), i32, vp]
+    lib.fp8_multi_quantize_amax_timed.argtypes = [ctypes.POINTER(fp8q_tensor), i32, vp, vp, vp]
     lib.fp8_gelu_quantize_amax.argtypes = [vp, i32, vp, i64, i32, vp, vp, vp]
     lib.fp8_layernorm_quantize_amax.argtypes = [vp, i32, vp, vp, ctypes.c_float, i64, i64, vp,
                                                 i32, vp, vp, vp, vp, vp]
     lib.fp8_dequantize.argtypes = [vp, i32, vp, i32, i64, vp, vp]
     lib.fp8_gemm.argtypes = [vp, i32, vp, i32, i64, i64, i64, vp, vp, vp, i32, vp]
     lib.fp8_amax_and_scale_update.argtypes = [vp, vp, vp, vp, vp, i64, i64, i32, i32, i32, vp]
+    lib.fp8_quantize_amax_and_update.argtypes = [ctypes.POINTER(fp8q_tensor), i32, vp, vp, vp,
+                                                 vp, vp, i64, i64, i32, i32, i32, vp, vp, vp,
+                                                 vp]
     lib.fp8_status_string.argtypes = [i32]
     lib.fp8_status_string.restype = ctypes.c_char_p
-    for f in ("fp8_quantize_amax", "fp8_multi_quantize_amax", "fp8_gelu_quantize_amax",
+    for f in ("fp8_quantize_amax", "fp8_multi_quantize_amax", "fp8_multi_quantize_amax_timed",
+              "fp8_gelu_quantize_amax",
               "fp8_layernorm_quantize_amax", "fp8_gemm", "fp8_dequantize", "fp8_amax_and_scale_update",
-              "fp8_gemm"):
+              "fp8_quantize_amax_and_update"):
         getattr(lib, f).restype = i32
     return lib
 
@@ -167,11 +176,7 @@ def fp8_gemm(A: torch.Tensor, a_format: int, B: torch.Tensor, b_format: int,
             _DTYPE.get(C.dtype, -1), _stream(A.device)))
 
 
-def fp8_multi_quantize_amax(entries) -> None:
-    """entries: sequence of (src, dst, scale, amax, format)."""
-    entries = list(entries)
-    if not entries:
-        return
+def _entry_table(entries):
     arr = (fp8q_tensor * len(entries))()
     for i, (src, dst, scale, amax, fmt) in enumerate(entries):
         if dst.dtype != torch.uint8 or dst.numel() != src.numel():
@@ -179,10 +184,43 @@ def fp8_multi_quantize_amax(entries) -> None:
         arr[i] = fp8q_tensor(_dense(src, "src"), _dense(dst, "dst"), src.numel(),
                              _DTYPE.get(src.dtype, -1), int(fmt), _one_float(scale, "scale"),
                              _one_float(amax, "amax"))
+    return arr
+
+
+def fp8_multi_quantize_amax(entries) -> None:
+    """entries: sequence of (src, dst, scale, amax, format)."""
+    entries = list(entries)
+    if not entries:
+        return
+    arr = _entry_table(entries)
     dev = entries[0][0].device
     with torch.cuda.device(dev):
         _check("fp8_multi_quantize_amax",
                lib.fp8_multi_quantize_amax(arr, len(entries), _stream(dev)))
+
+
+def _event_handle(ev) -> int | None:
+    """hipEvent_t of a torch.cuda.Event (created with enable_timing=True), or None."""
+    if ev is None:
+        return None
+    if ev.cuda_event == 0:  # torch creates the event at its first record
+        ev.record()
+    return int(ev.cuda_event)
+
+
+def fp8_multi_quantize_amax_timed(entries, start_event, stop_event) -> None:
+    """fp8_multi_quantize_amax whose kernel launches set two torch.cuda.Event objects
+    (enable_timing=True; either may be None) to the kernels' own start and stop times:
+    start_event.elapsed_time(stop_event) is the kernels' duration without the dispatch
+    latency that events recorded on the stream around the call also span."""
+    entries = list(entries)
+    dev = entries[0][0].device if entries else torch.device("cuda", torch.cuda.current_device())
+    arr = _entry_table(entries)
+    with torch.cuda.device(dev):
+        _check("fp8_multi_quantize_amax_timed",
+               lib.fp8_multi_quantize_amax_timed(arr, len(entries), _stream(dev),
+                                                 _event_handle(start_event),
+                                                 _event_handle(stop_event)))
 
 
 def fp8_dequantize(src: torch.Tensor, dst: torch.Tensor, scale: torch.Tensor,
@@ -195,10 +233,7 @@ def fp8_dequantize(src: torch.Tensor, dst: torch.Tensor, scale: torch.Tensor,
             src.numel(), _one_float(scale, "scale"), _stream(src.device)))
 
 
-def fp8_amax_and_scale_update(amax: torch.Tensor, amax_history: torch.Tensor,
-                              scale: torch.Tensor, scale_inv: torch.Tensor,
-                              formats: torch.Tensor, algo: int = AMAX_MAX, margin: int = 0,
-                              reset_amax: bool = False) -> None:
+def _update_shape(amax, amax_history, scale, scale_inv, formats):
     if amax_history.dim() != 2:
         raise ValueError("amax_history must be [history_len, n]")
     H, n = amax_history.shape
@@ -209,6 +244,14 @@ def fp8_amax_and_scale_update(amax: torch.Tensor, amax_history: torch.Tensor,
         raise ValueError("amax_history must be float32")
     if formats.dtype != torch.uint8 or formats.numel() != n:
         raise ValueError("formats must be uint8 with n elements")
+    return H, n
+
+
+def fp8_amax_and_scale_update(amax: torch.Tensor, amax_history: torch.Tensor,
+                              scale: torch.Tensor, scale_inv: torch.Tensor,
+                              formats: torch.Tensor, algo: int = AMAX_MAX, margin: int = 0,
+                              reset_amax: bool = False) -> None:
+    H, n = _update_shape(amax, amax_history, scale, scale_inv, formats)
     with torch.cuda.device(amax.device):
         _check("fp8_amax_and_scale_update", lib.fp8_amax_and_scale_update(
             _dense(amax, "amax"), _dense(amax_history, "amax_history"), _dense(scale, "scale"),
@@ -216,7 +259,32 @@ def fp8_amax_and_scale_update(amax: torch.Tensor, amax_history: torch.Tensor,
             int(margin), int(bool(reset_amax)), _stream(amax.device)))
 
 
-__all__ = ["fp8_quantize_amax", "fp8_multi_quantize_amax", "fp8_gelu_quantize_amax",
+
+def fp8_quantize_amax_and_update(entries, amax: torch.Tensor, amax_history: torch.Tensor,
+                                 scale: torch.Tensor, scale_inv: torch.Tensor,
+                                 formats: torch.Tensor, workspace: torch.Tensor,
+                                 algo: int = AMAX_MAX, margin: int = 0,
+                                 reset_amax: bool = False, start_event=None,
+                                 stop_event=None) -> None:
+    """One delayed-scaling step: fp8_multi_quantize_amax(entries) then
+    fp8_amax_and_scale_update(...), in one kernel launch when it fits.  workspace: a
+    1-element int32/uint32 device tensor holding 0 (every call leaves it 0)."""
+    entries = list(entries)
+    H, n = _update_shape(amax, amax_history, scale, scale_inv, formats)
+    if workspace.numel() != 1 or workspace.element_size() != 4:
+        raise ValueError("workspace must be one 4-byte element")
+    arr = _entry_table(entries)
+    with torch.cuda.device(amax.device):
+        _check("fp8_quantize_amax_and_update", lib.fp8_quantize_amax_and_update(
+            arr, len(entries), _dense(amax, "amax"), _dense(amax_history, "amax_history"),
+            _dense(scale, "scale"), _dense(scale_inv, "scale_inv"), _dense(formats, "formats"),
+            n, H, int(algo), int(margin), int(bool(reset_amax)), _dense(workspace, "workspace"),
+            _stream(amax.device), _event_handle(start_event), _event_handle(stop_event)))
+
+
+__all__ = ["fp8_quantize_amax", "fp8_multi_quantize_amax", "fp8_multi_quantize_amax_timed",
+           "fp8_quantize_amax_and_update",
+           "fp8_gelu_quantize_amax",
            "fp8_layernorm_quantize_amax", "fp8_gemm", "fp8_dequantize",
            "fp8_amax_and_scale_update", "fp8_status_string", "fp8q_tensor", "Fp8qError",
            "E4M3", "E5M2", "BF16", "F32", "AMAX_MAX", "AMAX_MOST_RECENT", "LIB_PATH", "lib"]

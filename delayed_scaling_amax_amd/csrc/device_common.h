@@ -45,4 +45,20 @@ __device__ __forceinline__ uint32_t block_max_u32(uint32_t v, uint32_t* red) {
   return r;
 }
 
+// New scale of one tensor from its selected amax (bit pattern `sel_bits`): RN32(sel /
+// FP8_MAX) * 2^margin, or the previous scale when sel or the result is not finite or
+// not > 0 ("User Guide on Native XLA-FP8", section "JAX": scale = amax / FP8_MAX).
+__device__ __forceinline__ float next_scale(uint32_t sel_bits, uint32_t fmt, float s_old,
+                                            int margin) {
+  const float sel = as_float(sel_bits);
+  const float fmax = fmt ? kE5M2Max : kE4M3Max;
+  float s = s_old;
+  if (__builtin_isfinite(sel) && sel > 0.0f) {
+    float c = sel / fmax;
+    c = ldexpf(c, margin);
+    if (__builtin_isfinite(c) && c > 0.0f) s = c;
+  }
+  return s;
+}
+
 }  // namespace fp8q

@@ -34,4 +34,17 @@ inline int current_device_cus(int* cus) {
 
 inline int launch_status(hipError_t e) { return e == hipSuccess ? FP8Q_OK : FP8Q_EHIP; }
 
+// Host checks of fp8_amax_and_scale_update's arguments (shared with the fused step).
+inline int validate_update(const float* amax, const float* hist, const float* scale,
+                           const float* scale_inv, const uint8_t* formats, int64_t n,
+                           int64_t history_len, int algo, int margin) {
+  if (n < 0 || history_len < 1) return FP8Q_EINVAL;
+  if (algo != FP8Q_AMAX_MAX && algo != FP8Q_AMAX_MOST_RECENT) return FP8Q_EINVAL;
+  if (margin < -126 || margin > 126) return FP8Q_EINVAL;
+  if (n == 0) return FP8Q_OK;
+  if (!amax || !hist || !scale || !scale_inv || !formats) return FP8Q_EINVAL;
+  if (history_len > (INT64_MAX / 8) / n) return FP8Q_EINVAL;  // H*n floats must be addressable
+  return FP8Q_OK;
+}
+
 }  // namespace fp8q

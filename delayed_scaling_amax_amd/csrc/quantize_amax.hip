@@ -25,6 +25,8 @@
 //  * Saturation with v_med3_f32 against +-FP8_MAX, then the native OCP convert
 //    v_cvt_pk_fp8_f32 / v_cvt_pk_bf8_f32 (round to nearest even).  NaN quotients
 //    (only possible on the IEEE path) are written as 0x7F with the sign of x.
+#include <hip/hip_ext.h>
+
 #include "device_common.h"
 #include "host_common.h"
 #include "quant_math.h"
@@ -137,12 +139,33 @@ __host__ __device__ __forceinline__ int entry_kind(const QEntry& e) {
   return e.gelu ? 4 + e.fmt : e.dtype * 2 + e.fmt;
 }
 
+// The batched amax_and_scale_update appended to a quantize launch
+// (fp8_quantize_amax_and_update): run by the block that finishes last, over n <=
+// kQUpdMaxCols tensors with history[H][n], H * n <= kQUpdMaxElems.
+constexpr int64_t kQUpdMaxCols = 256;
+constexpr int64_t kQUpdMaxElems = 65536;
+struct QUpdate {
+  float* amax;
+  float* hist;
+  float* scale;
+  float* scale_inv;
+  const uint8_t* formats;
+  uint32_t* counter;  // blocks finished; 0 at launch, left 0 by the last block
+  int64_t n;
+  int64_t H;
+  int32_t algo;
+  int32_t margin;
+  int32_t reset;
+  int32_t pad;
+};
+
 // Entries are sorted by kind: kind k occupies [run_end[k-1], run_end[k]).
 struct QTable {
   QEntry e[kQMaxEntries];
   int64_t total_full;
   int32_t n;
   int32_t run_end[kQKinds];
+  QUpdate upd;  // used by the kUpd kernel instances only
 };
 static_assert(sizeof(QTable) <= 4096, "the table travels as the kernel argument");
 
@@ -226,6 +249,7 @@ struct QShared {
   uint32_t xlim[kQMaxEntries];  // magnitude bits at which the fixed-code path starts
   uint32_t win[kQMaxEntries];   // scale inside the Markstein window
   uint32_t amax[kQMaxEntries];  // this block's amax bits per tensor
+  uint32_t last;                // kUpd: this block finished last
 };
 
 // Fold a thread's accumulator into the block's amax slot of tensor t: wavefront max,
@@ -626,7 +650,71 @@ __device__ __forceinline__ void phase2_entry(const QTable& tab, QShared& sh, int
     if (kind == kKind) tensor_rest<T::kBF16, T::kFmt, T::kGelu>(tab, sh, t);
 }
 
-template <int kSrc>
+// ---------------------------------------------------------------- appended update
+// Whether this block is the last of the grid to finish.  Every thread's amax atomic is
+// performed before the block counts itself, so the last block sees every block's
+// contribution.  Only device-scope atomics have to be ordered here (the amax maxima and
+// the count), so waiting for the atomics to complete is enough: a device-scope fence
+// would write back and invalidate the XCD's L2 in every block.  Contains barriers:
+// every thread of the block calls it once.
+__device__ __forceinline__ bool finished_last(uint32_t* counter, QShared& sh) {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this thread's amax atomic performed
+  __syncthreads();
+  if (threadIdx.x == 0) sh.last = atomicAdd(counter, 1u) == gridDim.x - 1 ? 1u : 0u;
+  __syncthreads();
+  return sh.last != 0;
+}
+
+// The batched update of u.n tensors by one block, after every block's amax atomics
+// (read back with device-scope atomic loads; nothing else it reads is written by another
+// block of the launch):
+// the same arithmetic as amax_and_scale_update_kernel ("Implement fused kernel for FP8
+// scale update": roll the history in place, insert the new amax, select, new scale).
+// The history's destination elements [n, H n) (flattened, row-major) are walked from
+// the top in chunks of kQBlock*4: a chunk loads its sources (one row up), a barrier,
+// then stores; sources below the chunk are loaded only by later chunks, so no element
+// is overwritten before it is read.
+__device__ void update_in_block(const QUpdate& u, uint32_t* colmax) {
+  constexpr int kR = 4;
+  const int tid = threadIdx.x;
+  const int64_t n = u.n, total = u.H * u.n;
+  uint32_t* hist = (uint32_t*)u.hist;
+  for (int64_t c = tid; c < n; c += kQBlock) colmax[c] = 0u;
+  __syncthreads();
+  for (int64_t hi = total; hi > n; hi -= kQBlock * kR) {
+    const int64_t lo = hi - kQBlock * kR > n ? hi - kQBlock * kR : n;
+    uint32_t v[kR];
+#pragma unroll
+    for (int k = 0; k < kR; ++k) {
+      const int64_t i = lo + tid + (int64_t)k * kQBlock;
+      if (i < hi) {
+        v[k] = hist[i - n];
+        atomicMax(&colmax[(uint32_t)i % (uint32_t)n], v[k]);  // H n <= kQUpdMaxElems
+      }
+    }
+    __syncthreads();  // every load of the chunk before any store
+#pragma unroll
+    for (int k = 0; k < kR; ++k) {
+      const int64_t i = lo + tid + (int64_t)k * kQBlock;
+      if (i < hi) hist[i] = v[k];
+    }
+  }
+  __syncthreads();
+  for (int64_t t = tid; t < n; t += kQBlock) {
+    const uint32_t ab = __hip_atomic_load((uint32_t*)u.amax + t, __ATOMIC_RELAXED,
+                                          __HIP_MEMORY_SCOPE_AGENT);
+    uint32_t sel_bits = colmax[t] > ab ? colmax[t] : ab;
+    if (u.algo == FP8Q_AMAX_MOST_RECENT) sel_bits = ab;
+    hist[t] = ab;  // row 0; loaded (as the source of row 1) before the last barrier
+    const float s = next_scale(sel_bits, u.formats[t], u.scale[t], u.margin);
+    u.scale[t] = s;
+    u.scale_inv[t] = 1.0f / s;
+    if (u.reset) u.amax[t] = 0.0f;
+  }
+  if (tid == 0) __hip_atomic_store(u.counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <int kSrc, bool kUpd>
 __global__ __launch_bounds__(kQBlock) void quantize_amax_kernel(const QTable tab) {
   __shared__ QShared sh;
   const int n = tab.n;
@@ -655,6 +743,10 @@ __global__ __launch_bounds__(kQBlock) void quantize_amax_kernel(const QTable tab
   __syncthreads();
   // one global atomic per tensor this block saw a non-zero |x| in
   if (tid < n && sh.amax[tid] != 0) atomicMax(tab.e[tid].amax, sh.amax[tid]);
+  if constexpr (kUpd) {
+    __shared__ uint32_t colmax[kQUpdMaxCols];
+    if (finished_last(tab.upd.counter, sh)) update_in_block(tab.upd, colmax);
+  }
 }
 
 // ---------------------------------------------------------------- host side
@@ -697,7 +789,12 @@ static void plan_entry(const fp8q_tensor& t, bool gelu, QEntry* e) {
   e->nfull = e->n_vec / kQChunk;
 }
 
-static int launch_table(QTable* tab, hipStream_t stream) {
+// Launch one table.  `start`/`stop` (may be null): events that take the start and stop
+// time of this kernel's own dispatch (hipExtLaunchKernel), for profiling.  *launched
+// tells whether a kernel was enqueued (a table of empty tensors enqueues nothing).
+static int launch_table(QTable* tab, bool upd, hipStream_t stream, hipEvent_t start,
+                        hipEvent_t stop, bool* launched) {
+  *launched = false;
   int64_t units = 0;
   for (int i = 0; i < tab->n; ++i) units += tab->e[i].n_units;
   if (units == 0) return FP8Q_OK;
@@ -708,41 +805,71 @@ static int launch_table(QTable* tab, hipStream_t stream) {
   for (int i = 0; i < tab->n; ++i)
     src_kinds |= tab->e[i].gelu ? 4 : tab->e[i].dtype == FP8Q_BF16 ? 1 : 2;
   // tables hold either plain entries (any mix of bf16 and fp32) or gelu entries only
-  const void* fn = src_kinds == 1   ? (const void*)quantize_amax_kernel<1>
-                   : src_kinds == 2 ? (const void*)quantize_amax_kernel<2>
-                   : src_kinds == 3 ? (const void*)quantize_amax_kernel<3>
-                   : src_kinds == 4 ? (const void*)quantize_amax_kernel<4>
-                                    : nullptr;
+  const void* fn = nullptr;
+  if (!upd)
+    fn = src_kinds == 1   ? (const void*)quantize_amax_kernel<1, false>
+         : src_kinds == 2 ? (const void*)quantize_amax_kernel<2, false>
+         : src_kinds == 3 ? (const void*)quantize_amax_kernel<3, false>
+         : src_kinds == 4 ? (const void*)quantize_amax_kernel<4, false>
+                          : nullptr;
+  else
+    fn = src_kinds == 1   ? (const void*)quantize_amax_kernel<1, true>
+         : src_kinds == 2 ? (const void*)quantize_amax_kernel<2, true>
+         : src_kinds == 3 ? (const void*)quantize_amax_kernel<3, true>
+                          : nullptr;
   if (fn == nullptr) return FP8Q_EINVAL;
   // The grid-stride schedule needs every block resident at once: cap the blocks per
   // CU at what the instance's register use allows.
-  static std::atomic<int> fit[8];
-  int per_cu = fit[src_kinds].load(std::memory_order_relaxed);
+  static std::atomic<int> fit[16];
+  const int inst = src_kinds + (upd ? 8 : 0);
+  int per_cu = fit[inst].load(std::memory_order_relaxed);
   if (per_cu <= 0) {
     int occ = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, fn, kQBlock, 0) != hipSuccess)
       return FP8Q_EHIP;
     const int want = src_kinds == 4 ? kQGeluBlocksPerCU : kQBlocksPerCU;
     per_cu = occ < want ? (occ > 0 ? occ : 1) : want;
-    fit[src_kinds].store(per_cu, std::memory_order_relaxed);
+    fit[inst].store(per_cu, std::memory_order_relaxed);
   }
   const int64_t max_blocks = (int64_t)cus * per_cu;
   int64_t blocks = tab->total_full > tab->n ? tab->total_full : tab->n;
   if (blocks > max_blocks) blocks = max_blocks;
   if (blocks < 1) blocks = 1;
   void* args[] = {tab};
-  return launch_status(hipLaunchKernel(fn, dim3((unsigned)blocks), dim3(kQBlock), args, 0, stream));
+  *launched = true;
+  if (start == nullptr && stop == nullptr)
+    return launch_status(
+        hipLaunchKernel(fn, dim3((unsigned)blocks), dim3(kQBlock), args, 0, stream));
+  return launch_status(hipExtLaunchKernel(fn, dim3((unsigned)blocks), dim3(kQBlock), args, 0,
+                                          stream, start, stop, 0));
 }
 
 // Quantize n tensors (with the gelu prologue on every one if `gelu`), at most
-// kQMaxEntries per launch.
-static int quantize_entries(const fp8q_tensor* tensors, int n, bool gelu, hipStream_t stream) {
+// kQMaxEntries per launch.  Optional profiling events: `start` takes the start time of
+// the first kernel launched, `stop` the stop time of the last; when no kernel is
+// launched both are recorded on the stream, so they still form a valid (empty) interval.
+static int validate_entries(const fp8q_tensor* tensors, int n, bool gelu) {
   if (n < 0 || (n > 0 && tensors == nullptr)) return FP8Q_EINVAL;
   for (int i = 0; i < n; ++i) {
     int st = validate_entry(tensors[i]);
     if (st != FP8Q_OK) return st;
     if (gelu && tensors[i].src_dtype != FP8Q_BF16) return FP8Q_EUNSUPPORTED;
   }
+  return FP8Q_OK;
+}
+
+// With `upd` (validated entries, at most kQMaxEntries, at least one non-empty), the
+// single launch also carries the appended update.
+static int quantize_entries(const fp8q_tensor* tensors, int n, bool gelu, hipStream_t stream,
+                            hipEvent_t start = nullptr, hipEvent_t stop = nullptr,
+                            const QUpdate* upd = nullptr) {
+  int vst = validate_entries(tensors, n, gelu);
+  if (vst != FP8Q_OK) return vst;
+  // the stop event goes to the last launch: find the last block of entries with work
+  int last_base = -1;
+  for (int i = 0; i < n; ++i)
+    if (tensors[i].numel > 0) last_base = i / kQMaxEntries * kQMaxEntries;
+  bool started = false;
   for (int base = 0; base < n; base += kQMaxEntries) {
     QTable tab;
     tab.n = 0;
@@ -760,8 +887,16 @@ static int quantize_entries(const fp8q_tensor* tensors, int n, bool gelu, hipStr
       }
       tab.run_end[kind] = tab.n;
     }
-    int st = launch_table(&tab, stream);
+    tab.upd = upd != nullptr ? *upd : QUpdate{};
+    bool launched = false;
+    int st = launch_table(&tab, upd != nullptr, stream, started ? nullptr : start,
+                          base == last_base ? stop : nullptr, &launched);
     if (st != FP8Q_OK) return st;
+    started = started || launched;
+  }
+  if (last_base < 0) {  // nothing launched
+    if (start != nullptr && hipEventRecord(start, stream) != hipSuccess) return FP8Q_EHIP;
+    if (stop != nullptr && hipEventRecord(stop, stream) != hipSuccess) return FP8Q_EHIP;
   }
   return FP8Q_OK;
 }
@@ -772,6 +907,44 @@ using namespace fp8q;
 
 extern "C" int fp8_multi_quantize_amax(const fp8q_tensor* tensors, int n, void* stream) {
   return quantize_entries(tensors, n, false, (hipStream_t)stream);
+}
+
+extern "C" int fp8_multi_quantize_amax_timed(const fp8q_tensor* tensors, int n, void* stream,
+                                             void* start_event, void* stop_event) {
+  return quantize_entries(tensors, n, false, (hipStream_t)stream, (hipEvent_t)start_event,
+                          (hipEvent_t)stop_event);
+}
+
+extern "C" int fp8_quantize_amax_and_update(const fp8q_tensor* tensors, int n_tensors,
+                                            float* amax, float* amax_history, float* scale,
+                                            float* scale_inv, const uint8_t* formats, int64_t n,
+                                            int64_t history_len, int algo, int margin,
+                                            int reset_amax, uint32_t* workspace, void* stream,
+                                            void* start_event, void* stop_event) {
+  // everything is validated before anything is enqueued
+  int st = validate_entries(tensors, n_tensors, false);
+  if (st != FP8Q_OK) return st;
+  st = validate_update(amax, amax_history, scale, scale_inv, formats, n, history_len, algo,
+                       margin);
+  if (st != FP8Q_OK) return st;
+  if (workspace == nullptr) return FP8Q_EINVAL;
+  bool any = false;
+  for (int i = 0; i < n_tensors; ++i) any = any || tensors[i].numel > 0;
+  const bool fuse = n > 0 && any && n_tensors <= kQMaxEntries && n <= kQUpdMaxCols &&
+                    history_len <= kQUpdMaxElems / n;
+  hipStream_t s = (hipStream_t)stream;
+  if (fuse) {
+    QUpdate u{amax, amax_history, scale, scale_inv, formats, workspace, n, history_len,
+              algo, margin, reset_amax ? 1 : 0, 0};
+    return quantize_entries(tensors, n_tensors, false, s, (hipEvent_t)start_event,
+                            (hipEvent_t)stop_event, &u);
+  }
+  // the same results as two launches
+  st = quantize_entries(tensors, n_tensors, false, s, (hipEvent_t)start_event,
+                        (hipEvent_t)stop_event);
+  if (st != FP8Q_OK) return st;
+  return fp8_amax_and_scale_update(amax, amax_history, scale, scale_inv, formats, n,
+                                   history_len, algo, margin, reset_amax, stream);
 }
 
 static fp8q_tensor single_entry(const void* src, int src_dtype, uint8_t* dst, int64_t numel,

@@ -164,14 +164,7 @@ __global__ __launch_bounds__(kUBlock) void amax_and_scale_update_kernel(
     for (int w = 0; w < kUBlock / 64; ++w) sel_bits = sel_bits > red[w][tid] ? sel_bits : red[w][tid];
     hist[t] = a_in;  // row 0; row 0 was loaded (as source of row 1) before the last barrier
     if (algo == FP8Q_AMAX_MOST_RECENT) sel_bits = ab;
-    const float sel = as_float(sel_bits);
-    const float fmax = fmt ? kE5M2Max : kE4M3Max;
-    float s = s_old;
-    if (__builtin_isfinite(sel) && sel > 0.0f) {
-      float c = sel / fmax;
-      c = ldexpf(c, margin);
-      if (__builtin_isfinite(c) && c > 0.0f) s = c;
-    }
+    const float s = next_scale(sel_bits, fmt, s_old, margin);
     scale[t] = s;
     scale_inv[t] = 1.0f / s;
     if (reset_amax) amax[t] = 0.0f;
@@ -186,12 +179,9 @@ extern "C" int fp8_amax_and_scale_update(float* amax, float* amax_history, float
                                          float* scale_inv, const uint8_t* formats, int64_t n,
                                          int64_t history_len, int algo, int margin,
                                          int reset_amax, void* stream) {
-  if (n < 0 || history_len < 1) return FP8Q_EINVAL;
-  if (algo != FP8Q_AMAX_MAX && algo != FP8Q_AMAX_MOST_RECENT) return FP8Q_EINVAL;
-  if (margin < -126 || margin > 126) return FP8Q_EINVAL;
-  if (n == 0) return FP8Q_OK;
-  if (!amax || !amax_history || !scale || !scale_inv || !formats) return FP8Q_EINVAL;
-  if (history_len > (INT64_MAX / 8) / n) return FP8Q_EINVAL;  // H*n floats must be addressable
+  const int st = validate_update(amax, amax_history, scale, scale_inv, formats, n, history_len,
+                                 algo, margin);
+  if (st != FP8Q_OK || n == 0) return st;
   const int64_t groups = ceil_div(n, kUCols);
   const int64_t per_xcd = ceil_div(groups, 8);
   const int64_t blocks = 8 * per_xcd;

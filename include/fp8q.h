@@ -121,6 +121,22 @@ int fp8_quantize_amax(const void* src, int src_dtype, uint8_t* dst, int64_t nume
 int fp8_multi_quantize_amax(const fp8q_tensor* tensors, int n, void* stream);
 
 /*
+ * fp8_multi_quantize_amax_timed -- fp8_multi_quantize_amax with profiling events: the
+ * same validation, kernels and results, each kernel launched with hipExtLaunchKernel so
+ * that the events take the start and stop time of the kernel's own dispatch rather than
+ * of a stream position before it (an event recorded on the stream ahead of a launch also
+ * spans the dispatch latency).  For measuring the kernel's duration with HIP events.
+ *   start_event  hipEvent_t created by the caller with timing enabled, or NULL: takes
+ *                the start of the first kernel launched.
+ *   stop_event   likewise, or NULL: takes the end of the last kernel launched.
+ * When no kernel is launched (n == 0 or every numel == 0) both events are recorded on
+ * the stream, an empty interval.  The events remain the caller's.
+ * Returns FP8Q_OK, FP8Q_EINVAL or FP8Q_EHIP.
+ */
+int fp8_multi_quantize_amax_timed(const fp8q_tensor* tensors, int n, void* stream,
+                                  void* start_event, void* stop_event);
+
+/*
  * fp8_gelu_quantize_amax -- the activation between the two dense layers of the MLP,
  * quantized in the kernel that produces it: the bf16 pre-activation x is read, the
  * tanh-form gelu is applied, and the result goes through fp8_quantize_amax's quantize
@@ -247,6 +263,39 @@ int fp8_amax_and_scale_update(float* amax, float* amax_history, float* scale,
                               float* scale_inv, const uint8_t* formats, int64_t n,
                               int64_t history_len, int algo, int margin, int reset_amax,
                               void* stream);
+
+/*
+ * fp8_quantize_amax_and_update -- one whole delayed-scaling step: exactly
+ *   fp8_multi_quantize_amax(tensors, n_tensors, stream);
+ *   fp8_amax_and_scale_update(amax, amax_history, scale, scale_inv, formats, n,
+ *                             history_len, algo, margin, reset_amax, stream);
+ * (same results, bit for bit) in ONE kernel launch when it fits: the quantize pass of
+ * "Fusion of Fp8 quantization and amax reduction kernels" and the fused update of
+ * "Implement fused kernel for FP8 scale update" share the launch, the update running in
+ * the block that finishes the quantize last, after every block's amax is accumulated.
+ * This removes the kernel boundary and the second launch between the two passes.
+ * The single launch is used when 1 <= n_tensors <= 32, some tensor is non-empty,
+ * 1 <= n <= 256 and history_len * n <= 65536; otherwise the call enqueues the two
+ * launches above (same results).  The quantize reads each tensor's scale before the
+ * update writes `scale`, so the entries' scale/amax pointers may (and normally do)
+ * point into scale[] / amax[].
+ *   tensors, n_tensors   as fp8_multi_quantize_amax.
+ *   amax ... reset_amax  as fp8_amax_and_scale_update.
+ *   workspace   DEVICE pointer to one uint32_t (4 bytes, caller-owned), 0 at the first
+ *               call; every call leaves it 0.  It counts the finished blocks, so calls
+ *               that may run concurrently (different streams) need separate
+ *               workspaces.  Required (non-NULL) even when the two-launch form is used.
+ *   start_event, stop_event   optional profiling events as in
+ *               fp8_multi_quantize_amax_timed (NULL for none); with the two-launch form
+ *               they span the quantize kernels only.
+ * Every argument is validated before anything is enqueued.
+ * Returns FP8Q_OK, FP8Q_EINVAL or FP8Q_EHIP.
+ */
+int fp8_quantize_amax_and_update(const fp8q_tensor* tensors, int n_tensors, float* amax,
+                                 float* amax_history, float* scale, float* scale_inv,
+                                 const uint8_t* formats, int64_t n, int64_t history_len,
+                                 int algo, int margin, int reset_amax, uint32_t* workspace,
+                                 void* stream, void* start_event, void* stop_event);
 
 /* Static, human-readable text for a status code. */
 const char* fp8_status_string(int status);

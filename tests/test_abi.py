@@ -19,8 +19,8 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted([
-        "fp8_quantize_amax", "fp8_multi_quantize_amax", "fp8_gelu_quantize_amax",
-        "fp8_layernorm_quantize_amax", "fp8_dequantize", "fp8_amax_and_scale_update",
+        "fp8_quantize_amax", "fp8_multi_quantize_amax", "fp8_multi_quantize_amax_timed",
+        "fp8_gelu_quantize_amax", "fp8_layernorm_quantize_amax", "fp8_quantize_amax_and_update", "fp8_dequantize", "fp8_amax_and_scale_update",
         "fp8_gemm", "fp8_status_string"])
 
 
@@ -142,6 +142,10 @@ def test_multi_rejects_before_enqueue():
     assert d.lib.fp8_multi_quantize_amax(arr, 3, None) == d.EINVAL
     assert d.lib.fp8_multi_quantize_amax(arr, -1, None) == d.EINVAL
     assert d.lib.fp8_multi_quantize_amax(None, 2, None) == d.EINVAL
+    # the profiling form validates the same way (events untouched when it rejects)
+    assert d.lib.fp8_multi_quantize_amax_timed(arr, 3, None, BAD, BAD) == d.EINVAL
+    assert d.lib.fp8_multi_quantize_amax_timed(arr, -1, None, BAD, BAD) == d.EINVAL
+    assert d.lib.fp8_multi_quantize_amax_timed(None, 2, None, BAD, BAD) == d.EINVAL
 
 
 def test_zero_size_is_noop_without_device():
@@ -151,6 +155,7 @@ def test_zero_size_is_noop_without_device():
         arr[i] = d.fp8q_tensor(None, None, 0, 1, 1, BAD, BAD)
     assert d.lib.fp8_multi_quantize_amax(arr, 2, None) == d.OK
     assert d.lib.fp8_multi_quantize_amax(None, 0, None) == d.OK
+    assert d.lib.fp8_multi_quantize_amax_timed(arr, 2, None, None, None) == d.OK
     assert d.lib.fp8_quantize_amax(None, 0, None, 0, 0, BAD, BAD, None) == d.OK
     assert d.lib.fp8_dequantize(None, 0, None, 1, 0, BAD, None) == d.OK
     assert d.lib.fp8_amax_and_scale_update(None, None, None, None, None, 0, 4, 0, 0, 0,
@@ -179,3 +184,34 @@ def test_update_rejects_invalid(n, H, algo, margin, ptrs):
     if ptrs < 5:
         p[ptrs] = None
     assert d.lib.fp8_amax_and_scale_update(*p, n, H, algo, margin, 0, None) == d.EINVAL
+
+
+def _step(d, arr, nt, n=3, H=4, algo=0, margin=0, ws=BAD, ptrs=5):
+    p = [BAD] * 5
+    if ptrs < 5:
+        p[ptrs] = None
+    return d.lib.fp8_quantize_amax_and_update(arr, nt, *p, n, H, algo, margin, 1, ws, None,
+                                              None, None)
+
+
+def test_fused_step_rejects_before_enqueue():
+    """Invalid entries, invalid update arguments or a NULL workspace: EINVAL with nothing
+    enqueued (no device exists here, so any enqueue would fail as EHIP instead)."""
+    import delayed_scaling_amax_amd as d
+    arr = (d.fp8q_tensor * 2)()
+    for i in range(2):
+        arr[i] = d.fp8q_tensor(None, None, 0, 0, 0, BAD, BAD)
+    bad = (d.fp8q_tensor * 2)()
+    for i in range(2):
+        bad[i] = d.fp8q_tensor(None, None, 0, 0, 0, BAD, BAD)
+    bad[1].src_dtype = 7
+    assert _step(d, bad, 2) == d.EINVAL               # invalid entry
+    assert _step(d, arr, -1) == d.EINVAL              # negative tensor count
+    assert _step(d, arr, 2, n=-1) == d.EINVAL         # negative update size
+    assert _step(d, arr, 2, H=0) == d.EINVAL          # empty history
+    assert _step(d, arr, 2, algo=5) == d.EINVAL       # unknown algo
+    assert _step(d, arr, 2, margin=200) == d.EINVAL   # margin out of range
+    assert _step(d, arr, 2, ptrs=2) == d.EINVAL       # NULL scale
+    assert _step(d, arr, 2, ws=None) == d.EINVAL      # NULL workspace
+    # empty tensors and an empty update: nothing to enqueue
+    assert _step(d, arr, 2, n=0) == d.OK

@@ -173,3 +173,40 @@ def test_amax_max_accumulates_and_is_deterministic(orc):
     for k in range(3):
         assert np.array_equal(np.atleast_1d(outs[0][k]).view(np.uint8),
                               np.atleast_1d(outs[1][k]).view(np.uint8))
+
+
+def test_timed_form_matches_oracle(orc):
+    """fp8_multi_quantize_amax_timed: the same codes and amaxes as the oracle over 40
+    entries (two launches: start taken by the first, stop by the last), events that
+    bound a positive interval no longer than the stream events around the call, and an
+    empty call that still records both events."""
+    import delayed_scaling_amax_amd as d
+    g = np.random.Generator(np.random.PCG64(4242))
+    n = 40
+    # bf16 (truncated binary32) N(0, 100) tensors of ragged sizes
+    xs = [((g.standard_normal(int(g.integers(1, 70000))) * 10).astype(np.float32)
+           .view(np.uint32) >> 16).astype(np.uint16) for _ in range(n)]
+    fmts = [i % 2 for i in range(n)]
+    scales = [float(np.float32(2.0 ** g.uniform(-8, 4))) for _ in range(n)]
+    note("timed form: %d entries, %d elements" % (n, sum(x.size for x in xs)))
+    srcs = [dev_src(x) for x in xs]
+    dsts = [torch.empty(x.size, dtype=torch.uint8, device="cuda") for x in xs]
+    s_dev, a_dev = f32(scales), torch.zeros(n, dtype=torch.float32, device="cuda")
+    outer = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    inner = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    outer[0].record()
+    d.fp8_multi_quantize_amax_timed([(srcs[i], dsts[i], s_dev[i:i + 1], a_dev[i:i + 1],
+                                      fmts[i]) for i in range(n)], inner[0], inner[1])
+    outer[1].record()
+    torch.cuda.synchronize()
+    amaxes = a_dev.cpu().numpy()
+    for i in range(n):
+        want, wa = orc.quantize_amax(xs[i], fmts[i], scales[i])
+        assert dsts[i].cpu().numpy().tobytes() == want.tobytes(), i
+        assert bits(amaxes[i]) == bits(wa), i
+    t_in, t_out = inner[0].elapsed_time(inner[1]), outer[0].elapsed_time(outer[1])
+    assert 0.0 < t_in <= t_out + 1e-3, (t_in, t_out)
+    e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    d.fp8_multi_quantize_amax_timed([], e[0], e[1])
+    torch.cuda.synchronize()
+    assert e[0].elapsed_time(e[1]) >= 0.0
