@@ -144,6 +144,7 @@ __host__ __device__ __forceinline__ int entry_kind(const QEntry& e) {
 // kQUpdMaxCols tensors with history[H][n], H * n <= kQUpdMaxElems.
 constexpr int64_t kQUpdMaxCols = 256;
 constexpr int64_t kQUpdMaxElems = 65536;
+static_assert(kQUpdMaxCols <= kQBlock, "the appended update gives each column a thread");
 struct QUpdate {
   float* amax;
   float* hist;
@@ -667,49 +668,68 @@ __device__ __forceinline__ bool finished_last(uint32_t* counter, QShared& sh) {
 
 // The batched update of u.n tensors by one block, after every block's amax atomics
 // (read back with device-scope atomic loads; nothing else it reads is written by another
-// block of the launch):
-// the same arithmetic as amax_and_scale_update_kernel ("Implement fused kernel for FP8
-// scale update": roll the history in place, insert the new amax, select, new scale).
-// The history's destination elements [n, H n) (flattened, row-major) are walked from
-// the top in chunks of kQBlock*4: a chunk loads its sources (one row up), a barrier,
-// then stores; sources below the chunk are loaded only by later chunks, so no element
-// is overwritten before it is read.
+// block of the launch): the same arithmetic as amax_and_scale_update_kernel ("Implement
+// fused kernel for FP8 scale update": roll the history in place, insert the new amax,
+// select, new scale).  Thread t owns column t mod n and every (kQBlock / n)-th history
+// row, so consecutive threads touch consecutive columns of a row and each keeps its
+// column maximum in a register (one LDS atomic per thread at the end: per-element
+// atomics on n slots would serialize).  Destination rows [1, H) are walked from the top
+// in chunks of (kQBlock / n) * 32 rows (history 1024 of up to 64 tensors in one chunk,
+// one load round trip): a chunk loads its source rows (one row up), a barrier, then
+// stores; rows below the chunk are read only by later chunks, so no row is overwritten
+// before it is read.
 __device__ void update_in_block(const QUpdate& u, uint32_t* colmax) {
-  constexpr int kR = 4;
+  constexpr int kR = 32;  // rows per thread per chunk
   const int tid = threadIdx.x;
-  const int64_t n = u.n, total = u.H * u.n;
+  const int n = (int)u.n;  // 1 .. kQUpdMaxCols (= kQBlock)
+  const int groups = kQBlock / n;
+  const int c = tid % n, g = tid / n;
+  const bool active = g < groups;
+  const int64_t H = u.H, span = (int64_t)groups * kR;
   uint32_t* hist = (uint32_t*)u.hist;
-  for (int64_t c = tid; c < n; c += kQBlock) colmax[c] = 0u;
-  __syncthreads();
-  for (int64_t hi = total; hi > n; hi -= kQBlock * kR) {
-    const int64_t lo = hi - kQBlock * kR > n ? hi - kQBlock * kR : n;
+  // thread t < n: tensor t's inputs, fetched now so their latency overlaps the history's
+  uint32_t ab = 0u, fmt = 0u;
+  float s_old = 0.0f;
+  if (tid < n) {
+    ab = __hip_atomic_load((uint32_t*)u.amax + tid, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_old = u.scale[tid];
+    fmt = u.formats[tid];
+    colmax[tid] = 0u;
+  }
+  uint32_t m = 0u;
+  for (int64_t d_hi = H; d_hi > 1; d_hi -= span) {
+    const int64_t d_lo = d_hi - span > 1 ? d_hi - span : 1;
+    // every lane loads (rows outside the chunk read element 0, always present) and the
+    // maxima come after all loads are issued: one round trip, no per-load wait
     uint32_t v[kR];
 #pragma unroll
     for (int k = 0; k < kR; ++k) {
-      const int64_t i = lo + tid + (int64_t)k * kQBlock;
-      if (i < hi) {
-        v[k] = hist[i - n];
-        atomicMax(&colmax[(uint32_t)i % (uint32_t)n], v[k]);  // H n <= kQUpdMaxElems
-      }
+      const int64_t d = d_lo + g + (int64_t)k * groups;
+      v[k] = hist[active && d < d_hi ? (d - 1) * n + c : 0];
+    }
+#pragma unroll
+    for (int k = 0; k < kR; ++k) {
+      const int64_t d = d_lo + g + (int64_t)k * groups;
+      if (active && d < d_hi) m = m > v[k] ? m : v[k];
     }
     __syncthreads();  // every load of the chunk before any store
 #pragma unroll
     for (int k = 0; k < kR; ++k) {
-      const int64_t i = lo + tid + (int64_t)k * kQBlock;
-      if (i < hi) hist[i] = v[k];
+      const int64_t d = d_lo + g + (int64_t)k * groups;
+      if (active && d < d_hi) hist[d * n + c] = v[k];
     }
   }
+  __syncthreads();  // colmax zeroed (and every chunk done) before the maxima go in
+  if (active && m != 0u) atomicMax(&colmax[c], m);
   __syncthreads();
-  for (int64_t t = tid; t < n; t += kQBlock) {
-    const uint32_t ab = __hip_atomic_load((uint32_t*)u.amax + t, __ATOMIC_RELAXED,
-                                          __HIP_MEMORY_SCOPE_AGENT);
-    uint32_t sel_bits = colmax[t] > ab ? colmax[t] : ab;
+  if (tid < n) {
+    uint32_t sel_bits = colmax[tid] > ab ? colmax[tid] : ab;
     if (u.algo == FP8Q_AMAX_MOST_RECENT) sel_bits = ab;
-    hist[t] = ab;  // row 0; loaded (as the source of row 1) before the last barrier
-    const float s = next_scale(sel_bits, u.formats[t], u.scale[t], u.margin);
-    u.scale[t] = s;
-    u.scale_inv[t] = 1.0f / s;
-    if (u.reset) u.amax[t] = 0.0f;
+    hist[tid] = ab;  // row 0; loaded (as the source of row 1) before the last barrier
+    const float s = next_scale(sel_bits, fmt, s_old, u.margin);
+    u.scale[tid] = s;
+    u.scale_inv[tid] = 1.0f / s;
+    if (u.reset) u.amax[tid] = 0.0f;
   }
   if (tid == 0) __hip_atomic_store(u.counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
