@@ -1,10 +1,10 @@
 """Benchmark of the FP8 delayed-scaling hot path on one MI355X.
 
-One step = the multi-tensor fused quantize+amax over every tensor of the workload
-(bf16 -> FP8 with the previous step's scale) and the batched amax_and_scale_update
-(history roll, amax selection, new scale/scale_inv, amax reset), on inputs already
-resident in HBM, in one launch (fp8_quantize_amax_and_update); the same steps as two
-launches (fp8_multi_quantize_amax, then fp8_amax_and_scale_update) are timed beside.  Default workload: the MLP at hidden
+One step = one multi-tensor fused quantize+amax launch over every tensor of the
+workload (bf16 -> FP8 with the previous step's scale) followed by one batched
+amax_and_scale_update launch (history roll, amax selection, new scale/scale_inv, amax
+reset), on inputs already resident in HBM; the same steps in one launch each
+(fp8_quantize_amax_and_update) are timed beside.  Default workload: the MLP at hidden
 4096 / ffn 16384 (activation (2048,4,4096), weights 4096x16384 and 16384x4096, all
 E4M3, history 16).  Prints one JSON line.
 
@@ -34,7 +34,7 @@ PEAK_FP8_TFLOPS = 5000.0  # MI355X dense FP8 matrix throughput, published
 METRIC = "fused quantize+amax GB/s & % HBM peak; µs per batched scale update"
 KERNEL_SOURCE = os.path.join(ROOT, "delayed_scaling_amax_amd", "csrc", "quantize_amax.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "quantize_amax_mlp_4096_traffic.txt")
-STEP_KERNEL = "quantize_amax_kernel<1, true>"  # bf16 sources, update appended
+ROOFLINE_KERNEL = "quantize_amax_kernel<1, false>"  # the multi-tensor quantize, bf16 sources
 
 
 def log(msg):
@@ -50,9 +50,9 @@ def kernel_hash() -> str:
 
 
 def measured_traffic(workload: str):
-    """HBM bytes per launch of the one-launch step kernel from the committed rocprofv3
-    counter summary, or None if absent, for another workload or kernel, or taken on a
-    different kernel source."""
+    """HBM bytes per quantize launch from the committed rocprofv3 counter summary, or
+    None if absent, for another workload or kernel, or taken on a different kernel
+    source."""
     try:
         kv = {}
         with open(TRAFFIC_FILE) as f:
@@ -61,7 +61,7 @@ def measured_traffic(workload: str):
                     k, v = line.split("=", 1)
                     kv[k.strip()] = v.strip()
         if (kv.get("kernel_source_sha256_16") != kernel_hash() or kv.get("workload") != workload
-                or kv.get("kernel") != STEP_KERNEL):
+                or kv.get("kernel") != ROOFLINE_KERNEL):
             return None
         return float(kv["hbm_bytes_per_launch"])
     except (OSError, KeyError, ValueError):
@@ -179,35 +179,44 @@ def main():
     def update():
         d.fp8_amax_and_scale_update(amax, hist, scale, scale_inv, fdev, reset_amax=True)
 
-    ws = torch.zeros(1, dtype=torch.int32, device=dev)  # the fused step's block counter
+    def step(events=None):
+        """One step: the multi-tensor quantize + amax launch, then the batched update
+        launch (reset amax)."""
+        quantize(events)
+        update()
 
-    def step(events=(None, None)):
-        """One whole step in one launch: quantize + amax, then the update (reset amax)
-        in the block that finishes last."""
+    ws = torch.zeros(1, dtype=torch.int32, device=dev)  # the one-launch step's counter
+
+    def one_launch_step(events=(None, None)):
+        """The same step in one launch: the update runs in the block that finishes the
+        quantize last."""
         d.fp8_quantize_amax_and_update(entry_sets[step_no[0] % args.rotate], amax, hist,
                                        scale, scale_inv, fdev, ws, reset_amax=True,
                                        start_event=events[0], stop_event=events[1])
         step_no[0] += 1
 
-    # first step (prior scale): kept on the host for the parity check against the oracle;
-    # the amax it accumulated is history row 0 once the update has reset amax
-    step()
+    # first step (prior scale): kept on the host for the parity check against the oracle
+    quantize()
     torch.cuda.synchronize()
     first_codes = [x.cpu().numpy() for x in dsts]
+    first_amax = amax.cpu().numpy().copy()
+    update()
+    torch.cuda.synchronize()
     first_meta = {"hist": hist.cpu().numpy().copy(), "scale": scale.cpu().numpy().copy(),
                   "scale_inv": scale_inv.cpu().numpy().copy(), "amax": amax.cpu().numpy().copy()}
-    first_amax = first_meta["hist"][0].copy()
 
     for _ in range(args.warmup):
         step()
+        one_launch_step()  # the first launches of each kernel load it
     torch.cuda.synchronize()
 
-    # Timed region: K steps, each one launch (fp8_quantize_amax_and_update) carrying two
-    # HIP events that take the kernel's own start and stop time (hipExtLaunchKernel): its
-    # live duration for the roofline, without the dispatch latency that events recorded
-    # on the stream around the call would add, and without event markers between the
-    # steps. Two stream events bracket the whole region (device time of the K steps,
-    # beside the host wall clock that `value` uses).
+    # Two timed regions of K steps each. (1) The steps alone, bracketed by two stream
+    # events and the host clock, with a synchronize on both sides: `value` and
+    # ms_per_step. (2) The same steps, each quantize launch carrying two HIP events that
+    # take the kernel's own start and stop time (hipExtLaunchKernel): its live duration
+    # for the roofline, without the dispatch latency that events recorded on the stream
+    # around the call would add. Launches that carry events cost ~30 us more host time
+    # each, which would make small steps host-bound, so (1) carries none.
     K = args.steps
 
     def make_events():
@@ -217,62 +226,56 @@ def main():
             b.record()
         return e
 
-    ev = make_events()
-    region = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-    torch.cuda.synchronize()
-    t_start = time.perf_counter()
-    region[0].record()
-    for k in range(K):
-        step(ev[k])
-    region[1].record()
-    t_enq = time.perf_counter()  # all K steps enqueued (the host runs ahead of the GPU)
-    torch.cuda.synchronize()
-    t_end = time.perf_counter()
-    s_ms = [ev[k][0].elapsed_time(ev[k][1]) for k in range(K)]
-    region_ms = region[0].elapsed_time(region[1])
-    ms_per_step = (t_end - t_start) * 1e3 / K
+    def steps_region(fn):
+        """(host wall ms per step, device ms per step, host enqueue us per step) of K
+        calls of fn(k)."""
+        region = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        region[0].record()
+        for k in range(K):
+            fn(k)
+        region[1].record()
+        t_enq = time.perf_counter()  # all K steps enqueued (the host runs ahead)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        return ((t1 - t0) * 1e3 / K, region[0].elapsed_time(region[1]) / K,
+                (t_enq - t0) * 1e6 / K)
+
     qbytes = alg_bytes_quantize(w)
     ubytes = alg_bytes_update(n, w.history_len)
+    ms_per_step, dev_ms_per_step, enq_us = steps_region(lambda k: step())
     value = (qbytes + ubytes) / (ms_per_step * 1e-3) / 1e9
-    s_avg_us = 1e3 * float(np.mean(s_ms))
-    s_gbps = (qbytes + ubytes) / (s_avg_us * 1e-6) / 1e9
-    log("step %.3f ms (device %.3f ms, host enqueue %.1f us); one-launch step kernel avg "
-        "%.2f us (median %.2f) = %.1f GB/s" % (
-            ms_per_step, region_ms / K, (t_enq - t_start) * 1e6 / K, s_avg_us,
-            1e3 * float(np.median(s_ms)), s_gbps))
-
-    # The same K steps as two launches (fp8_multi_quantize_amax, then
-    # fp8_amax_and_scale_update), the quantize kernel timed the same way; u_ms spans the
-    # update kernel plus the gaps from one quantize kernel's end to the next one's start.
-    for _ in range(args.warmup):  # the first launches of these kernels load them
-        quantize()
-        update()
-    ev2 = make_events()
-    region2 = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-    torch.cuda.synchronize()
-    t2 = time.perf_counter()
-    region2[0].record()
-    for k in range(K):
-        quantize(ev2[k])
-        update()
-    region2[1].record()
-    t2_enq = time.perf_counter()
-    torch.cuda.synchronize()
-    two_ms_per_step = (time.perf_counter() - t2) * 1e3 / K
-    q_ms = [ev2[k][0].elapsed_time(ev2[k][1]) for k in range(K)]
-    u_ms = [ev2[k][1].elapsed_time(ev2[k + 1][0]) for k in range(K - 1)] or [0.0]
+    ev = make_events()
+    steps_region(lambda k: step(ev[k]))
+    q_ms = [ev[k][0].elapsed_time(ev[k][1]) for k in range(K)]
+    u_ms = [ev[k][1].elapsed_time(ev[k + 1][0]) for k in range(K - 1)] or [0.0]
     q_avg_us = 1e3 * float(np.mean(q_ms))
     q_gbps = qbytes / (q_avg_us * 1e-6) / 1e9
-    log("two-launch step %.3f ms (device %.3f ms, host enqueue %.1f us); quantize avg %.2f us "
-        "(median %.2f) = %.1f GB/s; update + gaps avg %.2f us" % (
-            two_ms_per_step, region2[0].elapsed_time(region2[1]) / K,
-            (t2_enq - t2) * 1e6 / K, q_avg_us,
-            1e3 * float(np.median(q_ms)), q_gbps, 1e3 * float(np.mean(u_ms))))
-    two_launch = {"ms_per_step": round(two_ms_per_step, 5),
-                  "host_enqueue_us_per_step": round((t2_enq - t2) * 1e6 / K, 2),
-                  "device_ms_per_step": round(region2[0].elapsed_time(region2[1]) / K, 5),
-                  "value_gbps": round((qbytes + ubytes) / (two_ms_per_step * 1e-3) / 1e9, 2),
-                  "update_and_gaps_us": round(1e3 * float(np.mean(u_ms)), 3)}
+    log("step %.4f ms (device %.4f ms, host enqueue %.1f us); quantize avg %.2f us (median "
+        "%.2f) = %.1f GB/s; update + gaps avg %.2f us" % (
+            ms_per_step, dev_ms_per_step, enq_us, q_avg_us, 1e3 * float(np.median(q_ms)),
+            q_gbps, 1e3 * float(np.mean(u_ms))))
+
+    # The same K steps in one launch each (fp8_quantize_amax_and_update), timed the same
+    # two ways.
+    one_ms, one_dev_ms, one_enq_us = steps_region(lambda k: one_launch_step())
+    ev1 = make_events()
+    steps_region(lambda k: one_launch_step(ev1[k]))
+    s_ms = [ev1[k][0].elapsed_time(ev1[k][1]) for k in range(K)]
+    s_avg_us = 1e3 * float(np.mean(s_ms))
+    s_gbps = (qbytes + ubytes) / (s_avg_us * 1e-6) / 1e9
+    log("one-launch step %.4f ms (device %.4f ms, host enqueue %.1f us); kernel avg %.2f us "
+        "(median %.2f) = %.1f GB/s" % (one_ms, one_dev_ms, one_enq_us, s_avg_us,
+                                       1e3 * float(np.median(s_ms)), s_gbps))
+    one_launch = {"entry": "fp8_quantize_amax_and_update (quantize + amax + update, one "
+                           "launch)",
+                  "ms_per_step": round(one_ms, 5), "device_ms_per_step": round(one_dev_ms, 5),
+                  "host_enqueue_us_per_step": round(one_enq_us, 2),
+                  "value_gbps": round((qbytes + ubytes) / (one_ms * 1e-3) / 1e9, 2),
+                  "kernel_avg_us": round(s_avg_us, 3),
+                  "kernel_median_us": round(1e3 * float(np.median(s_ms)), 3),
+                  "kernel_gbps": round(s_gbps, 1)}
 
     # ------------------------------------------------------------ batched update, 1152 tensors
     uw = workloads.update_1152(threads=threads)
@@ -542,27 +545,18 @@ def main():
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
-        "device_ms_per_step": round(region_ms / K, 5),
-        "host_enqueue_us_per_step": round((t_enq - t_start) * 1e6 / K, 2),
+        "device_ms_per_step": round(dev_ms_per_step, 5),
+        "host_enqueue_us_per_step": round(enq_us, 2),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
         "data": "synthetic (seeded numpy PCG64, seed 12; shapes/distributions of the workload)",
         "config": {"workload": w.name, "description": w.description, "tensors": n,
                    "elements": w.numel, "history_len": w.history_len,
                    "formats": [t.fmt for t in w.tensors], "src_dtype": "bf16",
                    "rotating_input_sets": args.rotate},
-        "step_kernel": {"entry": "fp8_quantize_amax_and_update (quantize + amax + update, "
-                                 "one launch)",
-                        "timing": "HIP events set to each launch's kernel start/stop "
-                                  "(hipExtLaunchKernel), every timed step",
-                        "avg_us": round(s_avg_us, 3),
-                        "median_us": round(1e3 * float(np.median(s_ms)), 3),
-                        "gbps": round(s_gbps, 1),
-                        "pct_hbm_peak": round(100 * s_gbps / PEAK_HBM_GBPS, 2),
-                        "alg_bytes": qbytes + ubytes},
-        "two_launch_step": two_launch,
-        "quantize_amax": {"entry": "fp8_multi_quantize_amax (two-launch step)",
+        "one_launch_step": one_launch,
+        "quantize_amax": {"entry": "fp8_multi_quantize_amax",
                           "timing": "HIP events set to each launch's kernel start/stop "
-                                    "(hipExtLaunchKernel), every timed step",
+                                    "(hipExtLaunchKernel), every step of the second region",
                           "avg_us": round(q_avg_us, 3),
                           "median_us": round(1e3 * float(np.median(q_ms)), 3),
                           "gbps": round(q_gbps, 1), "pct_hbm_peak": round(100 * q_gbps /
@@ -577,7 +571,8 @@ def main():
                             "host_wall_us_per_call": round(wall_us, 3),
                             "torch_ops_per_module_us_per_update": (
                                 round(torch_ops_us, 1) if torch_ops_us else None),
-                            "alg_bytes": alg_bytes_update(un, uH)},
+                            "alg_bytes": alg_bytes_update(un, uH),
+                            "step_update_and_gaps_us": round(1e3 * float(np.mean(u_ms)), 3)},
         "dequantize": {"tensor": w.tensors[big].name, "elements": int(w.tensors[big].data.size),
                        "out": "bf16", "events_median_us": round(dq_us, 3),
                        "gbps": round(dq_bytes / (dq_us * 1e-6) / 1e9, 1)},
@@ -585,9 +580,9 @@ def main():
         "layernorm_quantize": ln_out,
         "fp8_gemm": gemm_out,
         "copy_d2d_gbps": round(copy_gbps, 1),
-        "roofline": {"bound": "hbm", "kernel": STEP_KERNEL + " (one-launch step)",
-                     "achieved": round(s_gbps, 1), "peak": PEAK_HBM_GBPS,
-                     "unit": "GB/s", "frac": round(s_gbps / PEAK_HBM_GBPS, 4),
+        "roofline": {"bound": "hbm", "kernel": ROOFLINE_KERNEL + " (fp8_multi_quantize_amax)",
+                     "achieved": round(q_gbps, 1), "peak": PEAK_HBM_GBPS,
+                     "unit": "GB/s", "frac": round(q_gbps / PEAK_HBM_GBPS, 4),
                      "traffic": traffic},
     }
 
