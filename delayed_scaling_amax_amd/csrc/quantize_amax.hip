@@ -697,14 +697,13 @@ __device__ void update_in_block(const QUpdate& u, uint32_t* colmax) {
   const int64_t H = u.H, span = (int64_t)groups * kR;
   uint32_t* hist = (uint32_t*)u.hist;
   // thread t < n: tensor t's inputs, fetched now so their latency overlaps the history's
-  uint32_t ab = 0u, fmt = 0u;
-  float s_old = 0.0f;
-  if (tid < n) {
-    ab = __hip_atomic_load((uint32_t*)u.amax + tid, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    s_old = u.scale[tid];
-    fmt = u.formats[tid];
-    colmax[tid] = 0u;
-  }
+  // (every lane loads, lanes past n tensor 0's, so no merge waits for the loads)
+  const int tt = tid < n ? tid : 0;
+  const uint32_t ab =
+      __hip_atomic_load((uint32_t*)u.amax + tt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const float s_old = u.scale[tt];
+  uint32_t fmt = u.formats[tt];
+  if (tid < n) colmax[tid] = 0u;
   uint32_t m = 0u;
   for (int64_t d_hi = H; d_hi > 1; d_hi -= span) {
     const int64_t d_lo = d_hi - span > 1 ? d_hi - span : 1;
@@ -735,6 +734,9 @@ __device__ void update_in_block(const QUpdate& u, uint32_t* colmax) {
     uint32_t sel_bits = colmax[tid] > ab ? colmax[tid] : ab;
     if (u.algo == FP8Q_AMAX_MOST_RECENT) sel_bits = ab;
     hist[tid] = ab;  // row 0; loaded (as the source of row 1) before the last barrier
+    // opaque rebind (no instruction): without it the compiler tests fmt right after its
+    // load, which makes the history loads wait for that load first
+    asm volatile("" : "+v"(fmt));
     const float s = next_scale(sel_bits, fmt, s_old, u.margin);
     u.scale[tid] = s;
     u.scale_inv[tid] = 1.0f / s;

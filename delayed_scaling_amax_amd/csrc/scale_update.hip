@@ -105,14 +105,12 @@ __global__ __launch_bounds__(kUBlock) void amax_and_scale_update_kernel(
   const int rr = tid / kUTpr;       // row within a pass
   const int cl = 4 * lc;            // first column (local) of this thread
 
-  // per-tensor inputs, fetched now so their latency overlaps the history loads
-  float a_in = 0.0f, s_old = 0.0f;
-  uint32_t fmt = 0;
-  if (tid < ncols) {
-    a_in = amax[c0 + tid];
-    s_old = scale[c0 + tid];
-    fmt = formats[c0 + tid];
-  }
+  // per-tensor inputs, fetched now so their latency overlaps the history loads (every
+  // lane loads, lanes past ncols the group's first tensor, so no merge waits for them)
+  const int64_t ct = c0 + (tid < ncols ? tid : 0);
+  const float a_in = amax[ct];
+  const float s_old = scale[ct];
+  uint32_t fmt = formats[ct];
 
   const __amdgpu_buffer_rsrc_t rh = __builtin_amdgcn_make_buffer_rsrc(
       hist, (short)0, (int)(kVec ? H * n * 4 : 0), 0x00020000);
@@ -164,6 +162,9 @@ __global__ __launch_bounds__(kUBlock) void amax_and_scale_update_kernel(
     for (int w = 0; w < kUBlock / 64; ++w) sel_bits = sel_bits > red[w][tid] ? sel_bits : red[w][tid];
     hist[t] = a_in;  // row 0; row 0 was loaded (as source of row 1) before the last barrier
     if (algo == FP8Q_AMAX_MOST_RECENT) sel_bits = ab;
+    // opaque rebind (no instruction): without it the compiler tests fmt right after its
+    // load, which makes every history load wait for that load first
+    asm volatile("" : "+v"(fmt));
     const float s = next_scale(sel_bits, fmt, s_old, margin);
     scale[t] = s;
     scale_inv[t] = 1.0f / s;
