@@ -372,7 +372,7 @@ void ln_quantize_kernel(const LnArgs a) {
   m = wave_max_u32(m);
   if (lane == 0 && m != 0) atomicMax(&block_amax, m);
   __syncthreads();
-  if (threadIdx.x == 0 && block_amax != 0) atomicMax(a.amax, block_amax);
+  if (threadIdx.x == 0 && block_amax != 0) amax_accumulate(a.amax, block_amax);
 }
 
 // ---------------------------------------------------------------- host side

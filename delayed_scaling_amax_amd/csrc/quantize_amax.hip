@@ -14,8 +14,9 @@
 //    one contiguous window of memory; a block issues one amax atomic per tensor.
 //  * amax is an integer max: |x| is the bit pattern with the sign cleared (bf16: two
 //    halves at once with v_pk_max_u16), reduced lane -> wavefront -> block, then one
-//    atomicMax on the binary32 bit pattern.  Non-negative floats order like their
-//    bits, NaN above inf, so the result does not depend on atomic order.
+//    atomicMax on the binary32 bit pattern (skipped when amax already holds as much).
+//    Non-negative floats order like their bits, NaN above inf, so the result does not
+//    depend on atomic order.
 //  * Division.  r = RN(1/scale) once per tensor (IEEE).  Per element the quotient is
 //    q0 = RN(x*r) corrected by Markstein's step (q = q0 - (q0*s - x)*r as two FMAs;
 //    twice for fp32 sources), which equals the IEEE quotient while scale is in
@@ -662,8 +663,8 @@ __device__ __forceinline__ void phase2_entry(const QTable& tab, QShared& sh, int
 
 // ---------------------------------------------------------------- appended update
 // Whether this block is the last of the grid to finish.  Every thread's amax atomic is
-// performed before the block counts itself, so the last block sees every block's
-// contribution.  Only device-scope atomics have to be ordered here (the amax maxima and
+// performed (or skipped because amax already held as much) before the block counts
+// itself, so the last block sees every block's contribution.  Only device-scope atomics have to be ordered here (the amax maxima and
 // the count), so waiting for the atomics to complete is enough: a device-scope fence
 // would write back and invalidate the XCD's L2 in every block.  Contains barriers:
 // every thread of the block calls it once.
@@ -773,7 +774,7 @@ __global__ __launch_bounds__(kQBlock) void quantize_amax_kernel(const QTable tab
   }
   __syncthreads();
   // one global atomic per tensor this block saw a non-zero |x| in
-  if (tid < n && sh.amax[tid] != 0) atomicMax(tab.e[tid].amax, sh.amax[tid]);
+  if (tid < n && sh.amax[tid] != 0) amax_accumulate(tab.e[tid].amax, sh.amax[tid]);
   if constexpr (kUpd) {
     __shared__ uint32_t colmax[kQUpdMaxCols];
     if (finished_last(tab.upd.counter, sh)) update_in_block(tab.upd, colmax);
