@@ -208,3 +208,20 @@ def test_timed_events_cover_the_fused_kernel(orc):
     # and the step's results are the oracle's (the same call once more, checked)
     st2 = Step(xs, [E4M3, E4M3], 16)
     st2.run(orc)
+
+
+def test_one_workspace_across_grid_sizes(orc):
+    """The same workspace through calls whose launches have 1, 64 and 512 blocks (and a
+    two-launch form in between): every call is bit-exact and leaves the counter at 0."""
+    import delayed_scaling_amax_amd as d
+    g = np.random.Generator(np.random.PCG64(9700))
+    ws = torch.zeros(1, dtype=torch.int32, device="cuda")
+    cases = [[bf16(g, 100)], [bf16(g, 1 << 20)], [bf16(g, 1 << 24), bf16(g, 777)],
+             [bf16(g, 50) for _ in range(40)], [bf16(g, 3000, 5.0)]]
+    note("fused step: one workspace across grid sizes")
+    for xs in cases:
+        st = Step(xs, [i % 2 for i in range(len(xs))], 8)
+        st.ws = ws  # shared
+        for _ in range(2):
+            st.run(orc)
+        assert int(ws.item()) == 0
