@@ -127,6 +127,8 @@ def main():
     ap.add_argument("--rotate", type=int, default=3,
                     help="input/output sets used in turn by successive steps")
     args = ap.parse_args()
+    if args.steps < 1 or args.warmup < 0 or args.rotate < 1 or args.update_calls < 1:
+        ap.error("--steps, --rotate and --update-calls must be >= 1, --warmup >= 0")
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (the amax "
               "all-reduce across replicas is described in the design notes, not built); "

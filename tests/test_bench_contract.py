@@ -41,3 +41,9 @@ def test_algorithmic_bytes():
     # scale_inv write, one format byte per tensor
     n, H = 1152, 1024
     assert b.alg_bytes_update(n, H) == 2 * H * n * 4 + 8 * n + 8 * n + 4 * n + n == 9461376
+
+
+def test_rejects_empty_timed_region():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--steps", "0"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2 and "--steps" in r.stderr and r.stdout == ""
