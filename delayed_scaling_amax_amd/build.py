@@ -15,11 +15,16 @@ ARCH = "gfx950"
 
 # -ffp-contract=off: every binary32 step is the one written (the kernels spell out
 #   their FMAs); -fhip-fp32-correctly-rounded-divide-sqrt: '/' is the IEEE division;
-# -packed-fp32-ops off: no v_pk_{add,mul,fma}_f32 in the generated code.
+# -packed-fp32-ops off: no v_pk_{add,mul,fma}_f32 in the generated code;
+# -instcombine-max-copied-from-constant-users: the kernels read their argument table in
+#   place only if the optimiser follows every use of it; the largest instance (mixed
+#   sources with the appended update) has more uses than it follows by default (300 is
+#   also too few), which leaves a 3.2 KB copy of the table on the stack.
 HIP_FLAGS = [
     "--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-Wall",
     "-ffp-contract=off", "-fhip-fp32-correctly-rounded-divide-sqrt",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-mllvm", "-instcombine-max-copied-from-constant-users=4096",
 ]
 
 

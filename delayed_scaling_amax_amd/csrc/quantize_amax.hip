@@ -93,6 +93,10 @@ constexpr int kQPass = FP8Q_Q_PASS;    // bf16 groups per pass (fp32: half)
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
+// s_waitcnt immediate for vmcnt(0) alone (gfx9 encoding: expcnt and lgkmcnt at their
+// maxima, so only vector memory operations are waited for).
+constexpr int kVmcnt0 = 0x0F70;
+
 // Buffer resource over [base, base + bytes) (raw, dword-granular, no swizzle).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
@@ -397,7 +401,7 @@ __device__ __forceinline__ void run_full_chunks(const QTable& tab, QShared& sh, 
   const Owned own = owned_chunks(f0, f1);
   int64_t j = own.first;
   int t = t_begin;
-  auto settle = [&](int& tt, int64_t& jj) {  // move (tt, jj) to a chunk this phase does
+  auto settle = [&](int& tt, int64_t& jj) __attribute__((always_inline)) {  // move (tt, jj) to a chunk this phase does
     while (tt < t_end) {
       const int64_t end = tab.e[tt].fbegin + tab.e[tt].nfull;
       if (jj >= own.limit) {
@@ -420,7 +424,7 @@ __device__ __forceinline__ void run_full_chunks(const QTable& tab, QShared& sh, 
     int64_t fbegin;     // first full chunk
     int64_t fend;       // one past the last full chunk
   };
-  auto view = [&](int tt) {
+  auto view = [&](int tt) __attribute__((always_inline)) {
     TensorView v;
     v.in = (const uint4*)((const char*)tab.e[tt].src + tab.e[tt].head * esz);
     v.out = (uint2*)(tab.e[tt].dst + tab.e[tt].head);
@@ -432,9 +436,13 @@ __device__ __forceinline__ void run_full_chunks(const QTable& tab, QShared& sh, 
   struct Pass {
     uint4 w[kU][kL];
   };
-  auto load_pass = [&](Pass& P, const TensorView& v, int64_t jj, int pp) {
+  // live == false: the same loads through an empty descriptor (no memory access, zeros
+  // returned), for a slot past the end of the run.
+  auto load_pass = [&](Pass& P, const TensorView& v, int64_t jj, int pp,
+                       bool live) __attribute__((always_inline)) {
     const int64_t unit0 = (jj - v.fbegin) * kQChunk + pp * kU * kQBlock;
-    const __amdgpu_buffer_rsrc_t rin = buffer_rsrc(v.in + unit0 * kL, kU * kQBlock * kL * 16);
+    const __amdgpu_buffer_rsrc_t rin =
+        buffer_rsrc(v.in + unit0 * kL, live ? kU * kQBlock * kL * 16 : 0);
 #pragma unroll
     for (int u = 0; u < kU; ++u)
 #pragma unroll
@@ -454,7 +462,7 @@ __device__ __forceinline__ void run_full_chunks(const QTable& tab, QShared& sh, 
     int p;
     TensorView v;
   };
-  auto advance = [&](const Slot& a) {  // the pass after a (t == t_end: none)
+  auto advance = [&](const Slot& a) __attribute__((always_inline)) {  // the pass after a (t == t_end: none)
     Slot n = a;
     if (++n.p == kP) {
       n.p = 0;
@@ -467,107 +475,143 @@ __device__ __forceinline__ void run_full_chunks(const QTable& tab, QShared& sh, 
     return n;
   };
 
-  // kD passes are in flight ahead of the one being converted
-  Pass buf[kD + 1];
-  Slot pos[kD + 1];
+  // kD passes are in flight ahead of the one being converted, in a ring of kD + 1 pass
+  // buffers that the loop below walks with constant indexes (no register copies).  Every
+  // pass issues the same loads and stores -- the loads of a slot past the end go through
+  // an empty descriptor, and the set-up issues empty stand-ins for the stores of the
+  // passes it loads -- so the vmcnt wait the compiler places before each group is the
+  // same on every path into it and covers that group's loads only.  (A load under a
+  // branch, or a copy of a buffer still being loaded, makes it wait for the passes
+  // behind as well.)
+  constexpr int kR = kD + 1;
+  constexpr int kS = kQPair ? kU / 2 : kU;  // stores per pass
+  auto stand_in_stores = [&](const TensorView& v) __attribute__((always_inline)) {
+    const __amdgpu_buffer_rsrc_t rnull = buffer_rsrc(v.out, 0);
+#pragma unroll
+    for (int q = 0; q < kS; ++q) {
+      if constexpr (kQPair)
+        buffer_store16(rnull, tid * 16, q * kQBlock * 16, make_uint2(0, 0), make_uint2(0, 0));
+      else
+        buffer_store8(rnull, tid * 8, q * kQBlock * 8, make_uint2(0, 0));
+    }
+  };
+  Pass buf[kR];
+  Slot pos[kR];
   int ts = t_begin;  // speculative first position: chunk ranges only
   int64_t js = j;
   if (setup) {
     while (ts < t_end && js < own.limit && js >= tab.e[ts].fbegin + tab.e[ts].nfull) ++ts;
     if (js >= own.limit) ts = t_end;
-    if (ts < t_end) load_pass(buf[0], view(ts), js, 0);
+    if (ts < t_end) load_pass(buf[0], view(ts), js, 0, true);
     setup_shared(tab, sh);
   }
   settle(t, j);
   if (t >= t_end) return;
   pos[0] = Slot{t, j, 0, view(t)};
-  if (!setup || ts != t || js != j) load_pass(buf[0], pos[0].v, pos[0].j, pos[0].p);
+  if (!setup) {
+    load_pass(buf[0], pos[0].v, pos[0].j, pos[0].p, true);
+  } else if (ts != t || js != j) {  // rare: the speculative pass is not this block's first
+    // Let the speculative loads land before the reload, so that no path reaches the loop
+    // with them in flight (the waits in the loop would then cover them too).
+    __builtin_amdgcn_s_waitcnt(kVmcnt0);
+    load_pass(buf[0], pos[0].v, pos[0].j, pos[0].p, true);
+  }
+  stand_in_stores(pos[0].v);
 #pragma unroll
   for (int d = 1; d < kD; ++d) {
     pos[d] = pos[d - 1].t < t_end ? advance(pos[d - 1]) : pos[d - 1];
-    if (pos[d].t < t_end) load_pass(buf[d], pos[d].v, pos[d].j, pos[d].p);
+    load_pass(buf[d], pos[d].v, pos[d].j, pos[d].p, pos[d].t < t_end);
+    stand_in_stores(pos[d].v);
   }
   float s = uniform(sh.scale[t]), r = uniform(sh.rcp[t]);
   uint32_t xlim = uniform(sh.xlim[t]);
   uint32_t acc = 0;
+  // The loop leaves only at the end of the ring.  When a run ends partway round, the
+  // rest of the ring runs as dead passes: their loads are empty (zeros), their stores go
+  // through an empty descriptor and are dropped, and they flush no amax.  An exit from
+  // within the ring would give the loop head a second way in, with that pass's
+  // look-ahead loads in flight, and the waits in the loop would have to cover it.
   for (;;) {
-    Slot& c = pos[0];
-    Slot& last = pos[kD - 1];
-    pos[kD] = last.t < t_end ? advance(last) : last;
-    if (pos[kD].t < t_end)
-      load_pass(buf[kD], pos[kD].v, pos[kD].j, pos[kD].p);
-    // the next passes' loads are issued; keep them ahead of this pass's arithmetic
-    __builtin_amdgcn_sched_barrier(0);
-    Pass& cur = buf[0];
-    const __amdgpu_buffer_rsrc_t rout = buffer_rsrc(
-        c.v.out + (c.j - c.v.fbegin) * kQChunk + c.p * kU * kQBlock, kU * kQBlock * 8);
-    uint2 o[kU];
-    uint32_t pm = 0;  // pass magnitude max
+    bool more = false;
 #pragma unroll
-    for (int u = 0; u < kU; ++u) {
-      if constexpr (kBF16) {
-        uint32_t mg;
-        if constexpr (kGelu) {
-          // the magnitude max feeds both the amax and the test for NaN outputs
-          const uint4 x = cur.w[u][0];
-          cur.w[u][0] = gelu8_unpatched(x);
-          mg = mag8_bf16(cur.w[u][0]);
-          if (__builtin_amdgcn_ballot_w64(halves_nan(mg) != 0) != 0) {
-            cur.w[u][0] = gelu8_patch(x, cur.w[u][0]);
+    for (int k = 0; k < kR; ++k) {
+      const Slot& c = pos[k];
+      const bool real = k == 0 || c.t < t_end;  // the head of the ring is always real
+      const Slot& last = pos[(k + kD - 1) % kR];
+      Slot& ahead = pos[(k + kD) % kR];
+      ahead = last.t < t_end ? advance(last) : last;
+      load_pass(buf[(k + kD) % kR], ahead.v, ahead.j, ahead.p, ahead.t < t_end);
+      // the next passes' loads are issued; keep them ahead of this pass's arithmetic
+      __builtin_amdgcn_sched_barrier(0);
+      Pass& cur = buf[k];
+      const __amdgpu_buffer_rsrc_t rout =
+          buffer_rsrc(c.v.out + (c.j - c.v.fbegin) * kQChunk + c.p * kU * kQBlock,
+                      real ? kU * kQBlock * 8 : 0);
+      uint2 o[kU];
+      uint32_t pm = 0;  // pass magnitude max
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        if constexpr (kBF16) {
+          uint32_t mg;
+          if constexpr (kGelu) {
+            // the magnitude max feeds both the amax and the test for NaN outputs
+            const uint4 x = cur.w[u][0];
+            cur.w[u][0] = gelu8_unpatched(x);
+            mg = mag8_bf16(cur.w[u][0]);
+            if (__builtin_amdgcn_ballot_w64(halves_nan(mg) != 0) != 0) {
+              cur.w[u][0] = gelu8_patch(x, cur.w[u][0]);
+              mg = mag8_bf16(cur.w[u][0]);
+            }
+          } else {
             mg = mag8_bf16(cur.w[u][0]);
           }
+          pm = pk_max_u16(pm, mg);
+          o[u] = codes8_bf16<kFmt>(cur.w[u][0], s, r);
         } else {
-          mg = mag8_bf16(cur.w[u][0]);
+          const uint32_t m = mag8_f32(cur.w[u][0], cur.w[u][kL - 1]);
+          pm = pm > m ? pm : m;
+          o[u] = codes8_f32<kFmt>(cur.w[u][0], cur.w[u][kL - 1], s, r);
         }
-        pm = pk_max_u16(pm, mg);
-        o[u] = codes8_bf16<kFmt>(cur.w[u][0], s, r);
+      }
+      if constexpr (kBF16) {
+        acc = pk_max_u16(acc, pm);
+        if (max_halves(pm) >= xlim) {  // rare: inf/NaN or a quotient far beyond FP8
+#pragma unroll
+          for (int u = 0; u < kU; ++u)
+            if (max_halves(mag8_bf16(cur.w[u][0])) >= xlim)
+              o[u] = patch8_bf16<kFmt>(o[u], cur.w[u][0], xlim);
+        }
       } else {
-        const uint32_t m = mag8_f32(cur.w[u][0], cur.w[u][kL - 1]);
-        pm = pm > m ? pm : m;
-        o[u] = codes8_f32<kFmt>(cur.w[u][0], cur.w[u][kL - 1], s, r);
+        acc = acc > pm ? acc : pm;
+        if (pm >= xlim) {
+#pragma unroll
+          for (int u = 0; u < kU; ++u)
+            if (mag8_f32(cur.w[u][0], cur.w[u][kL - 1]) >= xlim)
+              o[u] = patch8_f32<kFmt>(o[u], cur.w[u][0], cur.w[u][kL - 1], xlim);
+        }
+      }
+      if constexpr (kQPair) {
+        static_assert(kU % 2 == 0, "units pair up within a pass");
+#pragma unroll
+        for (int q = 0; q < kU / 2; ++q)
+          buffer_store16(rout, tid * 16, q * kQBlock * 16, o[2 * q], o[2 * q + 1]);
+      } else {
+#pragma unroll
+        for (int u = 0; u < kU; ++u) buffer_store8(rout, tid * 8, u * kQBlock * 8, o[u]);
+      }
+      const Slot& nx = pos[(k + 1) % kR];
+      more = nx.t < t_end;  // uniform
+      if (real && (!more || nx.t != c.t)) {
+        flush_amax<kBF16>(acc, sh, c.t);
+        acc = 0;
+        if (more) {
+          s = uniform(sh.scale[nx.t]);
+          r = uniform(sh.rcp[nx.t]);
+          xlim = uniform(sh.xlim[nx.t]);
+        }
       }
     }
-    if constexpr (kBF16) {
-      acc = pk_max_u16(acc, pm);
-      if (max_halves(pm) >= xlim) {  // rare: inf/NaN or a quotient far beyond FP8
-#pragma unroll
-        for (int u = 0; u < kU; ++u)
-          if (max_halves(mag8_bf16(cur.w[u][0])) >= xlim)
-            o[u] = patch8_bf16<kFmt>(o[u], cur.w[u][0], xlim);
-      }
-    } else {
-      acc = acc > pm ? acc : pm;
-      if (pm >= xlim) {
-#pragma unroll
-        for (int u = 0; u < kU; ++u)
-          if (mag8_f32(cur.w[u][0], cur.w[u][kL - 1]) >= xlim)
-            o[u] = patch8_f32<kFmt>(o[u], cur.w[u][0], cur.w[u][kL - 1], xlim);
-      }
-    }
-    if constexpr (kQPair) {
-      static_assert(kU % 2 == 0, "units pair up within a pass");
-#pragma unroll
-      for (int q = 0; q < kU / 2; ++q)
-        buffer_store16(rout, tid * 16, q * kQBlock * 16, o[2 * q], o[2 * q + 1]);
-    } else {
-#pragma unroll
-      for (int u = 0; u < kU; ++u) buffer_store8(rout, tid * 8, u * kQBlock * 8, o[u]);
-    }
-    const Slot& nx = pos[1];
-    const bool more = nx.t < t_end;  // uniform
-    if (!more || nx.t != c.t) {
-      flush_amax<kBF16>(acc, sh, c.t);
-      acc = 0;
-      if (!more) break;
-      s = uniform(sh.scale[nx.t]);
-      r = uniform(sh.rcp[nx.t]);
-      xlim = uniform(sh.xlim[nx.t]);
-    }
-#pragma unroll
-    for (int d = 0; d < kD; ++d) {
-      buf[d] = buf[d + 1];
-      pos[d] = pos[d + 1];
-    }
+    if (!more) return;
   }
 }
 
