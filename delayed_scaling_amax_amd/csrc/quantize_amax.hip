@@ -82,12 +82,10 @@ constexpr int kQChunk = kQBlock * kQUnroll;       // units (8-element groups) pe
 #define FP8Q_Q_PAIR 1
 #endif
 constexpr bool kQPair = FP8Q_Q_PAIR != 0;
-constexpr int kQDepth = FP8Q_Q_DEPTH;  // passes in flight ahead of the one being converted
-#ifndef FP8Q_Q_GELU_DEPTH
-#define FP8Q_Q_GELU_DEPTH 2
-#endif
-// the arithmetic-bound gelu instance keeps two passes in flight (one: ~7% slower)
-constexpr int kQGeluDepth = FP8Q_Q_GELU_DEPTH;
+// Passes in flight ahead of the one being converted.  One is enough for every instance
+// (the gelu one included) once the waits cover only the pass being converted: two were
+// 1-2% slower on the plain quantize of a 0.5 GB step and 2% on the gelu one.
+constexpr int kQDepth = FP8Q_Q_DEPTH;
 constexpr int kQPass = FP8Q_Q_PASS;    // bf16 groups per pass (fp32: half)
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -387,7 +385,7 @@ __device__ __forceinline__ void elementwise_units(const void* __restrict__ src,
 template <bool kBF16, int kFmt, bool kGelu>
 __device__ __forceinline__ void run_full_chunks(const QTable& tab, QShared& sh, int t_begin,
                                                 int t_end, bool setup) {
-  constexpr int kD = kGelu ? kQGeluDepth : kQDepth;  // passes in flight ahead
+  constexpr int kD = kQDepth;  // passes in flight ahead
   constexpr int kL = kBF16 ? 1 : 2;                // 16-byte loads per group
   constexpr int kU = kBF16 ? kQPass : kQPass / 2;  // groups per pass
   constexpr int kP = kQUnroll / kU;                // passes per chunk
@@ -527,8 +525,9 @@ __device__ __forceinline__ void run_full_chunks(const QTable& tab, QShared& sh, 
   uint32_t xlim = uniform(sh.xlim[t]);
   uint32_t acc = 0;
   // The loop leaves only at the end of the ring.  When a run ends partway round, the
-  // rest of the ring runs as dead passes: their loads are empty (zeros), their stores go
-  // through an empty descriptor and are dropped, and they flush no amax.  An exit from
+  // rest of the ring runs as dead passes: their loads are empty (zeros), they do no
+  // arithmetic, their stores go through an empty descriptor and are dropped, and they
+  // flush no amax.  An exit from
   // within the ring would give the loop head a second way in, with that pass's
   // look-ahead loads in flight, and the waits in the loop would have to cover it.
   for (;;) {
@@ -547,47 +546,52 @@ __device__ __forceinline__ void run_full_chunks(const QTable& tab, QShared& sh, 
       const __amdgpu_buffer_rsrc_t rout =
           buffer_rsrc(c.v.out + (c.j - c.v.fbegin) * kQChunk + c.p * kU * kQBlock,
                       real ? kU * kQBlock * 8 : 0);
-      uint2 o[kU];
-      uint32_t pm = 0;  // pass magnitude max
+      // A dead pass skips the arithmetic (vector ALU only: the memory operations are the
+      // same on both sides of this branch) and stores its zero codes through the empty
+      // descriptor.
+      uint2 o[kU] = {};
+      if (real) {
+        uint32_t pm = 0;  // pass magnitude max
 #pragma unroll
-      for (int u = 0; u < kU; ++u) {
-        if constexpr (kBF16) {
-          uint32_t mg;
-          if constexpr (kGelu) {
-            // the magnitude max feeds both the amax and the test for NaN outputs
-            const uint4 x = cur.w[u][0];
-            cur.w[u][0] = gelu8_unpatched(x);
-            mg = mag8_bf16(cur.w[u][0]);
-            if (__builtin_amdgcn_ballot_w64(halves_nan(mg) != 0) != 0) {
-              cur.w[u][0] = gelu8_patch(x, cur.w[u][0]);
+        for (int u = 0; u < kU; ++u) {
+          if constexpr (kBF16) {
+            uint32_t mg;
+            if constexpr (kGelu) {
+              // the magnitude max feeds both the amax and the test for NaN outputs
+              const uint4 x = cur.w[u][0];
+              cur.w[u][0] = gelu8_unpatched(x);
+              mg = mag8_bf16(cur.w[u][0]);
+              if (__builtin_amdgcn_ballot_w64(halves_nan(mg) != 0) != 0) {
+                cur.w[u][0] = gelu8_patch(x, cur.w[u][0]);
+                mg = mag8_bf16(cur.w[u][0]);
+              }
+            } else {
               mg = mag8_bf16(cur.w[u][0]);
             }
+            pm = pk_max_u16(pm, mg);
+            o[u] = codes8_bf16<kFmt>(cur.w[u][0], s, r);
           } else {
-            mg = mag8_bf16(cur.w[u][0]);
+            const uint32_t m = mag8_f32(cur.w[u][0], cur.w[u][kL - 1]);
+            pm = pm > m ? pm : m;
+            o[u] = codes8_f32<kFmt>(cur.w[u][0], cur.w[u][kL - 1], s, r);
           }
-          pm = pk_max_u16(pm, mg);
-          o[u] = codes8_bf16<kFmt>(cur.w[u][0], s, r);
+        }
+        if constexpr (kBF16) {
+          acc = pk_max_u16(acc, pm);
+          if (max_halves(pm) >= xlim) {  // rare: inf/NaN or a quotient far beyond FP8
+#pragma unroll
+            for (int u = 0; u < kU; ++u)
+              if (max_halves(mag8_bf16(cur.w[u][0])) >= xlim)
+                o[u] = patch8_bf16<kFmt>(o[u], cur.w[u][0], xlim);
+          }
         } else {
-          const uint32_t m = mag8_f32(cur.w[u][0], cur.w[u][kL - 1]);
-          pm = pm > m ? pm : m;
-          o[u] = codes8_f32<kFmt>(cur.w[u][0], cur.w[u][kL - 1], s, r);
-        }
-      }
-      if constexpr (kBF16) {
-        acc = pk_max_u16(acc, pm);
-        if (max_halves(pm) >= xlim) {  // rare: inf/NaN or a quotient far beyond FP8
+          acc = acc > pm ? acc : pm;
+          if (pm >= xlim) {
 #pragma unroll
-          for (int u = 0; u < kU; ++u)
-            if (max_halves(mag8_bf16(cur.w[u][0])) >= xlim)
-              o[u] = patch8_bf16<kFmt>(o[u], cur.w[u][0], xlim);
-        }
-      } else {
-        acc = acc > pm ? acc : pm;
-        if (pm >= xlim) {
-#pragma unroll
-          for (int u = 0; u < kU; ++u)
-            if (mag8_f32(cur.w[u][0], cur.w[u][kL - 1]) >= xlim)
-              o[u] = patch8_f32<kFmt>(o[u], cur.w[u][0], cur.w[u][kL - 1], xlim);
+            for (int u = 0; u < kU; ++u)
+              if (mag8_f32(cur.w[u][0], cur.w[u][kL - 1]) >= xlim)
+                o[u] = patch8_f32<kFmt>(o[u], cur.w[u][0], cur.w[u][kL - 1], xlim);
+          }
         }
       }
       if constexpr (kQPair) {
