@@ -38,14 +38,17 @@ namespace fp8q {
 #ifndef FP8Q_Q_BLOCK
 #define FP8Q_Q_BLOCK 256
 #endif
-// Chunks of 8 units per thread with one pass in flight ahead: measured against 16 units
-// and two passes, 1.5-2% faster on a 4 GB step and equal (within ~1%) on 0.5 GB; deeper
-// pipelines, smaller or larger chunks and 1 or 3 blocks per CU were no better.
+// Chunks of 8 units per thread with one pass in flight ahead and one block (four
+// wavefronts) per CU.  With the waits covering only the pass being converted, a wavefront
+// keeps a whole pass of loads in flight, and one block per CU is the fastest measured at
+// every size: against two, 701 vs 734 us on a 4 GB step, 89.3 vs 90.3 us on 0.5 GB, 6.75
+// vs 6.95 us on 3 x 1M elements (two blocks with the waits that also covered the
+// look-ahead: 708, 90.9 and 6.8 us).  16 units per thread were slower at every size.
 #ifndef FP8Q_Q_UNROLL
 #define FP8Q_Q_UNROLL 8
 #endif
 #ifndef FP8Q_Q_BLOCKS_PER_CU
-#define FP8Q_Q_BLOCKS_PER_CU 2
+#define FP8Q_Q_BLOCKS_PER_CU 1
 #endif
 // Cache policy of the streaming body (gfx950 buffer-op aux bits: 1 = sc0, 2 = nt,
 // 16 = sc1).  Measured on the read-16B/write-8B shape of this kernel: non-temporal
@@ -62,9 +65,10 @@ constexpr int kQUnroll = FP8Q_Q_UNROLL;           // 8-element groups per thread
 constexpr int kQMaxEntries = 32;                  // tensors per launch (kernel-argument table)
 constexpr int kQBlocksPerCU = FP8Q_Q_BLOCKS_PER_CU;  // persistent grid size per CU
 #ifndef FP8Q_Q_GELU_BLOCKS_PER_CU
-#define FP8Q_Q_GELU_BLOCKS_PER_CU 3
+#define FP8Q_Q_GELU_BLOCKS_PER_CU 4
 #endif
-// the gelu instance is arithmetic-bound: more resident waves hide exp/rcp latency
+// the gelu instance is arithmetic-bound: more resident waves hide exp/rcp latency (4 blocks
+// per CU: 91.4 us on 8192 x 16384 bf16, against 93.6 with 3 and 95.6 with 2)
 constexpr int kQGeluBlocksPerCU = FP8Q_Q_GELU_BLOCKS_PER_CU;
 constexpr int kQChunk = kQBlock * kQUnroll;       // units (8-element groups) per chunk
 #ifndef FP8Q_Q_DEPTH

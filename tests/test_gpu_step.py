@@ -211,8 +211,9 @@ def test_timed_events_cover_the_fused_kernel(orc):
 
 
 def test_one_workspace_across_grid_sizes(orc):
-    """The same workspace through calls whose launches have 1, 64 and 512 blocks (and a
-    two-launch form in between): every call is bit-exact and leaves the counter at 0."""
+    """The same workspace through calls whose launches have 1 block, 64 blocks and the
+    full persistent grid (and a two-launch form in between): every call is bit-exact and
+    leaves the counter at 0."""
     import delayed_scaling_amax_amd as d
     g = np.random.Generator(np.random.PCG64(9700))
     ws = torch.zeros(1, dtype=torch.int32, device="cuda")
