@@ -77,13 +77,17 @@ constexpr int kQChunk = kQBlock * kQUnroll;       // units (8-element groups) pe
 #ifndef FP8Q_Q_PASS
 #define FP8Q_Q_PASS 4
 #endif
-// Unit-to-lane layout of a pass: 1 = a lane takes two adjacent units (32 contiguous bytes
-// of bf16, 64 of fp32) and writes their 16 code bytes with one store; 0 = a lane takes
-// one unit and writes 8 bytes.  Measured with 4 units per pass and 2 passes in flight:
-// 4.3% faster on a 4 GB step, 0.7% on 0.5 GB, against the 8-byte form with 8 units and 1
-// pass (a no-arithmetic probe of the paired traffic streams 6.1 TB/s against 5.6-5.8).
+// Unit-to-lane layout of a pass: 0 = lane l takes unit l of each 256-unit row of the
+// pass, so each 16-byte load instruction reads one contiguous 4 KB span (bf16; fp32: two
+// instructions per unit, 32-byte stride) and each lane writes 8 code bytes; 1 = a lane
+// takes two adjacent units (32 contiguous bytes of bf16, 64 of fp32: each load
+// instruction then reads every second or fourth 16-byte piece of its span) and writes
+// their 16 code bytes with one store.  With the waits covering only the pass being
+// converted and one block per CU, 0 is faster at every size measured: 0.5 GB bf16 step
+// 83.0 vs 89.4 us, 4 GB 694 vs 702 us, fp32 134M elements 115.5 vs 160.7 us, gelu 97.7
+// vs 99.0 us.  (1 was adopted when the waits also covered the look-ahead pass.)
 #ifndef FP8Q_Q_PAIR
-#define FP8Q_Q_PAIR 1
+#define FP8Q_Q_PAIR 0
 #endif
 constexpr bool kQPair = FP8Q_Q_PAIR != 0;
 // Passes in flight ahead of the one being converted.  One is enough for every instance
