@@ -150,6 +150,35 @@ def test_multi_tensor_mixed_and_shared_amax(orc):
     assert (bits(amax.cpu().numpy()) == bits(want_amax)).all()
 
 
+def test_out_of_window_tensors_inside_one_run(orc):
+    """One launch of five bf16 E4M3 tensors spanning several 16384-element chunks per
+    block, the first and the fourth with scales outside the division window (done
+    element-wise in the second phase): blocks whose first chunk lies in the first tensor
+    have their speculative first loads discarded and reload from the second, and the
+    pipeline skips the fourth tensor mid-run.  Codes and amaxes against the oracle."""
+    import delayed_scaling_amax_amd as d
+    sizes = [3_000_000, 5_000_123, 2_000_007, 4_000_000, 1_000_005]
+    scales = [2.0 ** -90, 0.37, 1.7, 3.0e38, 0.05]
+    note("out-of-window tensors inside one run")
+    entries, host = [], []
+    amax = torch.zeros(len(sizes), dtype=torch.float32, device="cuda")
+    sc = f32(scales)
+    for i, n in enumerate(sizes):
+        x = workloads.random_bf16(n, 700 + i, -12, 12)
+        dst = torch.empty(n, dtype=torch.uint8, device="cuda")
+        entries.append((dev_src(x), dst, sc[i:i + 1], amax[i:i + 1], E4M3))
+        host.append((x, dst))
+    d.fp8_multi_quantize_amax(entries)
+    torch.cuda.synchronize()
+    got_amax = amax.cpu().numpy()
+    for i, (x, dst) in enumerate(host):
+        want, wa = orc.quantize_amax(x, E4M3, float(np.float32(scales[i])),
+                                     threads=workloads.default_threads())
+        bad = np.flatnonzero(dst.cpu().numpy() != want)
+        assert bad.size == 0, (i, bad[:8], bad.size)
+        assert bits(got_amax[i]) == bits(wa), i
+
+
 def test_amax_max_accumulates_and_is_deterministic(orc):
     import delayed_scaling_amax_amd as d
     x1 = workloads.random_bf16(1 << 20, 31, -5, 5)
