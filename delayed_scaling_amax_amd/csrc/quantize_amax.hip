@@ -65,10 +65,11 @@ constexpr int kQUnroll = FP8Q_Q_UNROLL;           // 8-element groups per thread
 constexpr int kQMaxEntries = 32;                  // tensors per launch (kernel-argument table)
 constexpr int kQBlocksPerCU = FP8Q_Q_BLOCKS_PER_CU;  // persistent grid size per CU
 #ifndef FP8Q_Q_GELU_BLOCKS_PER_CU
-#define FP8Q_Q_GELU_BLOCKS_PER_CU 4
+#define FP8Q_Q_GELU_BLOCKS_PER_CU 5
 #endif
-// the gelu instance is arithmetic-bound: more resident waves hide exp/rcp latency (4 blocks
-// per CU: 91.4 us on 8192 x 16384 bf16, against 93.6 with 3 and 95.6 with 2)
+// the gelu instance is arithmetic-bound: more resident waves hide exp/rcp latency (on
+// 8192 x 16384 bf16: 5 blocks per CU 88.5-90.0 us, 4 90.4-91.2, 6 like 5; on another box
+// 4 blocks 91.4 us, 3 93.6, 2 95.6)
 constexpr int kQGeluBlocksPerCU = FP8Q_Q_GELU_BLOCKS_PER_CU;
 constexpr int kQChunk = kQBlock * kQUnroll;       // units (8-element groups) per chunk
 #ifndef FP8Q_Q_DEPTH
