@@ -54,8 +54,6 @@ def _declare(lib):
     lib.oracle_quantize_element.restype = c.c_uint8
     lib.oracle_quantize_amax.argtypes = [vp, i32, vp, i64, i32, c.c_float, f32p]
     lib.oracle_quantize_amax.restype = None
-    lib.oracle_amax.argtypes = [vp, i32, i64, f32p]
-    lib.oracle_amax.restype = None
     lib.oracle_amax_and_scale_update.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i64, i64,
                                                  i32, i32, i32]
     lib.oracle_amax_and_scale_update.restype = None
@@ -130,12 +128,6 @@ class Oracle:
             with ThreadPoolExecutor(threads) as ex:
                 list(ex.map(run, range(threads)))
         return dst.reshape(x.shape), np.uint32(amaxes.view(np.uint32).max()).view(np.float32)
-
-    def amax(self, x: np.ndarray, amax_in: float = 0.0) -> np.float32:
-        x, dt = self._src(x)
-        a = ctypes.c_float(amax_in)
-        self.lib.oracle_amax(x.ctypes.data, dt, x.size, ctypes.byref(a))
-        return np.float32(a.value)
 
     def amax_and_scale_update(self, amax, hist, scale, formats, algo=AMAX_MAX, margin=0,
                               reset_amax=False):

@@ -140,16 +140,6 @@ void oracle_quantize_amax(const void* src, int src_dtype, uint8_t* dst, int64_t 
   *amax = u2f(acc);
 }
 
-/* Amax only (same R5 reduction), for checks that do not need the codes. */
-void oracle_amax(const void* src, int src_dtype, int64_t n, float* amax) {
-  uint32_t acc = f2u(*amax);
-  for (int64_t i = 0; i < n; ++i) {
-    uint32_t mag = f2u(load_wide(src, src_dtype, i)) & 0x7FFFFFFFu;
-    if (mag > acc) acc = mag;
-  }
-  *amax = u2f(acc);
-}
-
 /* The amax-history scale update of [TE-593] for n tensors, out of place
  * (hist_in/hist_out are [H][n] row-major; R6-R8; scale formula [NG-JAX]). */
 void oracle_amax_and_scale_update(const float* amax, const float* hist_in, float* hist_out,

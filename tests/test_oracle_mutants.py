@@ -85,8 +85,13 @@ MUTANTS = [
      "if (a.special == 2 || b.special == 2) { continue; }"),
     ("gemm_group_of_four", "if (k % 8 == 0) { gsum += gmax; gmax = 0.0; }",
      "if (k % 4 == 0) { gsum += gmax; gmax = 0.0; }"),
-    ("amax_nan_canonical", "  *amax = u2f(acc);\n}\n\n/* Amax only",
-     "  *amax = isnan(u2f(acc)) ? NAN : u2f(acc);\n}\n\n/* Amax only"),
+    ("amax_nan_canonical", "  *amax = u2f(acc);\n}\n\n/* The amax-history",
+     "  *amax = isnan(u2f(acc)) ? NAN : u2f(acc);\n}\n\n/* The amax-history"),
+    ("e4m3_max_480", "return fmt == ORC_E4M3 ? 448.0f : 57344.0f;",
+     "return fmt == ORC_E4M3 ? 480.0f : 57344.0f;"),
+    ("count_saturated_one_sided", "if (v > mx || v < -mx) ++c;", "if (v > mx) ++c;"),
+    ("gelu_array_index_shift", "y[i] = oracle_gelu_bf16(x[i], &alt[i]);",
+     "y[i] = oracle_gelu_bf16(x[i > 0 ? i - 1 : 0], &alt[i]);"),
     ("dequant_nan_unsigned", "uint32_t nan_bits = 0x7FC00000u | ((uint32_t)(src[i] & 0x80) << 24);",
      "uint32_t nan_bits = 0x7FC00000u;"),
 ]
@@ -116,3 +121,42 @@ def test_mutant_is_caught(tmp_path, name, old, new):
             caught.append("%s:%s" % (pin.__name__, type(e).__name__))
             break
     assert caught, "planted mistake %r passed every pin" % name
+
+
+def _functions(src):
+    """Top-level function definitions of the oracle source: name -> (is_static, body
+    text from the signature to the closing brace at column 0)."""
+    import re
+    out = {}
+    for m in re.finditer(r"^(static )?[a-z][\w ]*?\b(\w+)\(([^;{]*?)\)\s*\{", src, re.M):
+        start = m.start()
+        end = src.find("\n}", m.end())
+        one_line = src.find("}\n", m.end())
+        if one_line != -1 and "\n" not in src[m.end():one_line]:
+            end = one_line            # a definition on one line
+        out[m.group(2)] = (m.group(1) is not None, src[start:end + 2])
+    return out
+
+
+def test_every_exported_oracle_function_has_a_mutant():
+    """Each exported oracle function contains (itself or through a static helper it
+    calls) the site of at least one planted mistake above, so every function the tests
+    rely on is pinned by a pin that the parametrized test shows catching that mistake."""
+    src = open(SRC).read()
+    fns = _functions(src)
+    exported = sorted(k for k, (st, _) in fns.items() if not st and k.startswith("oracle_"))
+    assert "oracle_quantize_amax" in exported and "oracle_fp8_encode" in exported
+
+    def reach(name, seen=None):
+        seen = seen or set()
+        if name in seen:
+            return ""
+        seen.add(name)
+        text = fns[name][1]
+        for other, (st, _) in fns.items():
+            if other != name and (st or other.startswith("oracle_")) and other + "(" in text:
+                text += reach(other, seen)
+        return text
+
+    missing = [f for f in exported if not any(old in reach(f) for _, old, _ in MUTANTS)]
+    assert not missing, "exported oracle functions without a planted mistake: %s" % missing
