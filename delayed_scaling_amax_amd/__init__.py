@@ -92,13 +92,34 @@ def _check(fn: str, status: int) -> None:
         raise Fp8qError(fn, status)
 
 
-def _dense(t: torch.Tensor, name: str) -> int:
+def _on(t: torch.Tensor, name: str, dev: torch.device) -> None:
+    """Every tensor of a call must live on the call's GPU: a host pointer or another
+    device's pointer handed to a kernel would fault the GPU instead of raising."""
+    if not isinstance(t, torch.Tensor):
+        raise ValueError("%s must be a torch.Tensor" % name)
+    if not t.is_cuda:
+        raise ValueError("%s must be a GPU tensor (got device %s)" % (name, t.device))
+    if t.device != dev:
+        raise ValueError("%s is on %s, the call runs on %s" % (name, t.device, dev))
+
+
+def _device(t: torch.Tensor, name: str) -> torch.device:
+    """The GPU a call runs on: the device of its first tensor argument."""
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError("%s must be a GPU tensor (got %s)" % (
+            name, t.device if isinstance(t, torch.Tensor) else type(t).__name__))
+    return t.device
+
+
+def _dense(t: torch.Tensor, name: str, dev: torch.device) -> int:
+    _on(t, name, dev)
     if not t.is_contiguous():
         raise ValueError("%s must be contiguous" % name)
     return t.data_ptr()
 
 
-def _one_float(t: torch.Tensor, name: str) -> int:
+def _one_float(t: torch.Tensor, name: str, dev: torch.device) -> int:
+    _on(t, name, dev)
     if t.dtype != torch.float32 or t.numel() != 1:
         raise ValueError("%s must be a 1-element float32 tensor" % name)
     return t.data_ptr()
@@ -108,34 +129,34 @@ def _stream(device: torch.device) -> int:
     return torch.cuda.current_stream(device).cuda_stream
 
 
+def _single(fn: str, src, dst, scale, amax, format) -> None:
+    dev = _device(src, "src")
+    if not isinstance(dst, torch.Tensor) or dst.dtype != torch.uint8 or dst.numel() != src.numel():
+        raise ValueError("dst must be uint8 with src.numel() elements")
+    args = (_dense(src, "src", dev), _DTYPE.get(src.dtype, -1), _dense(dst, "dst", dev),
+            src.numel(), int(format), _one_float(scale, "scale", dev),
+            _one_float(amax, "amax", dev))
+    with torch.cuda.device(dev):
+        _check(fn, getattr(lib, fn)(*args, _stream(dev)))
+
+
 def fp8_quantize_amax(src: torch.Tensor, dst: torch.Tensor, scale: torch.Tensor,
                       amax: torch.Tensor, format: int) -> None:
-    if dst.dtype != torch.uint8 or dst.numel() != src.numel():
-        raise ValueError("dst must be uint8 with src.numel() elements")
-    with torch.cuda.device(src.device):
-        _check("fp8_quantize_amax", lib.fp8_quantize_amax(
-            _dense(src, "src"), _DTYPE.get(src.dtype, -1), _dense(dst, "dst"), src.numel(),
-            int(format), _one_float(scale, "scale"), _one_float(amax, "amax"),
-            _stream(src.device)))
+    _single("fp8_quantize_amax", src, dst, scale, amax, format)
 
 
 def fp8_gelu_quantize_amax(src: torch.Tensor, dst: torch.Tensor, scale: torch.Tensor,
                            amax: torch.Tensor, format: int) -> None:
-    if dst.dtype != torch.uint8 or dst.numel() != src.numel():
-        raise ValueError("dst must be uint8 with src.numel() elements")
-    with torch.cuda.device(src.device):
-        _check("fp8_gelu_quantize_amax", lib.fp8_gelu_quantize_amax(
-            _dense(src, "src"), _DTYPE.get(src.dtype, -1), _dense(dst, "dst"), src.numel(),
-            int(format), _one_float(scale, "scale"), _one_float(amax, "amax"),
-            _stream(src.device)))
+    _single("fp8_gelu_quantize_amax", src, dst, scale, amax, format)
 
 
-def _opt_f32(t, n: int, name: str) -> int | None:
+def _opt_f32(t, n: int, name: str, dev: torch.device) -> int | None:
     if t is None:
         return None
+    _on(t, name, dev)
     if t.dtype != torch.float32 or t.numel() != n:
         raise ValueError("%s must be a float32 tensor of %d elements" % (name, n))
-    return _dense(t, name)
+    return _dense(t, name, dev)
 
 
 def fp8_layernorm_quantize_amax(x: torch.Tensor, dst: torch.Tensor, scale: torch.Tensor,
@@ -143,24 +164,28 @@ def fp8_layernorm_quantize_amax(x: torch.Tensor, dst: torch.Tensor, scale: torch
                                 eps: float = 1e-6, mean=None, rstd=None) -> None:
     """LayerNorm over the last axis of x, quantized; mean/rstd (rows elements each) are
     optional outputs."""
+    dev = _device(x, "x")
     if x.dim() < 1:
         raise ValueError("x must have a last axis")
     hidden = x.shape[-1]
     rows = x.numel() // hidden if hidden else 0
-    if dst.dtype != torch.uint8 or dst.numel() != x.numel():
+    if not isinstance(dst, torch.Tensor) or dst.dtype != torch.uint8 or dst.numel() != x.numel():
         raise ValueError("dst must be uint8 with x.numel() elements")
-    with torch.cuda.device(x.device):
-        _check("fp8_layernorm_quantize_amax", lib.fp8_layernorm_quantize_amax(
-            _dense(x, "x"), _DTYPE.get(x.dtype, -1), _opt_f32(gamma, hidden, "gamma"),
-            _opt_f32(beta, hidden, "beta"), float(eps), rows, hidden, _dense(dst, "dst"),
-            int(format), _one_float(scale, "scale"), _one_float(amax, "amax"),
-            _opt_f32(mean, rows, "mean"), _opt_f32(rstd, rows, "rstd"), _stream(x.device)))
+    args = (_dense(x, "x", dev), _DTYPE.get(x.dtype, -1), _opt_f32(gamma, hidden, "gamma", dev),
+            _opt_f32(beta, hidden, "beta", dev), float(eps), rows, hidden,
+            _dense(dst, "dst", dev), int(format), _one_float(scale, "scale", dev),
+            _one_float(amax, "amax", dev), _opt_f32(mean, rows, "mean", dev),
+            _opt_f32(rstd, rows, "rstd", dev))
+    with torch.cuda.device(dev):
+        _check("fp8_layernorm_quantize_amax",
+               lib.fp8_layernorm_quantize_amax(*args, _stream(dev)))
 
 
 def fp8_gemm(A: torch.Tensor, a_format: int, B: torch.Tensor, b_format: int,
              a_scale: torch.Tensor, b_scale: torch.Tensor, C: torch.Tensor) -> None:
     """C (M, N) bf16/fp32 = a_scale * b_scale * decode(A) @ decode(B).T for uint8 code
     tensors A (M, K) and B (N, K)."""
+    dev = _device(A, "A")
     if A.dim() != 2 or B.dim() != 2 or C.dim() != 2:
         raise ValueError("A, B and C must be 2-D")
     M, K = A.shape
@@ -169,21 +194,24 @@ def fp8_gemm(A: torch.Tensor, a_format: int, B: torch.Tensor, b_format: int,
         raise ValueError("shapes: A (M, K), B (N, K), C (M, N)")
     if A.dtype != torch.uint8 or B.dtype != torch.uint8:
         raise ValueError("A and B hold FP8 codes as uint8")
-    with torch.cuda.device(A.device):
-        _check("fp8_gemm", lib.fp8_gemm(
-            _dense(A, "A"), int(a_format), _dense(B, "B"), int(b_format), M, N, K,
-            _one_float(a_scale, "a_scale"), _one_float(b_scale, "b_scale"), _dense(C, "C"),
-            _DTYPE.get(C.dtype, -1), _stream(A.device)))
+    args = (_dense(A, "A", dev), int(a_format), _dense(B, "B", dev), int(b_format), M, N, K,
+            _one_float(a_scale, "a_scale", dev), _one_float(b_scale, "b_scale", dev),
+            _dense(C, "C", dev), _DTYPE.get(C.dtype, -1))
+    with torch.cuda.device(dev):
+        _check("fp8_gemm", lib.fp8_gemm(*args, _stream(dev)))
 
 
-def _entry_table(entries):
+def _entry_table(entries, dev: torch.device):
     arr = (fp8q_tensor * len(entries))()
     for i, (src, dst, scale, amax, fmt) in enumerate(entries):
-        if dst.dtype != torch.uint8 or dst.numel() != src.numel():
+        name = "entry %d " % i
+        _on(src, name + "src", dev)
+        if not isinstance(dst, torch.Tensor) or dst.dtype != torch.uint8 or dst.numel() != src.numel():
             raise ValueError("entry %d: dst must be uint8 with src.numel() elements" % i)
-        arr[i] = fp8q_tensor(_dense(src, "src"), _dense(dst, "dst"), src.numel(),
-                             _DTYPE.get(src.dtype, -1), int(fmt), _one_float(scale, "scale"),
-                             _one_float(amax, "amax"))
+        arr[i] = fp8q_tensor(_dense(src, name + "src", dev), _dense(dst, name + "dst", dev),
+                             src.numel(), _DTYPE.get(src.dtype, -1), int(fmt),
+                             _one_float(scale, name + "scale", dev),
+                             _one_float(amax, name + "amax", dev))
     return arr
 
 
@@ -192,8 +220,8 @@ def fp8_multi_quantize_amax(entries) -> None:
     entries = list(entries)
     if not entries:
         return
-    arr = _entry_table(entries)
-    dev = entries[0][0].device
+    dev = _device(entries[0][0], "entry 0 src")
+    arr = _entry_table(entries, dev)
     with torch.cuda.device(dev):
         _check("fp8_multi_quantize_amax",
                lib.fp8_multi_quantize_amax(arr, len(entries), _stream(dev)))
@@ -214,8 +242,9 @@ def fp8_multi_quantize_amax_timed(entries, start_event, stop_event) -> None:
     start_event.elapsed_time(stop_event) is the kernels' duration without the dispatch
     latency that events recorded on the stream around the call also span."""
     entries = list(entries)
-    dev = entries[0][0].device if entries else torch.device("cuda", torch.cuda.current_device())
-    arr = _entry_table(entries)
+    dev = (_device(entries[0][0], "entry 0 src") if entries
+           else torch.device("cuda", torch.cuda.current_device()))
+    arr = _entry_table(entries, dev)
     with torch.cuda.device(dev):
         _check("fp8_multi_quantize_amax_timed",
                lib.fp8_multi_quantize_amax_timed(arr, len(entries), _stream(dev),
@@ -225,15 +254,21 @@ def fp8_multi_quantize_amax_timed(entries, start_event, stop_event) -> None:
 
 def fp8_dequantize(src: torch.Tensor, dst: torch.Tensor, scale: torch.Tensor,
                    format: int) -> None:
-    if src.dtype != torch.uint8 or dst.numel() != src.numel():
+    dev = _device(src, "src")
+    if src.dtype != torch.uint8 or not isinstance(dst, torch.Tensor) or dst.numel() != src.numel():
         raise ValueError("src must be uint8 and dst must have src.numel() elements")
-    with torch.cuda.device(src.device):
-        _check("fp8_dequantize", lib.fp8_dequantize(
-            _dense(src, "src"), int(format), _dense(dst, "dst"), _DTYPE.get(dst.dtype, -1),
-            src.numel(), _one_float(scale, "scale"), _stream(src.device)))
+    args = (_dense(src, "src", dev), int(format), _dense(dst, "dst", dev),
+            _DTYPE.get(dst.dtype, -1), src.numel(), _one_float(scale, "scale", dev))
+    with torch.cuda.device(dev):
+        _check("fp8_dequantize", lib.fp8_dequantize(*args, _stream(dev)))
 
 
-def _update_shape(amax, amax_history, scale, scale_inv, formats):
+def _update_args(amax, amax_history, scale, scale_inv, formats):
+    """(device, H, n, pointers...) of the update's five arrays, all checked."""
+    dev = _device(amax, "amax")
+    for t, name in ((amax_history, "amax_history"), (scale, "scale"),
+                    (scale_inv, "scale_inv"), (formats, "formats")):
+        _on(t, name, dev)
     if amax_history.dim() != 2:
         raise ValueError("amax_history must be [history_len, n]")
     H, n = amax_history.shape
@@ -244,20 +279,20 @@ def _update_shape(amax, amax_history, scale, scale_inv, formats):
         raise ValueError("amax_history must be float32")
     if formats.dtype != torch.uint8 or formats.numel() != n:
         raise ValueError("formats must be uint8 with n elements")
-    return H, n
+    ptrs = (_dense(amax, "amax", dev), _dense(amax_history, "amax_history", dev),
+            _dense(scale, "scale", dev), _dense(scale_inv, "scale_inv", dev),
+            _dense(formats, "formats", dev))
+    return dev, H, n, ptrs
 
 
 def fp8_amax_and_scale_update(amax: torch.Tensor, amax_history: torch.Tensor,
                               scale: torch.Tensor, scale_inv: torch.Tensor,
                               formats: torch.Tensor, algo: int = AMAX_MAX, margin: int = 0,
                               reset_amax: bool = False) -> None:
-    H, n = _update_shape(amax, amax_history, scale, scale_inv, formats)
-    with torch.cuda.device(amax.device):
+    dev, H, n, ptrs = _update_args(amax, amax_history, scale, scale_inv, formats)
+    with torch.cuda.device(dev):
         _check("fp8_amax_and_scale_update", lib.fp8_amax_and_scale_update(
-            _dense(amax, "amax"), _dense(amax_history, "amax_history"), _dense(scale, "scale"),
-            _dense(scale_inv, "scale_inv"), _dense(formats, "formats"), n, H, int(algo),
-            int(margin), int(bool(reset_amax)), _stream(amax.device)))
-
+            *ptrs, n, H, int(algo), int(margin), int(bool(reset_amax)), _stream(dev)))
 
 
 def fp8_quantize_amax_and_update(entries, amax: torch.Tensor, amax_history: torch.Tensor,
@@ -270,16 +305,16 @@ def fp8_quantize_amax_and_update(entries, amax: torch.Tensor, amax_history: torc
     fp8_amax_and_scale_update(...), in one kernel launch when it fits.  workspace: a
     1-element int32/uint32 device tensor holding 0 (every call leaves it 0)."""
     entries = list(entries)
-    H, n = _update_shape(amax, amax_history, scale, scale_inv, formats)
+    dev, H, n, ptrs = _update_args(amax, amax_history, scale, scale_inv, formats)
+    _on(workspace, "workspace", dev)
     if workspace.numel() != 1 or workspace.element_size() != 4:
         raise ValueError("workspace must be one 4-byte element")
-    arr = _entry_table(entries)
-    with torch.cuda.device(amax.device):
+    arr = _entry_table(entries, dev)
+    ws = _dense(workspace, "workspace", dev)
+    with torch.cuda.device(dev):
         _check("fp8_quantize_amax_and_update", lib.fp8_quantize_amax_and_update(
-            arr, len(entries), _dense(amax, "amax"), _dense(amax_history, "amax_history"),
-            _dense(scale, "scale"), _dense(scale_inv, "scale_inv"), _dense(formats, "formats"),
-            n, H, int(algo), int(margin), int(bool(reset_amax)), _dense(workspace, "workspace"),
-            _stream(amax.device), _event_handle(start_event), _event_handle(stop_event)))
+            arr, len(entries), *ptrs, n, H, int(algo), int(margin), int(bool(reset_amax)), ws,
+            _stream(dev), _event_handle(start_event), _event_handle(stop_event)))
 
 
 __all__ = ["fp8_quantize_amax", "fp8_multi_quantize_amax", "fp8_multi_quantize_amax_timed",
