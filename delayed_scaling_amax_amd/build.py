@@ -11,6 +11,9 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(PKG, "libfp8q.so")
+# measurement probes for the benchmark (same memory traffic without the method's
+# arithmetic); a library of their own, outside the interface of libfp8q.so
+PROBE_LIB_PATH = os.path.join(PKG, "libfp8q_probe.so")
 ARCH = "gfx950"
 
 # -ffp-contract=off: every binary32 step is the one written (the kernels spell out
@@ -39,17 +42,24 @@ def sources() -> list[str]:
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.cpp")))
 
 
-def build(verbose: bool = False) -> str:
-    tmp = LIB_PATH + ".tmp%d" % os.getpid()
-    cmd = [hipcc(), *HIP_FLAGS, "-shared", "-I", INCLUDE, "-I", CSRC, "-o", tmp, *sources()]
+def _link(out: str, srcs: list[str], verbose: bool) -> str:
+    tmp = out + ".tmp%d" % os.getpid()
+    cmd = [hipcc(), *HIP_FLAGS, "-shared", "-I", INCLUDE, "-I", CSRC, "-o", tmp, *srcs]
     res = subprocess.run(cmd, capture_output=True, text=True)
     noise = ("packed-fp32-ops", "--hip-link")
     msgs = [ln for ln in (res.stdout + res.stderr).splitlines() if not any(n in ln for n in noise)]
     if res.returncode != 0:
-        raise RuntimeError("libfp8q build failed:\n" + " ".join(cmd) + "\n" + "\n".join(msgs))
+        raise RuntimeError("%s build failed:\n" % os.path.basename(out) + " ".join(cmd) + "\n"
+                           + "\n".join(msgs))
     if verbose and msgs:
         print("\n".join(msgs))
-    os.replace(tmp, LIB_PATH)
+    os.replace(tmp, out)
+    return out
+
+
+def build(verbose: bool = False) -> str:
+    _link(LIB_PATH, sources(), verbose)
+    _link(PROBE_LIB_PATH, sorted(glob.glob(os.path.join(CSRC, "probe", "*.hip"))), verbose)
     return LIB_PATH
 
 

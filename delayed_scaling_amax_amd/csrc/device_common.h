@@ -20,29 +20,48 @@ __device__ __forceinline__ uint32_t pk_max_u16(uint32_t a, uint32_t b) {
                                                                 __builtin_bit_cast(u16x2, b)));
 }
 
-// Max over the 64 lanes of a wavefront (butterfly through ds_swizzle/bpermute).
-__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) {
-    uint32_t o = __shfl_xor(v, off, 64);
-    v = v > o ? v : o;
-  }
-  return v;
+// One step of a DPP max: lanes whose DPP source is invalid or whose row is outside
+// kRowMask read 0 (the identity of the unsigned max) and keep v.
+template <int kCtrl, int kRowMask>
+__device__ __forceinline__ uint32_t dpp_max_step(uint32_t v) {
+  const uint32_t t = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kCtrl, kRowMask, 0xF, false);
+  return v > t ? v : t;
 }
 
-// Block-wide max of one value per thread; every thread gets the result.  `red`
-// holds one slot per wavefront.  Contains two barriers: all threads must call it.
-template <int kBlock>
-__device__ __forceinline__ uint32_t block_max_u32(uint32_t v, uint32_t* red) {
-  v = wave_max_u32(v);
-  const int wave = threadIdx.x >> 6;
-  if ((threadIdx.x & 63) == 0) red[wave] = v;
-  __syncthreads();
-  uint32_t r = red[0];
-#pragma unroll
-  for (int w = 1; w < kBlock / 64; ++w) r = r > red[w] ? r : red[w];
-  __syncthreads();  // red may be reused right after
-  return r;
+// Max over the 64 lanes of a wavefront on the DPP network (no LDS round trips): xor-1
+// and xor-2 within quads, rotations by 4 and 8 within each 16-lane row, then rows 0 and
+// 1, 2 and 3 (row_bcast15) and the two halves (row_bcast31) into lane 63, whose value
+// every lane gets through a scalar register.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = dpp_max_step<0xB1, 0xF>(v);   // quad_perm [1,0,3,2]
+  v = dpp_max_step<0x4E, 0xF>(v);   // quad_perm [2,3,0,1]
+  v = dpp_max_step<0x124, 0xF>(v);  // row_ror:4
+  v = dpp_max_step<0x128, 0xF>(v);  // row_ror:8
+  v = dpp_max_step<0x142, 0xA>(v);  // row_bcast:15 into rows 1 and 3
+  v = dpp_max_step<0x143, 0xC>(v);  // row_bcast:31 into rows 2 and 3
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
+// Max of v over the lanes of the wavefront whose index agrees with this lane's modulo
+// `tpr` (a power of two, 1..32; wave-uniform), returned in every lane, without LDS:
+// lane l with l + 32 and l + 16 through the gfx950 lane-swap instructions
+// (v_permlane32_swap / v_permlane16_swap with both operands v: one result holds each
+// lane's partner), then rotations by 8 and 4 within each 16-lane row and the xor-2 and
+// xor-1 quad permutations on the DPP network.
+__device__ __forceinline__ uint32_t lane_class_max(uint32_t v, int tpr) {
+  if (tpr <= 32) {
+    const auto w = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    v = (uint32_t)w[0] > (uint32_t)w[1] ? (uint32_t)w[0] : (uint32_t)w[1];
+  }
+  if (tpr <= 16) {
+    const auto w = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    v = (uint32_t)w[0] > (uint32_t)w[1] ? (uint32_t)w[0] : (uint32_t)w[1];
+  }
+  if (tpr <= 8) v = dpp_max_step<0x128, 0xF>(v);  // row_ror:8
+  if (tpr <= 4) v = dpp_max_step<0x124, 0xF>(v);  // row_ror:4
+  if (tpr <= 2) v = dpp_max_step<0x4E, 0xF>(v);   // quad_perm [2,3,0,1]
+  if (tpr <= 1) v = dpp_max_step<0xB1, 0xF>(v);   // quad_perm [1,0,3,2]
+  return v;
 }
 
 // Max-accumulate a block's amax bits v into the tensor's amax at p (binary32 bit

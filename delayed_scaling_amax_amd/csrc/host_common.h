@@ -7,6 +7,7 @@
 #include <atomic>
 
 #include "fp8q.h"
+#include "update_grid.h"
 
 namespace fp8q {
 
@@ -44,6 +45,8 @@ inline int validate_update(const float* amax, const float* hist, const float* sc
   if (n == 0) return FP8Q_OK;
   if (!amax || !hist || !scale || !scale_inv || !formats) return FP8Q_EINVAL;
   if (history_len > (INT64_MAX / 8) / n) return FP8Q_EINVAL;  // H*n floats must be addressable
+  // the update kernel addresses the history with 32-bit buffer offsets
+  if (history_len * n >= kUpdateMaxElems) return FP8Q_EUNSUPPORTED;
   return FP8Q_OK;
 }
 

@@ -256,8 +256,9 @@ int fp8_dequantize(const uint8_t* src, int format, void* dst, int dst_dtype, int
  *   formats        device uint8[n]: 0 = E4M3 (max 448), any other value = E5M2
  *                  (max 57344)
  *   n >= 0 (0 enqueues nothing); history_len >= 1; algo FP8Q_AMAX_MAX or
- *   FP8Q_AMAX_MOST_RECENT; margin in [-126, 126].  The five arrays must not overlap.
- * Returns FP8Q_OK, FP8Q_EINVAL or FP8Q_EHIP.
+ *   FP8Q_AMAX_MOST_RECENT; margin in [-126, 126]; history_len * n below 2^29 (a 2 GiB
+ *   history; larger: FP8Q_EUNSUPPORTED).  The five arrays must not overlap.
+ * Returns FP8Q_OK, FP8Q_EINVAL, FP8Q_EUNSUPPORTED or FP8Q_EHIP.
  */
 int fp8_amax_and_scale_update(float* amax, float* amax_history, float* scale,
                               float* scale_inv, const uint8_t* formats, int64_t n,
@@ -289,7 +290,8 @@ int fp8_amax_and_scale_update(float* amax, float* amax_history, float* scale,
  *               fp8_multi_quantize_amax_timed (NULL for none); with the two-launch form
  *               they span the quantize kernels only.
  * Every argument is validated before anything is enqueued.
- * Returns FP8Q_OK, FP8Q_EINVAL or FP8Q_EHIP.
+ * Returns FP8Q_OK, FP8Q_EINVAL, FP8Q_EUNSUPPORTED (history as in
+ * fp8_amax_and_scale_update) or FP8Q_EHIP.
  */
 int fp8_quantize_amax_and_update(const fp8q_tensor* tensors, int n_tensors, float* amax,
                                  float* amax_history, float* scale, float* scale_inv,

@@ -186,6 +186,18 @@ def test_update_rejects_invalid(n, H, algo, margin, ptrs):
     assert d.lib.fp8_amax_and_scale_update(*p, n, H, algo, margin, 0, None) == d.EINVAL
 
 
+def test_update_refuses_histories_past_32bit_offsets():
+    """history_len * n >= 2^29 (2 GiB of history): FP8Q_EUNSUPPORTED before anything is
+    enqueued, from the update and from the one-launch step."""
+    import delayed_scaling_amax_amd as d
+    p = [BAD] * 5
+    assert d.lib.fp8_amax_and_scale_update(*p, 1 << 10, 1 << 19, 0, 0, 0, None) == d.EUNSUPPORTED
+    assert d.lib.fp8_amax_and_scale_update(*p, 1152, 466034, 0, 0, 0, None) == d.EUNSUPPORTED
+    arr = (d.fp8q_tensor * 1)()
+    arr[0] = d.fp8q_tensor(BAD, BAD, 1 << 20, 0, 0, BAD, BAD)
+    assert _step(d, arr, 1, n=1 << 10, H=1 << 19) == d.EUNSUPPORTED
+
+
 def _step(d, arr, nt, n=3, H=4, algo=0, margin=0, ws=BAD, ptrs=5):
     p = [BAD] * 5
     if ptrs < 5:

@@ -47,3 +47,27 @@ def test_rejects_empty_timed_region():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--steps", "0"],
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2 and "--steps" in r.stderr and r.stdout == ""
+
+
+def test_headline_is_the_largest_step():
+    """The default workload is the hidden-12288 MLP's full step (5 tensors, 1.36 G
+    elements): 4,076,863,488 algorithmic bytes plus 12 per tensor."""
+    b = _bench()
+    src = open(os.path.join(ROOT, "bench.py")).read()
+    assert 'default="mlp_12288"' in src
+
+    class T:
+        def __init__(self, n):
+            self.data = np.lib.stride_tricks.as_strided(np.zeros(1, np.uint16), (n,), (0,))
+
+    class W:
+        tensors = [T(2048 * 12288), T(2048 * 49152), T(12288 * 49152), T(49152 * 12288),
+                   T(2048 * 12288)]
+
+    assert b.alg_bytes_quantize(W) == 4076863488 + 5 * 12
+
+
+def test_cpu_baseline_uses_every_allowed_cpu():
+    b = _bench()
+    n = b.host_cpus()
+    assert 1 <= n <= len(os.sched_getaffinity(0))

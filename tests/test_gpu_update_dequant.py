@@ -51,7 +51,8 @@ def test_update_1152_workload(orc, margin, algo):
 
 @pytest.mark.parametrize("n,H", [(1, 1), (1, 16), (3, 16), (5, 1024), (4, 2), (7, 3),
                                  (1151, 1024), (1152, 1023), (1152, 1025), (12, 2049),
-                                 (64, 4100), (9, 1)])
+                                 (64, 4100), (9, 1), (4, 1025), (8, 1026), (1152, 1026),
+                                 (1156, 2), (6, 1026)])
 def test_update_shapes(orc, n, H):
     g = np.random.Generator(np.random.PCG64(n * 7919 + H))
     amax = lognormal(n, n + H)
