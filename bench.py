@@ -373,6 +373,9 @@ def main():
     ap.add_argument("--no-others", action="store_true",
                     help="skip the steps of the other large workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-list", action="store_true",
+                    help="skip the 1152-tensor list (32-entry launches against one planned "
+                         "launch)")
     ap.add_argument("--no-probes", action="store_true",
                     help="skip the stream ceiling and update floor probes")
     ap.add_argument("--no-gelu", action="store_true",
@@ -448,6 +451,85 @@ def main():
             torch.cuda.empty_cache()
     if w.name == "mlp_4096":
         w4096 = w
+
+    # ------------------------------------------------------------ 1152-tensor list
+    # the 1152 FP8 tensors of the batched-update layout as one quantize list: through
+    # fp8_multi_quantize_amax (one launch per 32 entries: 36) and through one planned
+    # launch; host time per call (the C entry points called directly, the ctypes entry
+    # array built once, so the binding's marshalling is not timed) and device time per
+    # call (events around K back-to-back calls)
+    list_out = None
+    if not args.no_list:
+        lw = workloads.make("list_1152", threads=threads)
+        lfm = [0 if t.fmt == workloads.E4M3 else 1 for t in lw.tensors]
+        lsrc = [torch.from_numpy(t.data.reshape(-1).view(np.int16)).view(torch.bfloat16).to(dev)
+                for t in lw.tensors]
+        ldst = [torch.empty(x.numel(), dtype=torch.uint8, device=dev) for x in lsrc]
+        lscale = torch.ones(len(lsrc), dtype=torch.float32, device=dev)
+        lamax = torch.zeros(len(lsrc), dtype=torch.float32, device=dev)
+        lent = [(lsrc[i], ldst[i], lscale[i:i + 1], lamax[i:i + 1], lfm[i])
+                for i in range(len(lsrc))]
+        arr = d._entry_table(lent, dev)
+        t0 = time.perf_counter()
+        plan = d.fp8_multi_quantize_plan(lent)
+        torch.cuda.synchronize()
+        plan_us = (time.perf_counter() - t0) * 1e6
+        cs = torch.cuda.current_stream(dev).cuda_stream
+        pdesc = ctypes.byref(plan.desc)
+
+        def chunked():
+            d._check("fp8_multi_quantize_amax", d.lib.fp8_multi_quantize_amax(arr, len(lent), cs))
+
+        def planned():
+            d._check("fp8_multi_quantize_amax_planned",
+                     d.lib.fp8_multi_quantize_amax_planned(pdesc, cs))
+
+        def per_call(fn):
+            for _ in range(3):
+                fn()
+            torch.cuda.synchronize()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            t0 = time.perf_counter()
+            a.record()
+            for _ in range(K):
+                fn()
+            b.record()
+            t_enq = time.perf_counter()
+            torch.cuda.synchronize()
+            return (t_enq - t0) * 1e6 / K, 1e3 * a.elapsed_time(b) / K
+
+        c_host, c_dev = per_call(chunked)
+        p_host, p_dev = per_call(planned)
+        # the two forms' outputs are compared (codes of every tensor, amax bits)
+        lamax.zero_()
+        chunked()
+        torch.cuda.synchronize()
+        ref_codes = [x.clone() for x in ldst]
+        ref_amax = lamax.clone()
+        lamax.zero_()
+        for x in ldst:
+            x.zero_()
+        planned()
+        torch.cuda.synchronize()
+        same = all(torch.equal(ref_codes[i], ldst[i]) for i in range(len(ldst))) and \
+            torch.equal(ref_amax.view(torch.int32), lamax.view(torch.int32))
+        lb = alg_bytes_quantize(lw)
+        list_out = {"workload": lw.name, "description": lw.description,
+                    "elements": lw.numel, "alg_bytes": lb, "tensors": len(lent),
+                    "chunked_launches_per_call": -(-len(lent) // 32),
+                    "chunked_host_us_per_call": round(c_host, 2),
+                    "chunked_device_us_per_call": round(c_dev, 2),
+                    "planned_host_us_per_call": round(p_host, 2),
+                    "planned_device_us_per_call": round(p_dev, 2),
+                    "planned_gbps": round(lb / (p_dev * 1e-6) / 1e9, 1),
+                    "plan_build_us": round(plan_us, 1),
+                    "planned_equals_chunked": bool(same)}
+        log("list_1152: 36 launches %.1f us host / %.1f us device per call; one planned "
+            "launch %.1f us host / %.1f us device (%.1f GB/s); plan built in %.0f us; %s" % (
+                c_host, c_dev, p_host, p_dev, lb / (p_dev * 1e-6) / 1e9, plan_us,
+                "identical" if same else "MISMATCH"))
+        del lsrc, ldst, lent, plan, ref_codes
+        torch.cuda.empty_cache()
 
     # ------------------------------------------------------------ batched update, 1152 tensors
     uw = workloads.update_1152(threads=threads)
@@ -754,6 +836,7 @@ def main():
                           "pct_hbm_peak": round(100 * q_gbps / PEAK_HBM_GBPS, 2),
                           "alg_bytes": qbytes},
         "other_workloads": others,
+        "multi_tensor_list": list_out,
         "stream_ceiling": ceilings,
         "scale_update_us": {"workload": "update_1152 (96 layers x 4 linears x 3 tensors, "
                                         "history 1024, margin 0, in place, one launch)",

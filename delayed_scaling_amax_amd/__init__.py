@@ -8,6 +8,9 @@ the current HIP stream.  Functions carry the C names:
   fp8_multi_quantize_amax([(src, dst, scale, amax, format), ...])   one launch
   fp8_multi_quantize_amax_timed(entries, start_event, stop_event)  the same, with
                             torch.cuda.Events set to the kernel's own start/stop
+  fp8_multi_quantize_plan(entries) -> Plan     up to 2048 entries laid out once in a
+                                               device workspace
+  fp8_multi_quantize_amax_planned(plan)        the whole planned list, one launch
   fp8_gelu_quantize_amax(src, dst, scale, amax, format)     gelu(bf16 src), quantized
   fp8_layernorm_quantize_amax(x, dst, scale, amax, format, gamma=None, beta=None,
                               eps=1e-6, mean=None, rstd=None)  LayerNorm(x), quantized
@@ -47,6 +50,10 @@ class Fp8qError(RuntimeError):
         self.status = status
 
 
+class fp8q_plan(ctypes.Structure):
+    _fields_ = [("opaque", ctypes.c_uint64 * 16)]
+
+
 class fp8q_tensor(ctypes.Structure):
     _fields_ = [("src", ctypes.c_void_p), ("dst", ctypes.c_void_p), ("numel", ctypes.c_int64),
                 ("src_dtype", ctypes.c_int32), ("format", ctypes.c_int32),
@@ -70,12 +77,18 @@ def _load():
     lib.fp8_quantize_amax_and_update.argtypes = [ctypes.POINTER(fp8q_tensor), i32, vp, vp, vp,
                                                  vp, vp, i64, i64, i32, i32, i32, vp, vp, vp,
                                                  vp]
+    lib.fp8_multi_quantize_plan_bytes.argtypes = [ctypes.POINTER(fp8q_tensor), i32]
+    lib.fp8_multi_quantize_plan_bytes.restype = i64
+    lib.fp8_multi_quantize_plan.argtypes = [ctypes.POINTER(fp8q_tensor), i32, vp, i64,
+                                            ctypes.POINTER(fp8q_plan), vp]
+    lib.fp8_multi_quantize_amax_planned.argtypes = [ctypes.POINTER(fp8q_plan), vp]
     lib.fp8_status_string.argtypes = [i32]
     lib.fp8_status_string.restype = ctypes.c_char_p
     for f in ("fp8_quantize_amax", "fp8_multi_quantize_amax", "fp8_multi_quantize_amax_timed",
               "fp8_gelu_quantize_amax",
               "fp8_layernorm_quantize_amax", "fp8_gemm", "fp8_dequantize", "fp8_amax_and_scale_update",
-              "fp8_quantize_amax_and_update"):
+              "fp8_quantize_amax_and_update", "fp8_multi_quantize_plan",
+              "fp8_multi_quantize_amax_planned"):
         getattr(lib, f).restype = i32
     return lib
 
@@ -252,6 +265,63 @@ def fp8_multi_quantize_amax_timed(entries, start_event, stop_event) -> None:
                                                  _event_handle(stop_event)))
 
 
+class Plan:
+    """A list of quantize entries laid out once in a device workspace
+    (fp8_multi_quantize_plan): fp8_multi_quantize_amax_planned(plan) quantizes the whole
+    list in one launch.  Holds the workspace and the entries' tensors, so the pointers the
+    plan records stay valid while it lives."""
+
+    def __init__(self, entries, workspace, desc, device):
+        self.entries = entries
+        self.workspace = workspace
+        self.desc = desc
+        self.device = device
+
+
+def fp8_multi_quantize_plan(entries, workspace: torch.Tensor | None = None) -> Plan:
+    """entries: sequence of (src, dst, scale, amax, format), at most 2048.  workspace: a
+    device uint8 tensor of at least fp8_multi_quantize_plan_bytes(entries) bytes, or
+    None to allocate one.  Set-up call (the layout is copied from host memory, which HIP
+    does synchronously); reuse the Plan every step."""
+    entries = list(entries)
+    dev = (_device(entries[0][0], "entry 0 src") if entries
+           else torch.device("cuda", torch.cuda.current_device()))
+    arr = _entry_table(entries, dev)
+    need = int(lib.fp8_multi_quantize_plan_bytes(arr, len(entries)))
+    if need < 0:
+        raise Fp8qError("fp8_multi_quantize_plan_bytes", need)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    _on(workspace, "workspace", dev)
+    if workspace.numel() * workspace.element_size() < need:
+        raise ValueError("workspace must hold %d bytes" % need)
+    desc = fp8q_plan()
+    with torch.cuda.device(dev):
+        _check("fp8_multi_quantize_plan", lib.fp8_multi_quantize_plan(
+            arr, len(entries), _dense(workspace, "workspace", dev), need, ctypes.byref(desc),
+            _stream(dev)))
+    return Plan(entries, workspace, desc, dev)
+
+
+def fp8_multi_quantize_plan_bytes(entries) -> int:
+    entries = list(entries)
+    dev = (_device(entries[0][0], "entry 0 src") if entries
+           else torch.device("cuda", torch.cuda.current_device()))
+    need = int(lib.fp8_multi_quantize_plan_bytes(_entry_table(entries, dev), len(entries)))
+    if need < 0:
+        raise Fp8qError("fp8_multi_quantize_plan_bytes", need)
+    return need
+
+
+def fp8_multi_quantize_amax_planned(plan: Plan) -> None:
+    """fp8_multi_quantize_amax over every entry of the plan, in one kernel launch."""
+    if not isinstance(plan, Plan):
+        raise ValueError("plan must come from fp8_multi_quantize_plan")
+    with torch.cuda.device(plan.device):
+        _check("fp8_multi_quantize_amax_planned", lib.fp8_multi_quantize_amax_planned(
+            ctypes.byref(plan.desc), _stream(plan.device)))
+
+
 def fp8_dequantize(src: torch.Tensor, dst: torch.Tensor, scale: torch.Tensor,
                    format: int) -> None:
     dev = _device(src, "src")
@@ -318,6 +388,8 @@ def fp8_quantize_amax_and_update(entries, amax: torch.Tensor, amax_history: torc
 
 
 __all__ = ["fp8_quantize_amax", "fp8_multi_quantize_amax", "fp8_multi_quantize_amax_timed",
+           "fp8_multi_quantize_plan", "fp8_multi_quantize_plan_bytes",
+           "fp8_multi_quantize_amax_planned", "Plan", "fp8q_plan",
            "fp8_quantize_amax_and_update",
            "fp8_gelu_quantize_amax",
            "fp8_layernorm_quantize_amax", "fp8_gemm", "fp8_dequantize",

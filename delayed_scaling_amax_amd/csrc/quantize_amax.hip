@@ -27,6 +27,7 @@
 //    v_cvt_pk_fp8_f32 / v_cvt_pk_bf8_f32 (round to nearest even).  NaN quotients
 //    (only possible on the IEEE path) are written as 0x7F with the sign of x.
 #include <hip/hip_ext.h>
+#include <string.h>
 
 #include "device_common.h"
 #include "host_common.h"
@@ -63,6 +64,7 @@ namespace fp8q {
 constexpr int kQBlock = FP8Q_Q_BLOCK;             // threads per block
 constexpr int kQUnroll = FP8Q_Q_UNROLL;           // 8-element groups per thread per chunk
 constexpr int kQMaxEntries = 32;                  // tensors per launch (kernel-argument table)
+constexpr int kQPlanMaxEntries = 2048;            // tensors per launch (planned table in device memory)
 constexpr int kQBlocksPerCU = FP8Q_Q_BLOCKS_PER_CU;  // persistent grid size per CU
 #ifndef FP8Q_Q_GELU_BLOCKS_PER_CU
 #define FP8Q_Q_GELU_BLOCKS_PER_CU 5
@@ -91,10 +93,32 @@ constexpr int kQChunk = kQBlock * kQUnroll;       // units (8-element groups) pe
 #define FP8Q_Q_PAIR 0
 #endif
 constexpr bool kQPair = FP8Q_Q_PAIR != 0;
+// Chunk split over the grid: 1 = grid-stride, 0 = contiguous ranges per block (kernel-
+// argument tables); planned tables: FP8Q_Q_PLAN_CONTIG (1 = contiguous ranges).
+#ifndef FP8Q_Q_SCHEDULE
+#define FP8Q_Q_SCHEDULE 1
+#endif
+#ifndef FP8Q_Q_PLAN_CONTIG
+#define FP8Q_Q_PLAN_CONTIG 0
+#endif
 // Passes in flight ahead of the one being converted.  One is enough for every instance
 // (the gelu one included) once the waits cover only the pass being converted: two were
 // 1-2% slower on the plain quantize of a 0.5 GB step and 2% on the gelu one.
 constexpr int kQDepth = FP8Q_Q_DEPTH;
+// Planned tables of many small tensors move to another tensor on nearly every chunk, and
+// finding it costs two dependent scalar loads (the chunk's entry, then its fields) that
+// stall the wavefront before the next loads can be issued.  More resident wavefronts
+// hide the stalls: on the 1152-tensor list (402.7 M elements), 1 block per CU 308 us, 2
+// 241, 3 229-230, 4 with two passes ahead 227; two passes ahead add 1-2 % (one block
+// per CU: 308 / 302 / 309 us for one, two, three).
+#ifndef FP8Q_Q_PLAN_DEPTH
+#define FP8Q_Q_PLAN_DEPTH 2
+#endif
+constexpr int kQPlanDepth = FP8Q_Q_PLAN_DEPTH;
+#ifndef FP8Q_Q_PLAN_BLOCKS_PER_CU
+#define FP8Q_Q_PLAN_BLOCKS_PER_CU 3
+#endif
+constexpr int kQPlanBlocksPerCU = FP8Q_Q_PLAN_BLOCKS_PER_CU;
 constexpr int kQPass = FP8Q_Q_PASS;    // bf16 groups per pass (fp32: half)
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -182,6 +206,8 @@ struct QUpdate {
 
 // Entries are sorted by kind: kind k occupies [run_end[k-1], run_end[k]).
 struct QTable {
+  static constexpr bool kPlanned = false;
+  static constexpr bool kContig = FP8Q_Q_SCHEDULE == 0;
   QEntry e[kQMaxEntries];
   int64_t total_full;
   int32_t n;
@@ -189,6 +215,21 @@ struct QTable {
   QUpdate upd;  // used by the kUpd kernel instances only
 };
 static_assert(sizeof(QTable) <= 4096, "the table travels as the kernel argument");
+
+// A planned table (fp8_multi_quantize_plan): up to kQPlanMaxEntries entries in device
+// memory, laid out and sorted as in QTable, and the entry holding each full chunk (so a
+// block that moves on to a chunk of another tensor finds it with one load, where a
+// search over the entries would cost a chain of dependent loads per move); the header
+// travels as the kernel argument.
+struct QPlanTable {
+  static constexpr bool kPlanned = true;
+  static constexpr bool kContig = FP8Q_Q_PLAN_CONTIG != 0;
+  const QEntry* __restrict__ e;
+  const int32_t* __restrict__ chunk_entry;  // [total_full]
+  int64_t total_full;
+  int32_t n;
+  int32_t run_end[kQKinds];
+};
 
 // ---------------------------------------------------------------- gelu prologue
 // y = RN_bf16(gelu(x)) for bf16 x, tanh form, in binary32 through its exact identity
@@ -264,19 +305,22 @@ __device__ __forceinline__ uint4 gelu8_bf16(uint4 w) {
 // ---------------------------------------------------------------- per-tensor constants
 // Filled once per block at kernel start (one thread per tensor) so that switching to
 // the next tensor costs an LDS read, not a dependent global load.
-struct QShared {
-  float scale[kQMaxEntries];
-  float rcp[kQMaxEntries];      // RN(1/scale)
-  uint32_t xlim[kQMaxEntries];  // magnitude bits at which the fixed-code path starts
-  uint32_t win[kQMaxEntries];   // scale inside the Markstein window
-  uint32_t amax[kQMaxEntries];  // this block's amax bits per tensor
-  uint32_t last;                // kUpd: this block finished last
+template <int kCap>
+struct QSharedT {
+  float scale[kCap];
+  float rcp[kCap];      // RN(1/scale)
+  uint32_t xlim[kCap];  // magnitude bits at which the fixed-code path starts
+  uint32_t win[kCap];   // scale inside the Markstein window
+  uint32_t amax[kCap];  // this block's amax bits per tensor
+  uint32_t last;        // kUpd: this block finished last
+  uint32_t any_out;     // planned tables: some tensor's scale is outside the window
 };
+using QShared = QSharedT<kQMaxEntries>;
 
 // Fold a thread's accumulator into the block's amax slot of tensor t: wavefront max,
 // then one LDS atomic max per wavefront (no barrier).
-template <bool kBF16>
-__device__ __forceinline__ void flush_amax(uint32_t acc, QShared& sh, int t) {
+template <bool kBF16, class Sh>
+__device__ __forceinline__ void flush_amax(uint32_t acc, Sh& sh, int t) {
   if constexpr (kBF16) {
     const uint32_t lo = acc & 0xFFFFu, hi = acc >> 16;
     acc = (lo > hi ? lo : hi) << 16;
@@ -285,20 +329,34 @@ __device__ __forceinline__ void flush_amax(uint32_t acc, QShared& sh, int t) {
   if ((threadIdx.x & 63) == 0 && acc != 0) atomicMax(&sh.amax[t], acc);
 }
 
-// Fill the per-tensor constants (one thread per tensor) and zero the block's amax
-// slots.  Contains a barrier: every thread of the block calls it exactly once.
-__device__ __forceinline__ void setup_shared(const QTable& tab, QShared& sh) {
+// The per-tensor constants of entry t (one thread per tensor).
+template <class Tab, class Sh>
+__device__ __forceinline__ void setup_entry(const Tab& tab, Sh& sh, int t) {
+  const float s = *tab.e[t].scale;
+  sh.scale[t] = s;
+  sh.rcp[t] = 1.0f / s;
+  // the window needs r normal and every residual exact (see the division notes)
+  sh.win[t] = (s >= 0x1p-80f) && (s <= 0x1p125f);
+  const uint32_t lim = as_uint(s * 0x1p126f);  // +inf when s >= 4
+  sh.xlim[t] = tab.e[t].dtype == FP8Q_BF16 ? min(lim >> 16, 0x7F80u) : min(lim, 0x7F800000u);
+  sh.amax[t] = 0;
+}
+
+// Fill the per-tensor constants and zero the block's amax slots; for a planned table
+// also note whether any tensor's scale lies outside the window.  Contains a barrier:
+// every thread of the block calls it exactly once.
+template <class Tab, class Sh>
+__device__ __forceinline__ void setup_shared(const Tab& tab, Sh& sh) {
   const int tid = threadIdx.x;
-  if (tid < tab.n) {
-    const float s = *tab.e[tid].scale;
-    sh.scale[tid] = s;
-    sh.rcp[tid] = 1.0f / s;
-    // the window needs r normal and every residual exact (see the division notes)
-    sh.win[tid] = (s >= 0x1p-80f) && (s <= 0x1p125f);
-    const uint32_t lim = as_uint(s * 0x1p126f);  // +inf when s >= 4
-    sh.xlim[tid] = tab.e[tid].dtype == FP8Q_BF16 ? min(lim >> 16, 0x7F80u)
-                                                 : min(lim, 0x7F800000u);
-    sh.amax[tid] = 0;
+  if constexpr (Tab::kPlanned) {
+    uint32_t out = 0;
+    for (int t = tid; t < tab.n; t += kQBlock) {
+      setup_entry(tab, sh, t);
+      out |= sh.win[t] ^ 1u;
+    }
+    sh.any_out = __syncthreads_or(out) != 0;
+  } else {
+    if (tid < tab.n) setup_entry(tab, sh, tid);
   }
   __syncthreads();
 }
@@ -307,32 +365,35 @@ __device__ __forceinline__ void setup_shared(const QTable& tab, QShared& sh) {
 // The full chunks of one run of same-kind tensors, [f0, f1), are split over the grid:
 // grid-stride (block b owns f0' + b + kG, the whole grid streams one window of memory)
 // or contiguous ranges (block b owns [f0 + (f1-f0)*b/G, f0 + (f1-f0)*(b+1)/G)).
-#ifndef FP8Q_Q_SCHEDULE
-#define FP8Q_Q_SCHEDULE 1
-#endif
+// Both table forms use the grid-stride split: for the 1152-tensor list of 4-64-chunk
+// tensors, contiguous ranges per block (a block then changes tensor only at tensor
+// boundaries) ran 460 us against 360 us, as for large tensors the chip streaming one
+// window of memory at a time wins.
 struct Owned {
   int64_t first;  // first owned chunk (>= limit: none)
   int64_t limit;  // owned chunks are < limit
   int64_t step;
 };
 
+template <bool kContig>
 __device__ __forceinline__ Owned owned_chunks(int64_t f0, int64_t f1) {
   const int64_t G = gridDim.x, b = blockIdx.x;
   Owned o;
-#if FP8Q_Q_SCHEDULE == 1
-  o.first = f0 + ((b - f0 % G) % G + G) % G;
-  o.limit = f1;
-  o.step = G;
-#else
-  o.first = f0 + (f1 - f0) * b / G;
-  o.limit = f0 + (f1 - f0) * (b + 1) / G;
-  o.step = 1;
-#endif
+  if constexpr (!kContig) {
+    o.first = f0 + ((b - f0 % G) % G + G) % G;
+    o.limit = f1;
+    o.step = G;
+  } else {
+    o.first = f0 + (f1 - f0) * b / G;
+    o.limit = f0 + (f1 - f0) * (b + 1) / G;
+    o.step = 1;
+  }
   return o;
 }
 
 // Full-chunk range [f0, f1) of the run (same-kind tensors) holding table entry t.
-__device__ __forceinline__ void run_bounds(const QTable& tab, int t, int64_t& f0, int64_t& f1) {
+template <class Tab>
+__device__ __forceinline__ void run_bounds(const Tab& tab, int t, int64_t& f0, int64_t& f1) {
   const int kind = entry_kind(tab.e[t]);
   const int tb = kind > 0 ? tab.run_end[kind - 1] : 0;
   const int te = tab.run_end[kind];
@@ -391,10 +452,10 @@ __device__ __forceinline__ void elementwise_units(const void* __restrict__ src,
 // speculatively (assuming that tensor's scale is in the window) before the per-tensor
 // constants are set up, so the block's first HBM requests do not wait for the scale
 // loads, the reciprocals and the barrier.
-template <bool kBF16, int kFmt, bool kGelu>
-__device__ __forceinline__ void run_full_chunks(const QTable& tab, QShared& sh, int t_begin,
+template <bool kBF16, int kFmt, bool kGelu, class Tab, class Sh>
+__device__ __forceinline__ void run_full_chunks(const Tab& tab, Sh& sh, int t_begin,
                                                 int t_end, bool setup) {
-  constexpr int kD = kQDepth;  // passes in flight ahead
+  constexpr int kD = Tab::kPlanned ? kQPlanDepth : kQDepth;  // passes in flight ahead
   constexpr int kL = kBF16 ? 1 : 2;                // 16-byte loads per group
   constexpr int kU = kBF16 ? kQPass : kQPass / 2;  // groups per pass
   constexpr int kP = kQUnroll / kU;                // passes per chunk
@@ -405,7 +466,7 @@ __device__ __forceinline__ void run_full_chunks(const QTable& tab, QShared& sh, 
   // first chunk of this block in the run, and the tensor holding it
   int64_t f0, f1;
   run_bounds(tab, t_begin, f0, f1);
-  const Owned own = owned_chunks(f0, f1);
+  const Owned own = owned_chunks<Tab::kContig>(f0, f1);
   int64_t j = own.first;
   int t = t_begin;
   auto settle = [&](int& tt, int64_t& jj) __attribute__((always_inline)) {  // move (tt, jj) to a chunk this phase does
@@ -414,7 +475,11 @@ __device__ __forceinline__ void run_full_chunks(const QTable& tab, QShared& sh, 
       if (jj >= own.limit) {
         tt = t_end;
       } else if (jj >= end) {
-        ++tt;
+        if constexpr (Tab::kPlanned) {
+          tt = tab.chunk_entry[jj];  // jj < own.limit <= the run's end: a chunk of the run
+        } else {
+          ++tt;
+        }
       } else if (!sh.win[tt]) {  // skip the tensor: next owned chunk at or after its end
         jj += (end - jj + own.step - 1) / own.step * own.step;
         ++tt;
@@ -507,7 +572,11 @@ __device__ __forceinline__ void run_full_chunks(const QTable& tab, QShared& sh, 
   int ts = t_begin;  // speculative first position: chunk ranges only
   int64_t js = j;
   if (setup) {
-    while (ts < t_end && js < own.limit && js >= tab.e[ts].fbegin + tab.e[ts].nfull) ++ts;
+    if constexpr (Tab::kPlanned) {
+      if (js < own.limit) ts = tab.chunk_entry[js];
+    } else {
+      while (ts < t_end && js < own.limit && js >= tab.e[ts].fbegin + tab.e[ts].nfull) ++ts;
+    }
     if (js >= own.limit) ts = t_end;
     if (ts < t_end) load_pass(buf[0], view(ts), js, 0, true);
     setup_shared(tab, sh);
@@ -632,18 +701,19 @@ __device__ __forceinline__ void run_full_chunks(const QTable& tab, QShared& sh, 
 // Per tensor t: this block's full chunks if the scale is outside the window (all
 // element-wise), and the tensor's remainder -- the units past its last full chunk:
 // aligned groups, then the scalar head/tail -- done by block t mod G.
-template <bool kBF16, int kFmt, bool kGelu>
-__device__ __forceinline__ void tensor_rest(const QTable& tab, QShared& sh, int t) {
+template <bool kBF16, int kFmt, bool kGelu, class Tab, class Sh>
+__device__ __forceinline__ void tensor_rest(const Tab& tab, Sh& sh, int t, bool full = true,
+                                            bool rest = true) {
   const QEntry& e = tab.e[t];
   const int64_t G = gridDim.x, b = blockIdx.x;
   const float s = uniform(sh.scale[t]);
   const bool win = uniform(sh.win[t]) != 0;
   uint32_t acc = 0;
   bool touched = false;
-  if (!win) {
+  if (full && !win) {
     int64_t f0, f1;
     run_bounds(tab, t, f0, f1);
-    const Owned own = owned_chunks(f0, f1);
+    const Owned own = owned_chunks<Tab::kContig>(f0, f1);
     // this block's chunks of tensor t, in the same ownership as phase 1
     int64_t jj = own.first;
     if (jj < e.fbegin) jj += (e.fbegin - jj + own.step - 1) / own.step * own.step;
@@ -656,7 +726,7 @@ __device__ __forceinline__ void tensor_rest(const QTable& tab, QShared& sh, int 
     }
   }
   const int64_t u0 = e.nfull * kQChunk;
-  if (u0 < e.n_units && t % G == b) {
+  if (rest && u0 < e.n_units && t % G == b) {
     touched = true;
     if (win) {
       constexpr int esz = kBF16 ? 2 : 4;
@@ -697,8 +767,8 @@ struct KindTraits {
 };
 
 // Phase 1 for the run of kind kKind, if the instance handles that kind.
-template <int kSrc, int kKind>
-__device__ __forceinline__ void phase1_run(const QTable& tab, QShared& sh, int& tb, bool& ready) {
+template <int kSrc, int kKind, class Tab, class Sh>
+__device__ __forceinline__ void phase1_run(const Tab& tab, Sh& sh, int& tb, bool& ready) {
   using T = KindTraits<kKind>;
   const int te = tab.run_end[kKind];
   if constexpr ((kSrc & T::kSrcBit) != 0) {
@@ -711,11 +781,24 @@ __device__ __forceinline__ void phase1_run(const QTable& tab, QShared& sh, int& 
 }
 
 // Phase 2 for table entry t if its kind is kKind.
-template <int kSrc, int kKind>
-__device__ __forceinline__ void phase2_entry(const QTable& tab, QShared& sh, int t, int kind) {
+template <int kSrc, int kKind, class Tab, class Sh>
+__device__ __forceinline__ void phase2_entry(const Tab& tab, Sh& sh, int t, int kind,
+                                             bool full = true, bool rest = true) {
   using T = KindTraits<kKind>;
   if constexpr ((kSrc & T::kSrcBit) != 0)
-    if (kind == kKind) tensor_rest<T::kBF16, T::kFmt, T::kGelu>(tab, sh, t);
+    if (kind == kKind) tensor_rest<T::kBF16, T::kFmt, T::kGelu>(tab, sh, t, full, rest);
+}
+
+template <int kSrc, class Tab, class Sh>
+__device__ __forceinline__ void phase2_dispatch(const Tab& tab, Sh& sh, int t, bool full,
+                                                bool rest) {
+  const int kind = entry_kind(tab.e[t]);  // uniform
+  phase2_entry<kSrc, 0>(tab, sh, t, kind, full, rest);
+  phase2_entry<kSrc, 1>(tab, sh, t, kind, full, rest);
+  phase2_entry<kSrc, 2>(tab, sh, t, kind, full, rest);
+  phase2_entry<kSrc, 3>(tab, sh, t, kind, full, rest);
+  phase2_entry<kSrc, 4>(tab, sh, t, kind, full, rest);
+  phase2_entry<kSrc, 5>(tab, sh, t, kind, full, rest);
 }
 
 // ---------------------------------------------------------------- appended update
@@ -725,7 +808,8 @@ __device__ __forceinline__ void phase2_entry(const QTable& tab, QShared& sh, int
 // the count), so waiting for the atomics to complete is enough: a device-scope fence
 // would write back and invalidate the XCD's L2 in every block.  Contains barriers:
 // every thread of the block calls it once.
-__device__ __forceinline__ bool finished_last(uint32_t* counter, QShared& sh) {
+template <class Sh>
+__device__ __forceinline__ bool finished_last(uint32_t* counter, Sh& sh) {
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this thread's amax atomic performed
   __syncthreads();
   if (threadIdx.x == 0) sh.last = atomicAdd(counter, 1u) == gridDim.x - 1 ? 1u : 0u;
@@ -803,9 +887,9 @@ __device__ void update_in_block(const QUpdate& u, uint32_t* colmax) {
   if (tid == 0) __hip_atomic_store(u.counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <int kSrc, bool kUpd>
-__global__ __launch_bounds__(kQBlock) void quantize_amax_kernel(const QTable tab) {
-  __shared__ QShared sh;
+// Phases 1 and 2 of a launch and the block's amax atomics.
+template <int kSrc, class Tab, class Sh>
+__device__ __forceinline__ void quantize_body(const Tab& tab, Sh& sh) {
   const int n = tab.n;
   const int tid = threadIdx.x;
 
@@ -820,22 +904,40 @@ __global__ __launch_bounds__(kQBlock) void quantize_amax_kernel(const QTable tab
   phase1_run<kSrc, 5>(tab, sh, tb, ready);
   if (!ready) setup_shared(tab, sh);
   // phase 2
-  for (int t = 0; t < n; ++t) {
-    const int kind = entry_kind(tab.e[t]);  // uniform
-    phase2_entry<kSrc, 0>(tab, sh, t, kind);
-    phase2_entry<kSrc, 1>(tab, sh, t, kind);
-    phase2_entry<kSrc, 2>(tab, sh, t, kind);
-    phase2_entry<kSrc, 3>(tab, sh, t, kind);
-    phase2_entry<kSrc, 4>(tab, sh, t, kind);
-    phase2_entry<kSrc, 5>(tab, sh, t, kind);
+  if constexpr (Tab::kPlanned) {
+    // many entries: the remainders of tensors b, b + G, ..., and only when some scale is
+    // outside the window (rare) a pass over every entry for their full chunks
+    for (int t = blockIdx.x; t < n; t += gridDim.x) phase2_dispatch<kSrc>(tab, sh, t, false, true);
+    if (sh.any_out)
+      for (int t = 0; t < n; ++t)
+        if (!uniform(sh.win[t])) phase2_dispatch<kSrc>(tab, sh, t, true, false);
+    __syncthreads();
+    // one global atomic per tensor this block saw a non-zero |x| in
+    for (int t = tid; t < n; t += kQBlock)
+      if (sh.amax[t] != 0) amax_accumulate(tab.e[t].amax, sh.amax[t]);
+  } else {
+    for (int t = 0; t < n; ++t) phase2_dispatch<kSrc>(tab, sh, t, true, true);
+    __syncthreads();
+    // one global atomic per tensor this block saw a non-zero |x| in
+    if (tid < n && sh.amax[tid] != 0) amax_accumulate(tab.e[tid].amax, sh.amax[tid]);
   }
-  __syncthreads();
-  // one global atomic per tensor this block saw a non-zero |x| in
-  if (tid < n && sh.amax[tid] != 0) amax_accumulate(tab.e[tid].amax, sh.amax[tid]);
+}
+
+template <int kSrc, bool kUpd>
+__global__ __launch_bounds__(kQBlock) void quantize_amax_kernel(const QTable tab) {
+  __shared__ QShared sh;
+  quantize_body<kSrc>(tab, sh);
   if constexpr (kUpd) {
     __shared__ uint32_t colmax[kQUpdMaxCols];
     if (finished_last(tab.upd.counter, sh)) update_in_block(tab.upd, colmax);
   }
+}
+
+// A planned table of up to kQPlanMaxEntries tensors (fp8_multi_quantize_amax_planned).
+template <int kSrc>
+__global__ __launch_bounds__(kQBlock) void quantize_amax_planned_kernel(const QPlanTable tab) {
+  __shared__ QSharedT<kQPlanMaxEntries> sh;
+  quantize_body<kSrc>(tab, sh);
 }
 
 // ---------------------------------------------------------------- host side
@@ -990,12 +1092,172 @@ static int quantize_entries(const fp8q_tensor* tensors, int n, bool gelu, hipStr
   return FP8Q_OK;
 }
 
+// ---------------------------------------------------------------- planned tables
+// What fp8_multi_quantize_plan records in the caller's fp8q_plan (opaque to the caller).
+struct PlanRec {
+  const QEntry* table;  // the planned entries, in the caller's device workspace
+  const int32_t* chunk_entry;  // after them: the entry of every full chunk
+  int64_t total_full;
+  int64_t units;        // all units of all entries (0: nothing to launch)
+  int32_t n;
+  int32_t src_kinds;    // bit 0: bf16 sources, bit 1: fp32 sources
+  int32_t run_end[kQKinds];
+  uint32_t magic;
+};
+static_assert(sizeof(PlanRec) <= sizeof(fp8q_plan), "the plan record fits the descriptor");
+constexpr uint32_t kPlanMagic = 0x51385046u;
+constexpr int kPlanChunk = 128;  // entries staged on the host per copy
+constexpr int kMapChunk = 4096;  // chunk-map words staged on the host per copy
+
+static int64_t entries_bytes(int n) { return ((int64_t)n * (int64_t)sizeof(QEntry) + 15) / 16 * 16; }
+
+// Workspace bytes of a plan of these (validated) entries: the entries, then one int32
+// per full chunk.
+static int64_t plan_bytes(const fp8q_tensor* tensors, int n) {
+  if (n <= 0) return 0;
+  int64_t full = 0;
+  for (int i = 0; i < n; ++i) {
+    QEntry e;
+    plan_entry(tensors[i], false, &e);
+    full += e.nfull;
+  }
+  return entries_bytes(n) + 4 * full;
+}
+
+// Validate and plan n entries (grouped by kind, stable within a kind, as in QTable), copy
+// the planned entries into the device workspace and fill *rec.  The copies come from host
+// memory (staged kPlanChunk entries at a time on the stack), which HIP performs
+// synchronously: the call returns with the table in place.
+static int build_plan(const fp8q_tensor* tensors, int n, void* workspace, int64_t bytes,
+                      PlanRec* rec, hipStream_t stream) {
+  int st = validate_entries(tensors, n, false);
+  if (st != FP8Q_OK) return st;
+  if (n > kQPlanMaxEntries) return FP8Q_EUNSUPPORTED;
+  if (n > 0 && (workspace == nullptr || (uintptr_t)workspace % 16 != 0 ||
+                bytes < plan_bytes(tensors, n)))
+    return FP8Q_EINVAL;
+  int16_t order[kQPlanMaxEntries];  // output position -> input index
+  int32_t count[kQKinds] = {};
+  for (int i = 0; i < n; ++i) ++count[tensors[i].src_dtype * 2 + tensors[i].format];
+  int32_t pos[kQKinds];
+  for (int k = 0, at = 0; k < kQKinds; ++k) {
+    pos[k] = at;
+    at += count[k];
+    rec->run_end[k] = at;
+  }
+  for (int i = 0; i < n; ++i) order[pos[tensors[i].src_dtype * 2 + tensors[i].format]++] = (int16_t)i;
+  QEntry stage[kPlanChunk];
+  rec->total_full = 0;
+  rec->units = 0;
+  rec->src_kinds = 0;
+  for (int p0 = 0; p0 < n; p0 += kPlanChunk) {
+    const int m = n - p0 < kPlanChunk ? n - p0 : kPlanChunk;
+    for (int j = 0; j < m; ++j) {
+      const fp8q_tensor& t = tensors[order[p0 + j]];
+      plan_entry(t, false, &stage[j]);
+      stage[j].fbegin = rec->total_full;
+      rec->total_full += stage[j].nfull;
+      rec->units += stage[j].n_units;
+      rec->src_kinds |= t.src_dtype == FP8Q_BF16 ? 1 : 2;
+    }
+    if (hipMemcpyAsync((QEntry*)workspace + p0, stage, m * sizeof(QEntry),
+                       hipMemcpyHostToDevice, stream) != hipSuccess)
+      return FP8Q_EHIP;
+  }
+  // the entry of every full chunk, in the planned order
+  int32_t* map = (int32_t*)((char*)workspace + entries_bytes(n));
+  int32_t words[kMapChunk];
+  int m = 0;
+  int64_t at = 0;
+  for (int p = 0; p < n; ++p) {
+    QEntry e;
+    plan_entry(tensors[order[p]], false, &e);
+    for (int64_t c = 0; c < e.nfull; ++c) {
+      words[m++] = p;
+      if (m == kMapChunk) {
+        if (hipMemcpyAsync(map + at, words, m * 4, hipMemcpyHostToDevice, stream) != hipSuccess)
+          return FP8Q_EHIP;
+        at += m;
+        m = 0;
+      }
+    }
+  }
+  if (m > 0 &&
+      hipMemcpyAsync(map + at, words, m * 4, hipMemcpyHostToDevice, stream) != hipSuccess)
+    return FP8Q_EHIP;
+  rec->table = (const QEntry*)workspace;
+  rec->chunk_entry = map;
+  rec->n = n;
+  rec->magic = kPlanMagic;
+  return FP8Q_OK;
+}
+
+// One launch of the planned kernel over every entry of the plan.
+static int launch_planned(const PlanRec& rec, hipStream_t stream) {
+  if (rec.units == 0) return FP8Q_OK;
+  int cus = 0;
+  int st = current_device_cus(&cus);
+  if (st != FP8Q_OK) return st;
+  const void* fn = rec.src_kinds == 1   ? (const void*)quantize_amax_planned_kernel<1>
+                   : rec.src_kinds == 2 ? (const void*)quantize_amax_planned_kernel<2>
+                                        : (const void*)quantize_amax_planned_kernel<3>;
+  static std::atomic<int> fit[4];
+  int per_cu = fit[rec.src_kinds & 3].load(std::memory_order_relaxed);
+  if (per_cu <= 0) {
+    int occ = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, fn, kQBlock, 0) != hipSuccess)
+      return FP8Q_EHIP;
+    per_cu = occ < kQPlanBlocksPerCU ? (occ > 0 ? occ : 1) : kQPlanBlocksPerCU;
+    fit[rec.src_kinds & 3].store(per_cu, std::memory_order_relaxed);
+  }
+  const int64_t max_blocks = (int64_t)cus * per_cu;
+  int64_t blocks = rec.total_full > rec.n ? rec.total_full : rec.n;
+  if (blocks > max_blocks) blocks = max_blocks;
+  if (blocks < 1) blocks = 1;
+  QPlanTable tab;
+  tab.e = rec.table;
+  tab.chunk_entry = rec.chunk_entry;
+  tab.total_full = rec.total_full;
+  tab.n = rec.n;
+  for (int k = 0; k < kQKinds; ++k) tab.run_end[k] = rec.run_end[k];
+  void* args[] = {&tab};
+  return launch_status(hipLaunchKernel(fn, dim3((unsigned)blocks), dim3(kQBlock), args, 0, stream));
+}
+
 }  // namespace fp8q
 
 using namespace fp8q;
 
 extern "C" int fp8_multi_quantize_amax(const fp8q_tensor* tensors, int n, void* stream) {
   return quantize_entries(tensors, n, false, (hipStream_t)stream);
+}
+
+extern "C" int64_t fp8_multi_quantize_plan_bytes(const fp8q_tensor* tensors, int n) {
+  const int st = validate_entries(tensors, n, false);
+  if (st != FP8Q_OK) return st;
+  if (n > kQPlanMaxEntries) return FP8Q_EUNSUPPORTED;
+  return plan_bytes(tensors, n);
+}
+
+extern "C" int fp8_multi_quantize_plan(const fp8q_tensor* tensors, int n, void* workspace,
+                                       int64_t workspace_bytes, fp8q_plan* plan, void* stream) {
+  if (plan == nullptr) return FP8Q_EINVAL;
+  PlanRec rec{};
+  const int st = build_plan(tensors, n, workspace, workspace_bytes, &rec, (hipStream_t)stream);
+  if (st != FP8Q_OK) return st;
+  *plan = fp8q_plan{};
+  memcpy(plan, &rec, sizeof(rec));
+  return FP8Q_OK;
+}
+
+extern "C" int fp8_multi_quantize_amax_planned(const fp8q_plan* plan, void* stream) {
+  if (plan == nullptr) return FP8Q_EINVAL;
+  PlanRec rec;
+  memcpy(&rec, plan, sizeof(rec));
+  if (rec.magic != kPlanMagic || rec.n < 0 || rec.n > kQPlanMaxEntries ||
+      (rec.n > 0 && rec.table == nullptr))
+    return FP8Q_EINVAL;
+  return launch_planned(rec, (hipStream_t)stream);
 }
 
 extern "C" int fp8_multi_quantize_amax_timed(const fp8q_tensor* tensors, int n, void* stream,

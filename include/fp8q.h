@@ -121,6 +121,56 @@ int fp8_quantize_amax(const void* src, int src_dtype, uint8_t* dst, int64_t nume
 int fp8_multi_quantize_amax(const fp8q_tensor* tensors, int n, void* stream);
 
 /*
+ * A plan: a list of up to 2048 quantize entries laid out once in a caller-owned device
+ * workspace, so that every later call quantizes the whole list in ONE kernel launch with
+ * no per-call host work beyond the launch (the per-call launches of many small ops are
+ * what "Implement fused kernel for FP8 scale update" profiles; a list longer than the 32
+ * entries one launch of fp8_multi_quantize_amax takes would otherwise need several
+ * launches).  The plan holds the entries' pointers and sizes; the tensors' contents and
+ * their scales and amaxes are read when the planned launch runs, so one plan serves
+ * every step while the buffers stay in place.  Opaque to the caller; filled by
+ * fp8_multi_quantize_plan.
+ */
+typedef struct fp8q_plan {
+  uint64_t opaque[16];
+} fp8q_plan;
+
+/* Bytes of device workspace the plan of these n entries needs: 96 per entry (rounded
+ * up to a multiple of 16) plus 4 per full chunk of 16384 aligned elements (0 for n ==
+ * 0).  Negative: the status the plan call would return for this list (FP8Q_EINVAL,
+ * FP8Q_EUNSUPPORTED). */
+int64_t fp8_multi_quantize_plan_bytes(const fp8q_tensor* tensors, int n);
+
+/*
+ * fp8_multi_quantize_plan -- validate a list of n quantize entries (as
+ * fp8_multi_quantize_amax) and lay it out in `workspace` for
+ * fp8_multi_quantize_amax_planned.  The layout is copied from host memory with
+ * hipMemcpyAsync on `stream`, which HIP performs synchronously for host memory that is
+ * not page-locked: the call returns with the workspace written, after the work enqueued
+ * before it on the stream.  A set-up call, not one per step; not for graph capture.
+ *   tensors    HOST array of n entries (bf16 or fp32 sources; no gelu), read during the
+ *              call only.
+ *   n          0 .. 2048 (more: FP8Q_EUNSUPPORTED).
+ *   workspace  DEVICE memory of at least fp8_multi_quantize_plan_bytes(tensors, n) bytes,
+ *              16-byte aligned, caller-owned; it must stay allocated and unchanged while
+ *              the plan is in use, and not be rewritten while a planned launch reading
+ *              it may still run.  (NULL allowed when n == 0.)
+ *   plan       HOST descriptor, filled on success.
+ * Returns FP8Q_OK, FP8Q_EINVAL, FP8Q_EUNSUPPORTED or FP8Q_EHIP.
+ */
+int fp8_multi_quantize_plan(const fp8q_tensor* tensors, int n, void* workspace,
+                            int64_t workspace_bytes, fp8q_plan* plan, void* stream);
+
+/*
+ * fp8_multi_quantize_amax_planned -- fp8_multi_quantize_amax over every entry of a plan,
+ * in one kernel launch (none when every entry is empty).  Same results as
+ * fp8_multi_quantize_amax on the planned list.  Asynchronous: only enqueues the launch.
+ *   plan       HOST descriptor filled by fp8_multi_quantize_plan.
+ * Returns FP8Q_OK, FP8Q_EINVAL (a descriptor that no plan call filled) or FP8Q_EHIP.
+ */
+int fp8_multi_quantize_amax_planned(const fp8q_plan* plan, void* stream);
+
+/*
  * fp8_multi_quantize_amax_timed -- fp8_multi_quantize_amax with profiling events: the
  * same validation, kernels and results, each kernel launched with hipExtLaunchKernel so
  * that the events take the start and stop time of the kernel's own dispatch rather than

@@ -21,7 +21,8 @@ def test_header_declares_the_boundary():
     assert declared_functions() == sorted([
         "fp8_quantize_amax", "fp8_multi_quantize_amax", "fp8_multi_quantize_amax_timed",
         "fp8_gelu_quantize_amax", "fp8_layernorm_quantize_amax", "fp8_quantize_amax_and_update", "fp8_dequantize", "fp8_amax_and_scale_update",
-        "fp8_gemm", "fp8_status_string"])
+        "fp8_gemm", "fp8_status_string", "fp8_multi_quantize_plan_bytes",
+        "fp8_multi_quantize_plan", "fp8_multi_quantize_amax_planned"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -227,3 +228,47 @@ def test_fused_step_rejects_before_enqueue():
     assert _step(d, arr, 2, ws=None) == d.EINVAL      # NULL workspace
     # empty tensors and an empty update: nothing to enqueue
     assert _step(d, arr, 2, n=0) == d.OK
+
+
+def test_plan_layout_and_validation():
+    """Plans: the descriptor is 128 bytes, the workspace 96 bytes per entry (rounded to
+    16) plus 4 per full chunk; invalid lists,
+    too many entries, a missing, misaligned or short workspace, or a descriptor no plan
+    call filled are refused before anything is copied or launched."""
+    import ctypes
+    import delayed_scaling_amax_amd as d
+    assert ctypes.sizeof(d.fp8q_plan) == 128
+    plan = d.fp8q_plan()
+    arr = (d.fp8q_tensor * 2049)()
+    for i in range(2049):
+        arr[i] = d.fp8q_tensor(None, None, 0, i % 2, i % 2, BAD, BAD)
+    B = d.lib.fp8_multi_quantize_plan_bytes
+    assert B(arr, 0) == 0
+    assert B(arr, 3) == 3 * 96 + 0      # empty tensors: no chunks (288 is a multiple of 16)
+    assert B(arr, 1) == 96
+    assert B(arr, 2049) == d.EUNSUPPORTED
+    # a bf16 tensor of 3 * 16384 + 5 elements at a 16-byte aligned address: 3 full chunks
+    one = (d.fp8q_tensor * 1)()
+    one[0] = d.fp8q_tensor(0x20000, 0x40000, 3 * 16384 + 5, 0, 0, BAD, BAD)
+    assert B(one, 1) == 96 + 3 * 4
+    one[0].src_dtype = 7
+    assert B(one, 1) == d.EINVAL
+    ws = 0x10000  # 16-byte aligned, never dereferenced (validation fails first)
+    P = d.lib.fp8_multi_quantize_plan
+    assert P(arr, 2049, ws, 1 << 30, ctypes.byref(plan), None) == d.EUNSUPPORTED
+    assert P(arr, 4, None, 1 << 20, ctypes.byref(plan), None) == d.EINVAL      # no workspace
+    assert P(arr, 4, ws + 8, 1 << 20, ctypes.byref(plan), None) == d.EINVAL    # misaligned
+    assert P(arr, 4, ws, 4 * 96 - 1, ctypes.byref(plan), None) == d.EINVAL     # too short
+    assert P(arr, 4, ws, 4 * 96, None, None) == d.EINVAL                       # no descriptor
+    assert P(arr, -1, ws, 1 << 20, ctypes.byref(plan), None) == d.EINVAL
+    bad = (d.fp8q_tensor * 1)()
+    bad[0] = d.fp8q_tensor(None, None, 5, 0, 0, BAD, BAD)                       # NULL src
+    assert P(bad, 1, ws, 1 << 20, ctypes.byref(plan), None) == d.EINVAL
+    bad[0] = d.fp8q_tensor(BAD, BAD, 5, 0, 9, BAD, BAD)                         # bad format
+    assert P(bad, 1, ws, 1 << 20, ctypes.byref(plan), None) == d.EINVAL
+    assert all(w == 0 for w in plan.opaque)                                     # untouched
+    assert d.lib.fp8_multi_quantize_amax_planned(ctypes.byref(plan), None) == d.EINVAL
+    assert d.lib.fp8_multi_quantize_amax_planned(None, None) == d.EINVAL
+    # an empty list needs no workspace, copies nothing and launches nothing
+    assert P(arr, 0, None, 0, ctypes.byref(plan), None) == d.OK
+    assert d.lib.fp8_multi_quantize_amax_planned(ctypes.byref(plan), None) == d.OK

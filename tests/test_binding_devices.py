@@ -42,6 +42,8 @@ CASES = {
     "multi_timed": lambda: d.fp8_multi_quantize_amax_timed(
         [(_cpu(16, torch.bfloat16), _cpu(16, torch.uint8), _cpu(1), _cpu(1), d.E4M3)],
         None, None),
+    "plan": lambda: d.fp8_multi_quantize_plan(
+        [(_cpu(16, torch.bfloat16), _cpu(16, torch.uint8), _cpu(1), _cpu(1), d.E4M3)]),
     "dequantize": lambda: d.fp8_dequantize(_cpu(16, torch.uint8), _cpu(16), _cpu(1), d.E4M3),
     "gemm": lambda: d.fp8_gemm(_cpu(256, torch.uint8).view(16, 16), d.E4M3,
                                _cpu(256, torch.uint8).view(16, 16), d.E4M3, _cpu(1), _cpu(1),

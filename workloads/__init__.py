@@ -29,6 +29,13 @@ design notes list):
   mlp_4096_preact   the FFN pre-activation of mlp_4096, (2048,4,16384) bf16 ~ N(0,1/3):
                     the dense output of U[0,1) inputs (E[x^2] = 1/3) through unit-
                     variance fan_in weights; the input of the gelu-fused quantize.
+  list_1152         the 1152 FP8 tensors of the batched-update layout (96 layers x 4
+                    linear modules x input, weight, gradient) as one quantize list, at
+                    hidden 512 and 128 tokens: per layer the inputs (128,512) x3 and
+                    (128,2048), weights 512x1536, 512x512, 512x2048, 2048x512, output
+                    gradients (128,1536), (128,512), (128,2048), (128,512); inputs
+                    N(0,1), weights N(0,1/fan_in), gradients N(0,1e-4) (variance), as in
+                    mlp_12288; inputs and weights E4M3, gradients E5M2.
 """
 from __future__ import annotations
 
@@ -245,6 +252,34 @@ def mlp_4096_preact(threads=None, ffn=16384, seq=2048, batch=4) -> Workload:
                     [QTensor("h", h, E4M3)], history_len=16, first_scale=[1.0])
 
 
+def list_1152(threads=None, hidden=512, tokens=128, layers=96) -> Workload:
+    """The c4 layout's tensors with concrete shapes, in module order (input, weight,
+    gradient per linear: qkv, attention output, fc1, fc2)."""
+    th = threads or default_threads()
+    h, t = hidden, tokens
+    linears = [((t, h), (h, 3 * h), (t, 3 * h)), ((t, h), (h, h), (t, h)),
+               ((t, h), (h, 4 * h), (t, 4 * h)), ((t, 4 * h), (4 * h, h), (t, h))]
+    specs = []  # (name, stream id, shape, sampler, format)
+    for layer in range(layers):
+        for m, (xs, ws, gs) in enumerate(linears):
+            k = len(specs)
+            specs.append(("l%d.m%d.x" % (layer, m), k, xs, _normal(1.0), E4M3))
+            specs.append(("l%d.m%d.w" % (layer, m), k + 1, ws,
+                          _normal(math.sqrt(1.0 / ws[0])), E4M3))
+            specs.append(("l%d.m%d.g" % (layer, m), k + 2, gs, _normal(math.sqrt(1e-4)), E5M2))
+
+    def make_one(sp):  # each tensor from its own streams: the same bytes in any order
+        name, k, shape, sampler, fmt = sp
+        return QTensor(name, _generate(7, k, shape, np.uint16, sampler, 1), fmt)
+
+    with ThreadPoolExecutor(max(1, th)) as ex:
+        tensors = list(ex.map(make_one, specs))
+    return Workload("list_%d" % len(tensors),
+                    "%d tensors: %d layers x 4 linears x (input, weight, gradient) at hidden "
+                    "%d, %d tokens" % (len(tensors), layers, h, t),
+                    tensors, history_len=1024, first_scale=[1.0] * len(tensors))
+
+
 WORKLOADS = {
     "single_1024": single_1024,
     "mlp_4096": mlp_4096,
@@ -252,6 +287,7 @@ WORKLOADS = {
     "update_1152": update_1152,
     "mlp_12288": mlp_12288,
     "mlp_4096_preact": mlp_4096_preact,
+    "list_1152": list_1152,
 }
 
 
