@@ -82,13 +82,14 @@ def _load():
     lib.fp8_multi_quantize_plan.argtypes = [ctypes.POINTER(fp8q_tensor), i32, vp, i64,
                                             ctypes.POINTER(fp8q_plan), vp]
     lib.fp8_multi_quantize_amax_planned.argtypes = [ctypes.POINTER(fp8q_plan), vp]
+    lib.fp8_multi_quantize_amax_noalloc.argtypes = [ctypes.POINTER(fp8q_tensor), i32, vp]
     lib.fp8_status_string.argtypes = [i32]
     lib.fp8_status_string.restype = ctypes.c_char_p
     for f in ("fp8_quantize_amax", "fp8_multi_quantize_amax", "fp8_multi_quantize_amax_timed",
               "fp8_gelu_quantize_amax",
               "fp8_layernorm_quantize_amax", "fp8_gemm", "fp8_dequantize", "fp8_amax_and_scale_update",
               "fp8_quantize_amax_and_update", "fp8_multi_quantize_plan",
-              "fp8_multi_quantize_amax_planned"):
+              "fp8_multi_quantize_amax_planned", "fp8_multi_quantize_amax_noalloc"):
         getattr(lib, f).restype = i32
     return lib
 
@@ -322,6 +323,20 @@ def fp8_multi_quantize_amax_planned(plan: Plan) -> None:
             ctypes.byref(plan.desc), _stream(plan.device)))
 
 
+def fp8_multi_quantize_amax_noalloc(entries) -> None:
+    """fp8_multi_quantize_amax in one launch with the plan in the library's fixed device
+    array (no device allocation; at most 2048 entries).  Calls that may overlap on one
+    device race on that array."""
+    entries = list(entries)
+    if not entries:
+        return
+    dev = _device(entries[0][0], "entry 0 src")
+    arr = _entry_table(entries, dev)
+    with torch.cuda.device(dev):
+        _check("fp8_multi_quantize_amax_noalloc",
+               lib.fp8_multi_quantize_amax_noalloc(arr, len(entries), _stream(dev)))
+
+
 def fp8_dequantize(src: torch.Tensor, dst: torch.Tensor, scale: torch.Tensor,
                    format: int) -> None:
     dev = _device(src, "src")
@@ -390,6 +405,7 @@ def fp8_quantize_amax_and_update(entries, amax: torch.Tensor, amax_history: torc
 __all__ = ["fp8_quantize_amax", "fp8_multi_quantize_amax", "fp8_multi_quantize_amax_timed",
            "fp8_multi_quantize_plan", "fp8_multi_quantize_plan_bytes",
            "fp8_multi_quantize_amax_planned", "Plan", "fp8q_plan",
+           "fp8_multi_quantize_amax_noalloc",
            "fp8_quantize_amax_and_update",
            "fp8_gelu_quantize_amax",
            "fp8_layernorm_quantize_amax", "fp8_gemm", "fp8_dequantize",

@@ -29,6 +29,8 @@
 #include <hip/hip_ext.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "device_common.h"
 #include "host_common.h"
 #include "quant_math.h"
@@ -1224,9 +1226,56 @@ static int launch_planned(const PlanRec& rec, hipStream_t stream) {
   return launch_status(hipLaunchKernel(fn, dim3((unsigned)blocks), dim3(kQBlock), args, 0, stream));
 }
 
+// ---------------------------------------------------------------- allocation-free plans
+// fp8_multi_quantize_amax_noalloc keeps its plan in this file-scope device array instead
+// of a caller's workspace: up to kQPlanMaxEntries entries and kScratchMapWords full chunks
+// (2^18 chunks of 16384 elements: 4.3 G elements).  Each device holds its own copy for the
+// life of the process; host code reaches it only through the address hipGetSymbolAddress
+// returns for the current device (the array's name in host code is not a device address).
+constexpr int64_t kScratchMapWords = (int64_t)1 << 18;
+constexpr int64_t kScratchBytes =
+    ((int64_t)kQPlanMaxEntries * (int64_t)sizeof(QEntry) + 15) / 16 * 16 + 4 * kScratchMapWords;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+// The current device's address of `scratch`, looked up once per device.
+static int scratch_address(void** out) {
+  static std::atomic<void*> cache[64];
+  static std::mutex lock;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return FP8Q_EHIP;
+  void* p = cache[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    std::lock_guard<std::mutex> g(lock);
+    p = cache[dev].load(std::memory_order_relaxed);
+    if (p == nullptr) {
+      if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr)
+        return FP8Q_EHIP;
+      cache[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return FP8Q_OK;
+}
+
 }  // namespace fp8q
 
 using namespace fp8q;
+
+extern "C" int fp8_multi_quantize_amax_noalloc(const fp8q_tensor* tensors, int n,
+                                               void* stream) {
+  int st = validate_entries(tensors, n, false);
+  if (st != FP8Q_OK) return st;
+  if (n > kQPlanMaxEntries) return FP8Q_EUNSUPPORTED;
+  if (n == 0) return FP8Q_OK;
+  if ((plan_bytes(tensors, n) - entries_bytes(n)) / 4 > kScratchMapWords) return FP8Q_EUNSUPPORTED;
+  void* ptr = nullptr;
+  st = scratch_address(&ptr);
+  if (st != FP8Q_OK) return st;
+  PlanRec rec{};
+  st = build_plan(tensors, n, ptr, kScratchBytes, &rec, (hipStream_t)stream);
+  if (st != FP8Q_OK) return st;
+  return launch_planned(rec, (hipStream_t)stream);
+}
 
 extern "C" int fp8_multi_quantize_amax(const fp8q_tensor* tensors, int n, void* stream) {
   return quantize_entries(tensors, n, false, (hipStream_t)stream);

@@ -171,6 +171,26 @@ int fp8_multi_quantize_plan(const fp8q_tensor* tensors, int n, void* workspace,
 int fp8_multi_quantize_amax_planned(const fp8q_plan* plan, void* stream);
 
 /*
+ * fp8_multi_quantize_amax_noalloc -- for callers that cannot allocate device memory
+ * (code under graph capture set-up, tight serving loops, harnesses that forbid
+ * hipMalloc): fp8_multi_quantize_plan followed by fp8_multi_quantize_amax_planned, with
+ * the plan held in a fixed device array of the library instead of a caller's workspace.
+ * Same results as fp8_multi_quantize_amax; one launch.  Allocates nothing: the array
+ * (1,245,184 bytes per device: 2048 entries and the entries of 2^18 chunks of 16384
+ * elements) is part of the library's device code and each device keeps it until the
+ * process ends.  Every call on a device rewrites that device's array, so calls that may
+ * overlap on one device (different streams, or threads) race; calls in order on one
+ * stream do not.  Like fp8_multi_quantize_plan, the call copies the plan from host
+ * memory and returns once it is in place (after the work enqueued before it on the
+ * stream); not for graph capture.
+ *   tensors, n  as fp8_multi_quantize_amax; n <= 2048 and at most 2^18 full chunks of
+ *               16384 aligned elements in all (larger lists: FP8Q_EUNSUPPORTED, nothing
+ *               enqueued).
+ * Returns FP8Q_OK, FP8Q_EINVAL, FP8Q_EUNSUPPORTED or FP8Q_EHIP.
+ */
+int fp8_multi_quantize_amax_noalloc(const fp8q_tensor* tensors, int n, void* stream);
+
+/*
  * fp8_multi_quantize_amax_timed -- fp8_multi_quantize_amax with profiling events: the
  * same validation, kernels and results, each kernel launched with hipExtLaunchKernel so
  * that the events take the start and stop time of the kernel's own dispatch rather than

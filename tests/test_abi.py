@@ -22,7 +22,8 @@ def test_header_declares_the_boundary():
         "fp8_quantize_amax", "fp8_multi_quantize_amax", "fp8_multi_quantize_amax_timed",
         "fp8_gelu_quantize_amax", "fp8_layernorm_quantize_amax", "fp8_quantize_amax_and_update", "fp8_dequantize", "fp8_amax_and_scale_update",
         "fp8_gemm", "fp8_status_string", "fp8_multi_quantize_plan_bytes",
-        "fp8_multi_quantize_plan", "fp8_multi_quantize_amax_planned"])
+        "fp8_multi_quantize_plan", "fp8_multi_quantize_amax_planned",
+        "fp8_multi_quantize_amax_noalloc"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -272,3 +273,24 @@ def test_plan_layout_and_validation():
     # an empty list needs no workspace, copies nothing and launches nothing
     assert P(arr, 0, None, 0, ctypes.byref(plan), None) == d.OK
     assert d.lib.fp8_multi_quantize_amax_planned(ctypes.byref(plan), None) == d.OK
+
+
+def test_noalloc_refuses_before_enqueue():
+    """The allocation-free multi-tensor quantize: an invalid list (EINVAL), more than 2048
+    entries or more than 2^18 full chunks (EUNSUPPORTED) are refused before anything is
+    copied or launched; an empty list is a no-op."""
+    import delayed_scaling_amax_amd as d
+    N = d.lib.fp8_multi_quantize_amax_noalloc
+    arr = (d.fp8q_tensor * 2049)()
+    for i in range(2049):
+        arr[i] = d.fp8q_tensor(None, None, 0, 0, 0, BAD, BAD)
+    assert N(arr, 2049, None) == d.EUNSUPPORTED
+    assert N(arr, 0, None) == d.OK
+    big = (d.fp8q_tensor * 2)()
+    # bf16 at 16-byte aligned addresses: (2^18 + 1) full chunks of 16384 elements
+    big[0] = d.fp8q_tensor(0x100000, 0x200000, ((1 << 18) + 1) * 16384, 0, 0, BAD, BAD)
+    big[1] = d.fp8q_tensor(None, None, 0, 0, 0, BAD, BAD)
+    assert N(big, 2, None) == d.EUNSUPPORTED
+    big[0].format = 5
+    assert N(big, 2, None) == d.EINVAL
+    assert N(None, 3, None) == d.EINVAL
