@@ -12,7 +12,11 @@ from gpu_path import FMT, bits, dev_src, f32, note
 pytestmark = pytest.mark.gpu
 
 
-def two_steps(orc, w, steps=2, threads=16):
+def two_steps(orc, w, steps=2, threads=16, mode="two_launches"):
+    """mode: "two_launches" (fp8_multi_quantize_amax, then fp8_amax_and_scale_update),
+    "one_launch" (fp8_quantize_amax_and_update: the amax is checked through history row
+    0, where the update puts it), or "planned" (fp8_multi_quantize_amax_planned on a plan
+    made once, then the update)."""
     import delayed_scaling_amax_amd as d
     n = len(w.tensors)
     fmts = [FMT[t.fmt] for t in w.tensors]
@@ -26,12 +30,23 @@ def two_steps(orc, w, steps=2, threads=16):
     # oracle state
     o_scale = np.asarray(w.first_scale, np.float32)
     o_hist = np.zeros((w.history_len, n), np.float32)
+    entries = [(srcs[i], dsts[i], scale[i:i + 1], amax[i:i + 1], fmts[i]) for i in range(n)]
+    ws = torch.zeros(1, dtype=torch.int32, device="cuda")
+    plan = d.fp8_multi_quantize_plan(entries) if mode == "planned" else None
     for step in range(steps):
-        note("%s step %d" % (w.name, step))
-        d.fp8_multi_quantize_amax([(srcs[i], dsts[i], scale[i:i + 1], amax[i:i + 1], fmts[i])
-                                   for i in range(n)])
-        torch.cuda.synchronize()
-        g_amax = amax.cpu().numpy()
+        note("%s step %d (%s)" % (w.name, step, mode))
+        if mode == "one_launch":
+            d.fp8_quantize_amax_and_update(entries, amax, hist, scale, scale_inv, fdev, ws,
+                                           reset_amax=True)
+            torch.cuda.synchronize()
+            g_amax = hist[0].cpu().numpy()
+        else:
+            if mode == "planned":
+                d.fp8_multi_quantize_amax_planned(plan)
+            else:
+                d.fp8_multi_quantize_amax(entries)
+            torch.cuda.synchronize()
+            g_amax = amax.cpu().numpy()
         o_amax = np.zeros(n, np.float32)
         for i, t in enumerate(w.tensors):
             want, o_amax[i] = orc.quantize_amax(t.data, fmts[i], float(o_scale[i]),
@@ -43,8 +58,11 @@ def two_steps(orc, w, steps=2, threads=16):
                     w.name, step, t.name, int((got != want).sum()), bad.tolist()))
             del want, got
         assert (bits(g_amax) == bits(o_amax)).all(), (g_amax, o_amax)
-        d.fp8_amax_and_scale_update(amax, hist, scale, scale_inv, fdev, reset_amax=True)
-        torch.cuda.synchronize()
+        if mode != "one_launch":
+            d.fp8_amax_and_scale_update(amax, hist, scale, scale_inv, fdev, reset_amax=True)
+            torch.cuda.synchronize()
+        else:
+            assert int(ws.item()) == 0
         r = orc.amax_and_scale_update(o_amax, o_hist, o_scale, np.array(fmts, np.uint8),
                                       reset_amax=True)
         o_hist, o_scale = r["hist"], r["scale"]
@@ -81,6 +99,20 @@ def test_grad_8192x16384_saturation(orc):
 @pytest.mark.timeout(1200)
 def test_mlp_12288_full_step(orc):
     two_steps(orc, workloads.mlp_12288())
+
+
+@pytest.mark.timeout(1200)
+def test_mlp_12288_one_launch_step(orc):
+    """The hidden-12288 step (5 tensors, 1.36 G elements, history 1024) through the
+    one-launch entry point, two steps, bit-exact."""
+    two_steps(orc, workloads.mlp_12288(), mode="one_launch")
+
+
+@pytest.mark.timeout(1200)
+def test_mlp_12288_planned_step(orc):
+    """The hidden-12288 step through a plan made once and its planned launch, two steps,
+    bit-exact."""
+    two_steps(orc, workloads.mlp_12288(), mode="planned")
 
 
 def test_microbatch_accumulation_once_per_step(orc):
