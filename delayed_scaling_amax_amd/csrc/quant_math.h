@@ -174,6 +174,32 @@ __device__ __forceinline__ uint2 codes8_bf16(uint4 w, float s, float r) {
   return make_uint2(pack4<kFmt>(c[0], c[1], c[2], c[3]), pack4<kFmt>(c[4], c[5], c[6], c[7]));
 }
 
+// The codes of 8 bf16 values whose quotients cannot exceed FP8_MAX in magnitude (the
+// caller has checked that every |x| is at most the value of sat_limit_bf16(s)): the
+// saturation step would change nothing and is left out.
+template <int kFmt>
+__device__ __forceinline__ uint2 codes8_bf16_unsaturated(uint4 w, float s, float r) {
+  const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+  float c[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const float x = as_float((k & 1) ? (u[k >> 1] & 0xFFFF0000u) : (u[k >> 1] << 16));
+    c[k] = div_corrected1(x, s, r);
+  }
+  return make_uint2(pack4<kFmt>(c[0], c[1], c[2], c[3]), pack4<kFmt>(c[4], c[5], c[6], c[7]));
+}
+
+// Largest bf16 magnitude (bit pattern) whose quotient by s cannot exceed FP8_MAX: two
+// binary32 steps below RN(FP8_MAX * s), truncated to bf16, is at most FP8_MAX * s
+// exactly, so |x| <= it gives |x / s| <= FP8_MAX and RN32(x / s) <= FP8_MAX.  (s inside
+// the division window, so FP8_MAX * s is normal or +inf; +inf gives the largest finite.)
+template <int kFmt>
+__device__ __forceinline__ uint32_t sat_limit_bf16(float s) {
+  constexpr float m = kFmt == FP8Q_E4M3 ? kE4M3Max : kE5M2Max;
+  const uint32_t b = as_uint(m * s) - 2u;
+  return (b >> 16) < 0x7F7Fu ? (b >> 16) : 0x7F7Fu;
+}
+
 template <int kFmt>
 __device__ __forceinline__ uint2 codes8_f32(uint4 lo, uint4 hi, float s, float r) {
   const uint32_t u[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};

@@ -258,6 +258,23 @@ __device__ __forceinline__ float gelu_f32(float x) {
   return h > 0.0f ? (p * m) * m : p;
 }
 
+// The direct form for inputs above -9 (where 2^t < 2^104, far from overflow, and the
+// quotient stays a normal binary32): t = -2 log2(e) u folded into two constants,
+// y = x * rcp(1 + 2^t) -- one exp2, one reciprocal, five other operations (the form
+// above takes nine).  Error before the bf16 rounding: t carries 3 roundings amplified by
+// |2u| through the exponential, plus the exp2, the sum, the reciprocal and the product:
+// below (4|2u| + 5) * 2^-24 relative.  +inf gives +inf, NaN gives NaN (patched).
+__device__ __forceinline__ float gelu_f32_direct(float x) {
+  constexpr float kT = (float)(-2.0 * 0.7978845608028654 * 1.4426950408889634);
+  constexpr float kT3 = (float)(-2.0 * 0.7978845608028654 * 1.4426950408889634 * 0.044715);
+  const float t = x * __builtin_fmaf(kT3, x * x, kT);
+  return x * __builtin_amdgcn_rcpf(__builtin_amdgcn_exp2f(t) + 1.0f);
+}
+
+// Raw bf16 bits at or above this (as unsigned 16-bit values): x <= -9, -inf or a NaN with
+// the sign bit set -- the inputs the direct form is not used for.
+constexpr uint32_t kGeluDirectLimit = 0xC110u;
+
 // gelu of a non-finite bf16 input h (exponent all ones).
 __device__ __forceinline__ uint32_t gelu_special(uint32_t h) {
   if ((h & 0x7FFFu) > 0x7F80u) return (h & 0x8000u) | 0x7FC0u;  // NaN
@@ -278,6 +295,17 @@ __device__ __forceinline__ uint4 gelu8_unpatched(uint4 w) {
 #pragma unroll
   for (int k = 0; k < 4; ++k)
     o[k] = pack_bf16_rne(gelu_f32(as_float(u[k] << 16)), gelu_f32(as_float(u[k] & 0xFFFF0000u)));
+  return make_uint4(o[0], o[1], o[2], o[3]);
+}
+
+// Eight bf16 inputs, all above -9 (or +inf, or positive NaN), through the direct form.
+__device__ __forceinline__ uint4 gelu8_direct(uint4 w) {
+  const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+  uint32_t o[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+    o[k] = pack_bf16_rne(gelu_f32_direct(as_float(u[k] << 16)),
+                         gelu_f32_direct(as_float(u[k] & 0xFFFF0000u)));
   return make_uint4(o[0], o[1], o[2], o[3]);
 }
 
@@ -603,6 +631,7 @@ __device__ __forceinline__ void run_full_chunks(const Tab& tab, Sh& sh, int t_be
   }
   float s = uniform(sh.scale[t]), r = uniform(sh.rcp[t]);
   uint32_t xlim = uniform(sh.xlim[t]);
+  uint32_t clim = kGelu ? sat_limit_bf16<kFmt>(s) : 0u;
   uint32_t acc = 0;
   // The loop leaves only at the end of the ring.  When a run ends partway round, the
   // rest of the ring runs as dead passes: their loads are empty (zeros), they do no
@@ -632,22 +661,40 @@ __device__ __forceinline__ void run_full_chunks(const Tab& tab, Sh& sh, int t_be
       uint2 o[kU] = {};
       if (real) {
         uint32_t pm = 0;  // pass magnitude max
+        if constexpr (kGelu) {
+          // the direct gelu form unless some input of the pass is <= -9 (wave-uniform)
+          uint32_t raw = 0;
 #pragma unroll
-        for (int u = 0; u < kU; ++u) {
-          if constexpr (kBF16) {
-            uint32_t mg;
-            if constexpr (kGelu) {
-              // the magnitude max feeds both the amax and the test for NaN outputs
-              const uint4 x = cur.w[u][0];
-              cur.w[u][0] = gelu8_unpatched(x);
-              mg = mag8_bf16(cur.w[u][0]);
-              if (__builtin_amdgcn_ballot_w64(halves_nan(mg) != 0) != 0) {
-                cur.w[u][0] = gelu8_patch(x, cur.w[u][0]);
-                mg = mag8_bf16(cur.w[u][0]);
-              }
-            } else {
+          for (int u = 0; u < kU; ++u)
+            raw = pk_max_u16(raw, pk_max_u16(pk_max_u16(cur.w[u][0].x, cur.w[u][0].y),
+                                             pk_max_u16(cur.w[u][0].z, cur.w[u][0].w)));
+          const bool direct =
+              __builtin_amdgcn_ballot_w64(max_halves(raw) >= kGeluDirectLimit) == 0;
+#pragma unroll
+          for (int u = 0; u < kU; ++u) {
+            // the magnitude max feeds both the amax and the test for NaN outputs
+            const uint4 x = cur.w[u][0];
+            cur.w[u][0] = direct ? gelu8_direct(x) : gelu8_unpatched(x);
+            uint32_t mg = mag8_bf16(cur.w[u][0]);
+            if (__builtin_amdgcn_ballot_w64(halves_nan(mg) != 0) != 0) {
+              cur.w[u][0] = gelu8_patch(x, cur.w[u][0]);
               mg = mag8_bf16(cur.w[u][0]);
             }
+            pm = pk_max_u16(pm, mg);
+          }
+          // no saturation needed when no |y| of the pass exceeds clim (<= FP8_MAX * s)
+          const bool nosat = __builtin_amdgcn_ballot_w64(max_halves(pm) > clim) == 0;
+#pragma unroll
+          for (int u = 0; u < kU; ++u)
+            o[u] = nosat ? codes8_bf16_unsaturated<kFmt>(cur.w[u][0], s, r)
+                         : codes8_bf16<kFmt>(cur.w[u][0], s, r);
+        }
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+          if constexpr (kGelu) {
+            // done above
+          } else if constexpr (kBF16) {
+            const uint32_t mg = mag8_bf16(cur.w[u][0]);
             pm = pk_max_u16(pm, mg);
             o[u] = codes8_bf16<kFmt>(cur.w[u][0], s, r);
           } else {
@@ -692,6 +739,7 @@ __device__ __forceinline__ void run_full_chunks(const Tab& tab, Sh& sh, int t_be
           s = uniform(sh.scale[nx.t]);
           r = uniform(sh.rcp[nx.t]);
           xlim = uniform(sh.xlim[nx.t]);
+          if constexpr (kGelu) clim = sat_limit_bf16<kFmt>(s);
         }
       }
     }
