@@ -159,6 +159,7 @@ __device__ __forceinline__ float hi_f32(uint32_t w) { return as_float(w & 0xFFFF
 struct LnQuant {
   float s, r;
   uint32_t xlim;
+  uint32_t clim;  // sat_limit_bf16(s): units whose |y| stay within need no saturation
   bool win;
 };
 
@@ -264,7 +265,12 @@ __device__ __forceinline__ void ln_row(uint4 (&w)[kV], const LnArgs& a, int64_t 
     acc = pk_max_u16(acc, valid ? mg : 0u);
     uint2 c;
     if (q.win) {
-      c = codes8_bf16<kFmt>(yw, q.s, q.r);
+      // no saturation step where no quotient of the unit (across the wavefront) can
+      // exceed FP8_MAX
+      if (__builtin_amdgcn_ballot_w64(max_halves(mg) > q.clim) == 0)
+        c = codes8_bf16_unsaturated<kFmt>(yw, q.s, q.r);
+      else
+        c = codes8_bf16<kFmt>(yw, q.s, q.r);
       if (max_halves(mg) >= q.xlim) c = patch8_bf16<kFmt>(c, yw, q.xlim);
     } else {  // scale outside the corrected-division window: IEEE divide per element
       const uint32_t u[4] = {yw.x, yw.y, yw.z, yw.w};
@@ -340,6 +346,7 @@ void ln_quantize_kernel(const LnArgs a) {
   q.r = 1.0f / q.s;
   q.win = (q.s >= 0x1p-80f) && (q.s <= 0x1p125f);
   q.xlim = min(as_uint(q.s * 0x1p126f) >> 16, 0x7F80u);
+  q.clim = sat_limit_bf16<kFmt>(q.s);
   __syncthreads();
 
   uint32_t acc = 0;

@@ -69,11 +69,11 @@ constexpr int kQMaxEntries = 32;                  // tensors per launch (kernel-
 constexpr int kQPlanMaxEntries = 2048;            // tensors per launch (planned table in device memory)
 constexpr int kQBlocksPerCU = FP8Q_Q_BLOCKS_PER_CU;  // persistent grid size per CU
 #ifndef FP8Q_Q_GELU_BLOCKS_PER_CU
-#define FP8Q_Q_GELU_BLOCKS_PER_CU 5
+#define FP8Q_Q_GELU_BLOCKS_PER_CU 6
 #endif
 // the gelu instance is arithmetic-bound: more resident waves hide exp/rcp latency (on
-// 8192 x 16384 bf16: 5 blocks per CU 88.5-90.0 us, 4 90.4-91.2, 6 like 5; on another box
-// 4 blocks 91.4 us, 3 93.6, 2 95.6)
+// 8192 x 16384 bf16 with the direct form: 6 blocks per CU 75-80 us, 5 76-80, 4 79-86, 3
+// 79-89; its 79 registers leave room for six)
 constexpr int kQGeluBlocksPerCU = FP8Q_Q_GELU_BLOCKS_PER_CU;
 constexpr int kQChunk = kQBlock * kQUnroll;       // units (8-element groups) per chunk
 #ifndef FP8Q_Q_DEPTH
