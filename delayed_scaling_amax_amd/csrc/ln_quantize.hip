@@ -36,21 +36,33 @@
 namespace fp8q {
 
 constexpr int kLBlock = 256;       // 4 wavefronts, one row each at a time
-// 24 units per lane: 8 wavefronts share one block's 96 KB of gamma/beta, two per SIMD
-// (232-240 registers each); 32 units need more than 256 registers, so one per SIMD.
-template <int kV>
-constexpr int ln_block() { return kV == 24 ? 512 : kLBlock; }
+// Rows of 24 or 32 units per lane (hidden 8200-16384) are split over kSplit wavefronts
+// (4: 6 or 8 units each): a row's sums are combined through LDS, and the smaller register
+// need lets more wavefronts share one block's 96 or 128 KB of gamma/beta (24 units on one
+// wavefront took 232-240 registers, 32 units more than 256; 8 units take 106-111).
+template <int kV, int kSplit>
+constexpr int ln_block() { return kSplit == 1 ? kLBlock : (kV * kSplit == 32 && kSplit == 2 ? 512 : 1024); }
+template <int kV, int kSplit>
+constexpr int ln_rows_per_block() { return ln_block<kV, kSplit>() / (64 * kSplit); }
 constexpr int kLMaxH = 16384;      // 64 lanes x 32 units x 8 elements
 #ifndef FP8Q_LN_BLOCKS_PER_CU
 #define FP8Q_LN_BLOCKS_PER_CU 4
-#endif
-#ifndef FP8Q_LN_PREFETCH
-#define FP8Q_LN_PREFETCH 0
 #endif
 #ifndef FP8Q_LN_UNIT_BARRIER
 #define FP8Q_LN_UNIT_BARRIER 1
 #endif
 constexpr int kLBlocksPerCU = FP8Q_LN_BLOCKS_PER_CU;
+// Wavefronts per row for 24 and 32 units per lane (hidden 8200-12288, 12296-16384).
+// Measured (µs; one wavefront per row before the split): 4096 x 16384: 92 -> 2 parts 59-61,
+// 4 parts 53-55; 8192 x 12288: 78.5 -> 76.7-77.7 / 74.4; 8192 x 10000: 72-75 / 67.7-69.2.
+#ifndef FP8Q_LN_SPLIT24
+#define FP8Q_LN_SPLIT24 4
+#endif
+#ifndef FP8Q_LN_SPLIT32
+#define FP8Q_LN_SPLIT32 4
+#endif
+constexpr int kLSplit24 = FP8Q_LN_SPLIT24;
+constexpr int kLSplit32 = FP8Q_LN_SPLIT32;
 
 struct LnArgs {
   const uint16_t* x;
@@ -188,12 +200,53 @@ __device__ __forceinline__ void unpack8(const uint4& w, float (&x)[8]) {
 // unit by unit, so only the packed row and a few partial sums stay live.  Sums are
 // trees: 8 elements of a unit (depth 3), then the kV units (depth log2 kV), then the
 // wavefront (depth 6).
-template <int kFmt, int kV, bool kMasked>
+// Sums of a row split over kSplit wavefronts (2 or 4): each part's wavefront sum goes to
+// LDS and every lane adds the parts as the same tree ((p0 + p1) + (p2 + p3)), so all
+// parts hold the identical value.  `xch` holds 3 floats per part of each row slot: the
+// mean's partial, then the two deviation sums; one block barrier each.  (The next row's
+// mean partial is written only after every wavefront has passed the deviation sums'
+// barrier, i.e. has read this row's mean, and likewise for the deviation sums.)
+template <int kSplit>
+__device__ __forceinline__ float parts_sum(const float* xch, int i) {
+  if constexpr (kSplit == 2) return xch[i] + xch[3 + i];
+  else return (xch[i] + xch[3 + i]) + (xch[6 + i] + xch[9 + i]);
+}
+
+template <int kSplit>
+__device__ __forceinline__ float row_total(float v, float* xch, int part, int lane) {
+  if constexpr (kSplit == 1) {
+    return v;
+  } else {
+    if (lane == 0) xch[3 * part] = v;
+    __syncthreads();
+    return parts_sum<kSplit>(xch, 0);
+  }
+}
+
+template <int kSplit>
+__device__ __forceinline__ void row_total2(float& a, float& b, float* xch, int part, int lane) {
+  if constexpr (kSplit > 1) {
+    if (lane == 0) {
+      xch[3 * part + 1] = a;
+      xch[3 * part + 2] = b;
+    }
+    __syncthreads();
+    a = parts_sum<kSplit>(xch, 1);
+    b = parts_sum<kSplit>(xch, 2);
+  }
+}
+
+// `half`: which part of the row's units this wavefront holds (units lane + 64 k +
+// 64 kV half); `row_ok`: false for the padding rows of split blocks (no memory access,
+// nothing accumulated), which still take part in the barriers.
+template <int kFmt, int kV, bool kMasked, int kSplit>
 __device__ __forceinline__ void ln_row(uint4 (&w)[kV], const LnArgs& a, int64_t row,
-                                       int lane, const float* __restrict__ lg,
+                                       bool row_ok, int lane, int half, float* xch,
+                                       const float* __restrict__ lg,
                                        const float* __restrict__ lb, const LnQuant& q,
                                        uint32_t& acc) {
   const float invH = a.inv_h;  // RN(1/H), exact for a power-of-two H
+  const int ubase = 64 * kV * half;  // first unit of this wavefront's half
   // pass 1: mean (units past the row read as zeros)
   float p1[kV];
 #pragma unroll
@@ -202,7 +255,7 @@ __device__ __forceinline__ void ln_row(uint4 (&w)[kV], const LnArgs& a, int64_t 
     unpack8(w[k], x);
     p1[k] = tree_sum(x);
   }
-  const float mu = wave_sum(tree_sum(p1)) * invH;
+  const float mu = row_total<kSplit>(wave_sum(tree_sum(p1)), xch, half, lane) * invH;
   // pass 2: deviations from mu', their sum and sum of squares
   rebind(w);
   float s1[kV], s2[kV];
@@ -217,10 +270,11 @@ __device__ __forceinline__ void ln_row(uint4 (&w)[kV], const LnArgs& a, int64_t 
     }
     s1[k] = tree_sum(x);
     s2[k] = tree_sum(sq);
-    if (kMasked && lane + 64 * k >= a.nunits) s1[k] = s2[k] = 0.0f;
+    if (kMasked && ubase + lane + 64 * k >= a.nunits) s1[k] = s2[k] = 0.0f;
   }
   float t1 = tree_sum(s1), t2 = tree_sum(s2);
   wave_sum2(t1, t2);
+  row_total2<kSplit>(t1, t2, xch, half, lane);
   const float e = t1 * invH;
   float var = __builtin_fmaf(-e, e, t2 * invH);
   var = var < 0.0f ? 0.0f : var;  // rounding can dip below 0; a NaN stays NaN
@@ -228,16 +282,17 @@ __device__ __forceinline__ void ln_row(uint4 (&w)[kV], const LnArgs& a, int64_t 
   // hardware reciprocal square root (1 ulp) where its input is normal; the IEEE
   // square root and divide for a subnormal (or zero) V + eps
   const float rstd = ve >= 0x1p-126f ? __builtin_amdgcn_rsqf(ve) : 1.0f / __builtin_sqrtf(ve);
-  if (lane == 0) {
+  if (lane == 0 && half == 0 && row_ok) {
     if (a.mean_out) a.mean_out[row] = mu + e;
     if (a.rstd_out) a.rstd_out[row] = rstd;
   }
   // pass 3: y, its bf16 rounding, the codes and the amax
   rebind(w);
-  const __amdgpu_buffer_rsrc_t out = ln_rsrc(a.dst + row * (int64_t)a.H, (uint32_t)a.H);
+  const __amdgpu_buffer_rsrc_t out =
+      ln_rsrc(a.dst + (row_ok ? row * (int64_t)a.H : 0), row_ok ? (uint32_t)a.H : 0u);
 #pragma unroll
   for (int k = 0; k < kV; ++k) {
-    const int unit = lane + 64 * k;
+    const int unit = ubase + lane + 64 * k;
     const float4* g4 = (const float4*)(lg + 8 * unit);
     const float4* b4 = (const float4*)(lb + 8 * unit);
     const float4 g0 = g4[0], g1 = g4[1], b0 = b4[0], b1 = b4[1];
@@ -261,7 +316,7 @@ __device__ __forceinline__ void ln_row(uint4 (&w)[kV], const LnArgs& a, int64_t 
       yw = make_uint4(o[0], o[1], o[2], o[3]);
       mg = mag8_bf16(yw);
     }
-    const bool valid = !kMasked || unit < a.nunits;
+    const bool valid = row_ok && (!kMasked || unit < a.nunits);
     acc = pk_max_u16(acc, valid ? mg : 0u);
     uint2 c;
     if (q.win) {
@@ -291,26 +346,23 @@ __device__ __forceinline__ void ln_row(uint4 (&w)[kV], const LnArgs& a, int64_t 
   }
 }
 
-template <int kFmt, int kV, bool kMasked>
-__global__ __launch_bounds__(ln_block<kV>())
+template <int kFmt, int kV, bool kMasked, int kSplit>
+__global__ __launch_bounds__((ln_block<kV, kSplit>()))
 void ln_quantize_kernel(const LnArgs a) {
-  constexpr int kBlk = ln_block<kV>();
-  // gamma then beta, each 512 kV floats, zero-padded; 16-byte aligned for the b128 reads
+  constexpr int kBlk = ln_block<kV, kSplit>();
+  // gamma then beta, each 512 kV kSplit floats, zero-padded; 16-byte aligned for the
+  // b128 reads
   extern __shared__ __attribute__((aligned(16))) float lds[];
   __shared__ uint32_t block_amax;
-  constexpr int kPad = 512 * kV;
+  __shared__ float xch_all[kSplit > 1 ? 3 * kSplit * ln_rows_per_block<kV, kSplit>() : 1];
+  constexpr int kPad = 512 * kV * kSplit;
   float* lg = lds;
   float* lb = lds + kPad;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: SGPR
   const int64_t nwaves = (int64_t)gridDim.x * (kBlk / 64);
-  int64_t row = (int64_t)blockIdx.x * (kBlk / 64) + wave;
+  int64_t row = (int64_t)blockIdx.x * (kBlk / 64) + wave;  // (kSplit == 1)
   const uint32_t row_bytes = (uint32_t)a.H * 2u;
-#if FP8Q_LN_PREFETCH
-  // the first row's loads go out before the staging below, which they overlap
-  uint4 wa[kV], wb[kV];
-  if (row < a.rows) ln_load_row<kV>(wa, ln_rsrc(a.x + row * a.H, row_bytes), lane);
-#endif
   // stage gamma/beta: 16-byte loads, all issued before any is used
   if (a.vec_affine) {
     float4 gs[kPad / 4 / kBlk > 0 ? kPad / 4 / kBlk : 1];
@@ -350,30 +402,34 @@ void ln_quantize_kernel(const LnArgs a) {
   __syncthreads();
 
   uint32_t acc = 0;
-#if FP8Q_LN_PREFETCH
-  // two row buffers alternate so that the next row's loads are in flight while this
-  // row is reduced; the prefetch index is clamped so every load is unconditional
-  while (row < a.rows) {
-    int64_t nxt = row + nwaves < a.rows ? row + nwaves : a.rows - 1;
-    ln_load_row<kV>(wb, ln_rsrc(a.x + nxt * a.H, row_bytes), lane);
-    __builtin_amdgcn_sched_barrier(0);
-    ln_row<kFmt, kV, kMasked>(wa, a, row, lane, lg, lb, q, acc);
-    row += nwaves;
-    if (row >= a.rows) break;
-    nxt = row + nwaves < a.rows ? row + nwaves : a.rows - 1;
-    ln_load_row<kV>(wa, ln_rsrc(a.x + nxt * a.H, row_bytes), lane);
-    __builtin_amdgcn_sched_barrier(0);
-    ln_row<kFmt, kV, kMasked>(wb, a, row, lane, lg, lb, q, acc);
-    row += nwaves;
+  if constexpr (kSplit == 1) {
+    // one row at a time: latency is hidden by the other resident wavefronts
+    for (; row < a.rows; row += nwaves) {
+      uint4 w[kV];
+      ln_load_row<kV>(w, ln_rsrc(a.x + row * a.H, row_bytes), lane);
+      ln_row<kFmt, kV, kMasked, 1>(w, a, row, true, lane, 0, nullptr, lg, lb, q, acc);
+    }
+  } else {
+    // wavefronts kSplit r .. kSplit r + kSplit - 1 hold the parts of row slot r; every
+    // wavefront of the block runs the same iterations (the barriers), padding rows past
+    // the end
+    constexpr int kRows = ln_rows_per_block<kV, kSplit>();
+    const int slot = wave / kSplit, half = wave % kSplit;
+    float* xch = xch_all + 3 * kSplit * slot;
+    for (int64_t base = (int64_t)blockIdx.x * kRows; base < a.rows;
+         base += (int64_t)gridDim.x * kRows) {
+      const int64_t r = base + slot;
+      const bool ok = r < a.rows;
+      uint4 w[kV];
+      // this half's units start 64 kV units (1024 kV bytes) into the row
+      const __amdgpu_buffer_rsrc_t rs =
+          ok ? ln_rsrc(a.x + r * a.H + 512 * kV * half,
+                       row_bytes > 1024u * kV * half ? row_bytes - 1024u * kV * half : 0u)
+             : ln_rsrc(a.x, 0u);
+      ln_load_row<kV>(w, rs, lane);
+      ln_row<kFmt, kV, kMasked, kSplit>(w, a, r, ok, lane, half, xch, lg, lb, q, acc);
+    }
   }
-#else
-  // one row at a time: latency is hidden by the other resident wavefronts
-  for (; row < a.rows; row += nwaves) {
-    uint4 w[kV];
-    ln_load_row<kV>(w, ln_rsrc(a.x + row * a.H, row_bytes), lane);
-    ln_row<kFmt, kV, kMasked>(w, a, row, lane, lg, lb, q, acc);
-  }
-#endif
   // block amax: packed halves -> wavefront -> LDS -> one global atomic
   uint32_t m = max_halves(acc) << 16;
   m = wave_max_u32(m);
@@ -383,11 +439,11 @@ void ln_quantize_kernel(const LnArgs a) {
 }
 
 // ---------------------------------------------------------------- host side
-template <int kFmt, int kV, bool kMasked>
+template <int kFmt, int kV, bool kMasked, int kSplit = 1>
 static int ln_launch(const LnArgs& a, hipStream_t stream) {
-  constexpr int kBlk = ln_block<kV>();
-  const void* fn = (const void*)ln_quantize_kernel<kFmt, kV, kMasked>;
-  const size_t smem = (size_t)2 * 512 * kV * sizeof(float);
+  constexpr int kBlk = ln_block<kV, kSplit>();
+  const void* fn = (const void*)ln_quantize_kernel<kFmt, kV, kMasked, kSplit>;
+  const size_t smem = (size_t)2 * 512 * kV * kSplit * sizeof(float);
   static std::atomic<int> fit{0};
   int per_cu = fit.load(std::memory_order_relaxed);
   if (per_cu <= 0) {
@@ -405,7 +461,8 @@ static int ln_launch(const LnArgs& a, hipStream_t stream) {
   int cus = 0;
   const int st = current_device_cus(&cus);
   if (st != FP8Q_OK) return st;
-  int64_t blocks = (a.rows + (kBlk / 64) - 1) / (kBlk / 64);
+  constexpr int kRowsPerBlock = kBlk / (64 * kSplit);
+  int64_t blocks = (a.rows + kRowsPerBlock - 1) / kRowsPerBlock;
   const int64_t cap = (int64_t)cus * per_cu;
   if (blocks > cap) blocks = cap;
   void* args[] = {(void*)&a};
@@ -426,8 +483,12 @@ static int ln_dispatch(const LnArgs& a, hipStream_t stream) {
     case 8: return masked ? ln_launch<kFmt, 8, true>(a, stream) : ln_launch<kFmt, 8, false>(a, stream);
     case 16: return masked ? ln_launch<kFmt, 16, true>(a, stream) : ln_launch<kFmt, 16, false>(a, stream);
     // hidden 8200 .. 12288 (12288: the hidden-12288 MLP) and 12296 .. 16384
-    case 24: return masked ? ln_launch<kFmt, 24, true>(a, stream) : ln_launch<kFmt, 24, false>(a, stream);
-    default: return masked ? ln_launch<kFmt, 32, true>(a, stream) : ln_launch<kFmt, 32, false>(a, stream);
+    case 24:
+      return masked ? ln_launch<kFmt, 24 / kLSplit24, true, kLSplit24>(a, stream)
+                    : ln_launch<kFmt, 24 / kLSplit24, false, kLSplit24>(a, stream);
+    default:
+      return masked ? ln_launch<kFmt, 32 / kLSplit32, true, kLSplit32>(a, stream)
+                    : ln_launch<kFmt, 32 / kLSplit32, false, kLSplit32>(a, stream);
   }
 }
 
