@@ -82,13 +82,15 @@ __global__ __launch_bounds__(kUBlock) void amax_and_scale_update_kernel(
   const int64_t c = c0 + (int64_t)lc * W;
   const bool col_ok = c < n;  // W == 4: whole groups of 4 (n % 4 == 0)
 
-  // per-tensor inputs, fetched now so their latency overlaps the history loads (every
-  // lane loads, lanes past the group's columns its first tensor, so no merge waits)
+  // per-tensor inputs: loaded right after the first chunk's history loads (below), so
+  // their latency overlaps the history's without the history values waiting behind them
+  // (loads complete in issue order for the wait counter); every lane loads, lanes past the
+  // group's columns its first tensor, so no merge waits
   const int ncols = (int)min((int64_t)kUCols, n - c0);
   const int64_t ct = c0 + (tid < ncols ? tid : 0);
-  const float a_in = amax[ct];
-  const float s_old = scale[ct];
-  uint32_t fmt = formats[ct];
+  float a_in = 0.0f, s_old = 0.0f;
+  uint32_t fmt = 0;
+  bool have_inputs = false;
 
   // loads see rows [0, H-1) (the oldest row is dropped by the roll), stores rows [0, H)
   const uint32_t row_bytes = (uint32_t)(n * 4);
@@ -113,6 +115,12 @@ __global__ __launch_bounds__(kUBlock) void amax_and_scale_update_kernel(
       const int64_t d = d_lo + rr + (int64_t)k * rpp;
       off[k] = col_ok && d < d_hi ? (uint32_t)(d - 1) * row_bytes + col_off : kUOff;
       hist_load<W>(rld, off[k], v[k]);
+    }
+    if (!have_inputs) {  // uniform: the first chunk
+      a_in = amax[ct];
+      s_old = scale[ct];
+      fmt = formats[ct];
+      have_inputs = true;
     }
 #pragma unroll
     for (int k = 0; k < kURows; ++k)
