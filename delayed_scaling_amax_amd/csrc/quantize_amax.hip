@@ -888,13 +888,13 @@ __device__ void update_in_block(const QUpdate& u, uint32_t* colmax) {
   const bool active = g < groups;
   const int64_t H = u.H, span = (int64_t)groups * kR;
   uint32_t* hist = (uint32_t*)u.hist;
-  // thread t < n: tensor t's inputs, fetched now so their latency overlaps the history's
+  // thread t < n: tensor t's inputs, loaded after the first chunk's history loads so
+  // their latency overlaps the history's without the history values waiting behind them
   // (every lane loads, lanes past n tensor 0's, so no merge waits for the loads)
   const int tt = tid < n ? tid : 0;
-  const uint32_t ab =
-      __hip_atomic_load((uint32_t*)u.amax + tt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  const float s_old = u.scale[tt];
-  uint32_t fmt = u.formats[tt];
+  uint32_t ab = 0u, fmt = 0u;
+  float s_old = 0.0f;
+  bool have_inputs = false;
   if (tid < n) colmax[tid] = 0u;
   uint32_t m = 0u;
   for (int64_t d_hi = H; d_hi > 1; d_hi -= span) {
@@ -907,6 +907,12 @@ __device__ void update_in_block(const QUpdate& u, uint32_t* colmax) {
       const int64_t d = d_lo + g + (int64_t)k * groups;
       v[k] = hist[active && d < d_hi ? (d - 1) * n + c : 0];
     }
+    if (!have_inputs) {  // uniform: the first chunk
+      ab = __hip_atomic_load((uint32_t*)u.amax + tt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      s_old = u.scale[tt];
+      fmt = u.formats[tt];
+      have_inputs = true;
+    }
 #pragma unroll
     for (int k = 0; k < kR; ++k) {
       const int64_t d = d_lo + g + (int64_t)k * groups;
@@ -918,6 +924,11 @@ __device__ void update_in_block(const QUpdate& u, uint32_t* colmax) {
       const int64_t d = d_lo + g + (int64_t)k * groups;
       if (active && d < d_hi) hist[d * n + c] = v[k];
     }
+  }
+  if (!have_inputs) {  // H == 1: no chunk ran
+    ab = __hip_atomic_load((uint32_t*)u.amax + tt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_old = u.scale[tt];
+    fmt = u.formats[tt];
   }
   __syncthreads();  // colmax zeroed (and every chunk done) before the maxima go in
   if (active && m != 0u) atomicMax(&colmax[c], m);
