@@ -186,8 +186,9 @@ __host__ __device__ __forceinline__ int entry_kind(const QEntry& e) {
 }
 
 // The batched amax_and_scale_update appended to a quantize launch
-// (fp8_quantize_amax_and_update): run by the block that finishes last, over n <=
-// kQUpdMaxCols tensors with history[H][n], H * n <= kQUpdMaxElems.
+// (fp8_quantize_amax_and_update): the history roll by the block that finishes its
+// quantize work first, the rest by the block that finishes last, over n <= kQUpdMaxCols
+// tensors with history[H][n], H * n <= kQUpdMaxElems.
 constexpr int64_t kQUpdMaxCols = 256;
 constexpr int64_t kQUpdMaxElems = 65536;
 static_assert(kQUpdMaxCols <= kQBlock, "the appended update gives each column a thread");
@@ -197,7 +198,7 @@ struct QUpdate {
   float* scale;
   float* scale_inv;
   const uint8_t* formats;
-  uint32_t* counter;  // blocks finished; 0 at launch, left 0 by the last block
+  uint32_t* counter;  // blocks finished (+1 for the roll); 0 at launch, left 0
   int64_t n;
   int64_t H;
   int32_t algo;
@@ -342,7 +343,7 @@ struct QSharedT {
   uint32_t xlim[kCap];  // magnitude bits at which the fixed-code path starts
   uint32_t win[kCap];   // scale inside the Markstein window
   uint32_t amax[kCap];  // this block's amax bits per tensor
-  uint32_t last;        // kUpd: this block finished last
+  uint32_t last;        // kUpd: the finished-block count before this block's
   uint32_t any_out;     // planned tables: some tensor's scale is outside the window
 };
 using QShared = QSharedT<kQMaxEntries>;
@@ -852,34 +853,47 @@ __device__ __forceinline__ void phase2_dispatch(const Tab& tab, Sh& sh, int t, b
 }
 
 // ---------------------------------------------------------------- appended update
-// Whether this block is the last of the grid to finish.  Every thread's amax atomic is
-// performed (or skipped because amax already held as much) before the block counts
-// itself, so the last block sees every block's contribution.  Only device-scope atomics have to be ordered here (the amax maxima and
-// the count), so waiting for the atomics to complete is enough: a device-scope fence
-// would write back and invalidate the XCD's L2 in every block.  Contains barriers:
-// every thread of the block calls it once.
-template <class Sh>
-__device__ __forceinline__ bool finished_last(uint32_t* counter, Sh& sh) {
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this thread's amax atomic performed
+// Counts this block as finished and returns the count before it (block-uniform).  Every
+// thread's global writes and atomics -- the amax maxima, and the roll's stores in the
+// block that rolls -- are performed before the block counts itself.  kRelease (the block
+// that rolled the history, once) also writes the roll back past its XCD's L2 with a
+// device-scope release; the block that sees the full count (gridDim.x, the extra count
+// coming from that release) acquires at device scope, so its loads of row 0 see the
+// roll.  The other blocks order device-scope atomics only, for which waiting for them to
+// complete is enough: a device-scope fence would write back and invalidate the XCD's L2
+// in every block.  Contains barriers: every thread of the block calls it.
+template <bool kRelease, class Sh>
+__device__ __forceinline__ uint32_t arrive(uint32_t* counter, Sh& sh) {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
-  if (threadIdx.x == 0) sh.last = atomicAdd(counter, 1u) == gridDim.x - 1 ? 1u : 0u;
+  if (threadIdx.x == 0) {
+    const uint32_t old =
+        kRelease ? __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT)
+                 : __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (old == gridDim.x) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    sh.last = old;
+  }
   __syncthreads();
-  return sh.last != 0;
+  return sh.last;
 }
 
-// The batched update of u.n tensors by one block, after every block's amax atomics
-// (read back with device-scope atomic loads; nothing else it reads is written by another
-// block of the launch): the same arithmetic as amax_and_scale_update_kernel ("Implement
-// fused kernel for FP8 scale update": roll the history in place, insert the new amax,
-// select, new scale).  Thread t owns column t mod n and every (kQBlock / n)-th history
-// row, so consecutive threads touch consecutive columns of a row and each keeps its
-// column maximum in a register (one LDS atomic per thread at the end: per-element
+// The batched update of u.n tensors ("Implement fused kernel for FP8 scale update": roll
+// the history, insert the new amax, select, new scale; the same results as
+// amax_and_scale_update_kernel) split in two so that only one memory round trip follows
+// the launch's last quantize block.  The roll does not depend on this step's amax: the
+// first block to finish its quantize work moves rows [0, H-1) to [1, H) in place and
+// leaves each column's maximum over them in row 0, which the roll has freed.  The block
+// that finishes last then needs row 0 and the amaxes only.
+
+// The roll, by one block.  Thread t owns column t mod n and every (kQBlock / n)-th
+// history row, so consecutive threads touch consecutive columns of a row and each keeps
+// its column maximum in a register (one LDS atomic per thread at the end: per-element
 // atomics on n slots would serialize).  Destination rows [1, H) are walked from the top
 // in chunks of (kQBlock / n) * 32 rows (history 1024 of up to 64 tensors in one chunk,
 // one load round trip): a chunk loads its source rows (one row up), a barrier, then
 // stores; rows below the chunk are read only by later chunks, so no row is overwritten
-// before it is read.
-__device__ void update_in_block(const QUpdate& u, uint32_t* colmax) {
+// before it is read.  Row 0 then takes the column maxima as amax bits (0 when H == 1).
+__device__ void roll_in_block(const QUpdate& u, uint32_t* colmax) {
   constexpr int kR = 32;  // rows per thread per chunk
   const int tid = threadIdx.x;
   const int n = (int)u.n;  // 1 .. kQUpdMaxCols (= kQBlock)
@@ -888,13 +902,6 @@ __device__ void update_in_block(const QUpdate& u, uint32_t* colmax) {
   const bool active = g < groups;
   const int64_t H = u.H, span = (int64_t)groups * kR;
   uint32_t* hist = (uint32_t*)u.hist;
-  // thread t < n: tensor t's inputs, loaded after the first chunk's history loads so
-  // their latency overlaps the history's without the history values waiting behind them
-  // (every lane loads, lanes past n tensor 0's, so no merge waits for the loads)
-  const int tt = tid < n ? tid : 0;
-  uint32_t ab = 0u, fmt = 0u;
-  float s_old = 0.0f;
-  bool have_inputs = false;
   if (tid < n) colmax[tid] = 0u;
   uint32_t m = 0u;
   for (int64_t d_hi = H; d_hi > 1; d_hi -= span) {
@@ -906,12 +913,6 @@ __device__ void update_in_block(const QUpdate& u, uint32_t* colmax) {
     for (int k = 0; k < kR; ++k) {
       const int64_t d = d_lo + g + (int64_t)k * groups;
       v[k] = hist[active && d < d_hi ? (d - 1) * n + c : 0];
-    }
-    if (!have_inputs) {  // uniform: the first chunk
-      ab = __hip_atomic_load((uint32_t*)u.amax + tt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      s_old = u.scale[tt];
-      fmt = u.formats[tt];
-      have_inputs = true;
     }
 #pragma unroll
     for (int k = 0; k < kR; ++k) {
@@ -925,21 +926,31 @@ __device__ void update_in_block(const QUpdate& u, uint32_t* colmax) {
       if (active && d < d_hi) hist[d * n + c] = v[k];
     }
   }
-  if (!have_inputs) {  // H == 1: no chunk ran
-    ab = __hip_atomic_load((uint32_t*)u.amax + tt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    s_old = u.scale[tt];
-    fmt = u.formats[tt];
-  }
-  __syncthreads();  // colmax zeroed (and every chunk done) before the maxima go in
+  __syncthreads();  // colmax zeroed (and every chunk's loads done) before the maxima go in
   if (active && m != 0u) atomicMax(&colmax[c], m);
   __syncthreads();
-  if (tid < n) {
-    uint32_t sel_bits = colmax[tid] > ab ? colmax[tid] : ab;
+  if (tid < n) hist[tid] = colmax[tid];
+}
+
+// The rest, by the block that finishes last (after the roll and every block's amax
+// atomics): thread t < n selects from row 0's column maximum and the new amax (read with
+// device-scope atomic loads), writes the amax into row 0, the new scale and its inverse,
+// and resets the amax if asked.
+__device__ void finish_in_block(const QUpdate& u) {
+  const int tid = threadIdx.x;
+  if (tid < (int)u.n) {
+    // each loading wavefront acquires for itself: its L1 and L2 lines of the history
+    // are dropped before row 0 is read
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    uint32_t* hist = (uint32_t*)u.hist;
+    const uint32_t hm = hist[tid];
+    const uint32_t ab =
+        __hip_atomic_load((uint32_t*)u.amax + tid, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const float s_old = u.scale[tid];
+    const uint32_t fmt = u.formats[tid];
+    uint32_t sel_bits = hm > ab ? hm : ab;
     if (u.algo == FP8Q_AMAX_MOST_RECENT) sel_bits = ab;
-    hist[tid] = ab;  // row 0; loaded (as the source of row 1) before the last barrier
-    // opaque rebind (no instruction): without it the compiler tests fmt right after its
-    // load, which makes the history loads wait for that load first
-    asm volatile("" : "+v"(fmt));
+    hist[tid] = ab;
     const float s = next_scale(sel_bits, fmt, s_old, u.margin);
     u.scale[tid] = s;
     u.scale_inv[tid] = 1.0f / s;
@@ -990,7 +1001,13 @@ __global__ __launch_bounds__(kQBlock) void quantize_amax_kernel(const QTable tab
   quantize_body<kSrc>(tab, sh);
   if constexpr (kUpd) {
     __shared__ uint32_t colmax[kQUpdMaxCols];
-    if (finished_last(tab.upd.counter, sh)) update_in_block(tab.upd, colmax);
+    // every block counts once, the one that rolls the history (the first) twice
+    uint32_t k = arrive<false>(tab.upd.counter, sh);
+    if (k == 0) {
+      roll_in_block(tab.upd, colmax);
+      k = arrive<true>(tab.upd.counter, sh);
+    }
+    if (k == gridDim.x) finish_in_block(tab.upd);
   }
 }
 
