@@ -17,8 +17,10 @@
 //    wavefront butterfly, with no LDS round trip and no block barrier per row.
 //  * gamma and beta are staged once per block into LDS (zero-padded to the unit
 //    grid), read back per element.
-//  * Statistics in binary32 with tree sums (depth log2(8 kV) per lane + 6 across the
-//    wavefront, the latter on the DPP network) and a corrected second pass: mu' = RN(S/H); d' = RN(x - mu');
+//  * Statistics in binary32 with tree sums (depth log2(8 kV) per lane, the squares of
+//    rows over 512 long 8 + log2(kV), + 6 across the wavefront, the latter on the DPP
+//    network; at most ceil(log2 H) + 6 in all) and a corrected second pass:
+//    mu' = RN(S/H); d' = RN(x - mu');
 //    e' = sum(d')/H and V' = sum(d'^2)/H - e'^2 remove the first mean's rounding
 //    error from both the deviations and the variance (rows whose mean is large
 //    against their spread lose no accuracy); y' = RN(fma(d' - e', RN(gamma rstd'),
@@ -199,7 +201,8 @@ __device__ __forceinline__ void unpack8(const uint4& w, float (&x)[8]) {
 // stays packed; each pass re-derives x (and d = RN(x - mu'), bit-identical every time)
 // unit by unit, so only the packed row and a few partial sums stay live.  Sums are
 // trees: 8 elements of a unit (depth 3), then the kV units (depth log2 kV), then the
-// wavefront (depth 6).
+// wavefront (depth 6); for rows longer than 512, the squares of a unit are summed as a
+// chain of fmas (depth 8 instead of 3, 8 instructions instead of 15).
 // Sums of a row split over kSplit wavefronts (2 or 4): each part's wavefront sum goes to
 // LDS and every lane adds the parts as the same tree ((p0 + p1) + (p2 + p3)), so all
 // parts hold the identical value.  `xch` holds 3 floats per part of each row slot: the
@@ -236,40 +239,98 @@ __device__ __forceinline__ void row_total2(float& a, float& b, float* xch, int p
   }
 }
 
+// Rows of up to 8 units per lane, one wavefront per row, keep the unpacked row (then
+// its deviations d') in registers, 8 kV of them, instead of unpacking it again in each
+// pass (3 fewer instructions per element); the packed registers are then free after the
+// first pass and take the wavefront's next row, whose load overlaps this row's last two
+// passes.  Longer rows stay packed (the registers would halve the resident wavefronts).
+template <int kV, int kSplit>
+constexpr bool ln_keep() { return kSplit == 1 && kV <= 8; }
+// Measured (us, events; the row packed in every pass before): 8192 x 4096 28.2 -> kept
+// 26.3, kept with the next row's load after the first pass (3 wavefronts per SIMD at 8
+// units: the next row's registers do not fit under 4) 26.3; 16384 x 2048 28.3 -> 25.1
+// -> 23.7, 32768 x 1024 30.2 -> 27.3 -> 24.6.
+// Squares summed as fma chains (below); measured on 8192 x 4096 against the tree of
+// products: 25.8 vs 26.3 us, one chain of 8: 26.0 us.
+#ifndef FP8Q_LN_SQ_CHAIN
+#define FP8Q_LN_SQ_CHAIN 1
+#endif
+// the next row's load inside ln_row (below); FP8Q_LN_KEEP8_WAVES: wavefronts per SIMD
+// the 8-unit instance is compiled for
+#ifndef FP8Q_LN_PREFETCH
+#define FP8Q_LN_PREFETCH 1
+#endif
+#ifndef FP8Q_LN_KEEP8_WAVES
+#define FP8Q_LN_KEEP8_WAVES 3
+#endif
+
 // `half`: which part of the row's units this wavefront holds (units lane + 64 k +
 // 64 kV half); `row_ok`: false for the padding rows of split blocks (no memory access,
-// nothing accumulated), which still take part in the barriers.
+// nothing accumulated), which still take part in the barriers.  With ln_keep, w[] holds
+// the row `next_rs` covers on return (the next row's load issued after the first pass).
 template <int kFmt, int kV, bool kMasked, int kSplit>
 __device__ __forceinline__ void ln_row(uint4 (&w)[kV], const LnArgs& a, int64_t row,
                                        bool row_ok, int lane, int half, float* xch,
                                        const float* __restrict__ lg,
                                        const float* __restrict__ lb, const LnQuant& q,
-                                       uint32_t& acc) {
+                                       uint32_t& acc, __amdgpu_buffer_rsrc_t next_rs) {
   const float invH = a.inv_h;  // RN(1/H), exact for a power-of-two H
   const int ubase = 64 * kV * half;  // first unit of this wavefront's half
+  constexpr bool kKeep = ln_keep<kV, kSplit>();
+  float xs[kKeep ? kV : 1][8];
   // pass 1: mean (units past the row read as zeros)
   float p1[kV];
 #pragma unroll
   for (int k = 0; k < kV; ++k) {
     float x[8];
     unpack8(w[k], x);
+    if constexpr (kKeep) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) xs[k][j] = x[j];
+    }
     p1[k] = tree_sum(x);
+  }
+  if constexpr (kKeep && FP8Q_LN_PREFETCH) {
+    // the row is unpacked: its registers take the next row (kept below the unpacking)
+    __builtin_amdgcn_sched_barrier(0);
+    ln_load_row<kV>(w, next_rs, lane);
   }
   const float mu = row_total<kSplit>(wave_sum(tree_sum(p1)), xch, half, lane) * invH;
   // pass 2: deviations from mu', their sum and sum of squares
-  rebind(w);
+  if constexpr (!kKeep) rebind(w);
   float s1[kV], s2[kV];
 #pragma unroll
   for (int k = 0; k < kV; ++k) {
     float x[8], sq[8];
-    unpack8(w[k], x);
+    if constexpr (kKeep) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      x[j] = x[j] - mu;
-      sq[j] = x[j] * x[j];
+      for (int j = 0; j < 8; ++j) x[j] = xs[k][j];
+    } else {
+      unpack8(w[k], x);
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) x[j] = x[j] - mu;
+    if constexpr (kKeep) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) xs[k][j] = x[j];
+    }
+    if constexpr (kV * kSplit >= 2 && FP8Q_LN_SQ_CHAIN) {
+      // the unit's squares as two chains of 4 fmas (one rounding per element) and their
+      // sum: depth 5 instead of 3, which rows over 512 long have room for under the
+      // depth bound ceil(log2 H) + 6; 9 instructions instead of 15
+      float qa = x[0] * x[0], qb = x[1] * x[1];
+#pragma unroll
+      for (int j = 2; j < 8; j += 2) {
+        qa = __builtin_fmaf(x[j], x[j], qa);
+        qb = __builtin_fmaf(x[j + 1], x[j + 1], qb);
+      }
+      s2[k] = qa + qb;
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) sq[j] = x[j] * x[j];
+      s2[k] = tree_sum(sq);
     }
     s1[k] = tree_sum(x);
-    s2[k] = tree_sum(sq);
     if (kMasked && ubase + lane + 64 * k >= a.nunits) s1[k] = s2[k] = 0.0f;
   }
   float t1 = tree_sum(s1), t2 = tree_sum(s2);
@@ -287,21 +348,30 @@ __device__ __forceinline__ void ln_row(uint4 (&w)[kV], const LnArgs& a, int64_t 
     if (a.rstd_out) a.rstd_out[row] = rstd;
   }
   // pass 3: y, its bf16 rounding, the codes and the amax
-  rebind(w);
+  if constexpr (!kKeep) rebind(w);
   const __amdgpu_buffer_rsrc_t out =
       ln_rsrc(a.dst + (row_ok ? row * (int64_t)a.H : 0), row_ok ? (uint32_t)a.H : 0u);
 #pragma unroll
   for (int k = 0; k < kV; ++k) {
     const int unit = ubase + lane + 64 * k;
-    const float4* g4 = (const float4*)(lg + 8 * unit);
-    const float4* b4 = (const float4*)(lb + 8 * unit);
-    const float4 g0 = g4[0], g1 = g4[1], b0 = b4[0], b1 = b4[1];
+    // gamma/beta of the unit's first 4 and last 4 columns (two planes: consecutive lanes
+    // read consecutive 16 bytes)
+    constexpr int kPlane = 64 * kV * kSplit;  // units, i.e. float4s per plane
+    const float4* g4 = (const float4*)lg;
+    const float4* b4 = (const float4*)lb;
+    const float4 g0 = g4[unit], g1 = g4[kPlane + unit], b0 = b4[unit], b1 = b4[kPlane + unit];
     const float gv[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
     const float bv[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
-    float x[8], y[8];
-    unpack8(w[k], x);
+    float y[8];
+    if constexpr (kKeep) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) y[j] = __builtin_fmaf((x[j] - mu) - e, gv[j] * rstd, bv[j]);
+      for (int j = 0; j < 8; ++j) y[j] = __builtin_fmaf(xs[k][j] - e, gv[j] * rstd, bv[j]);
+    } else {
+      float x[8];
+      unpack8(w[k], x);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) y[j] = __builtin_fmaf((x[j] - mu) - e, gv[j] * rstd, bv[j]);
+    }
     uint4 yw = make_uint4(pack_bf16_rne(y[0], y[1]), pack_bf16_rne(y[2], y[3]),
                           pack_bf16_rne(y[4], y[5]), pack_bf16_rne(y[6], y[7]));
     uint32_t mg = mag8_bf16(yw);
@@ -346,12 +416,23 @@ __device__ __forceinline__ void ln_row(uint4 (&w)[kV], const LnArgs& a, int64_t 
   }
 }
 
+// Rows kept unpacked (ln_keep) are held to the register count at which kLBlocksPerCU
+// blocks of 4 wavefronts fit each CU (one wavefront of each block per SIMD).
+template <int kV, int kSplit>
+constexpr int ln_waves_per_eu() {
+  return !ln_keep<kV, kSplit>() ? 1 : kV == 8 ? FP8Q_LN_KEEP8_WAVES : kLBlocksPerCU;
+}
+
 template <int kFmt, int kV, bool kMasked, int kSplit>
 __global__ __launch_bounds__((ln_block<kV, kSplit>()))
+__attribute__((amdgpu_waves_per_eu(ln_waves_per_eu<kV, kSplit>())))
 void ln_quantize_kernel(const LnArgs a) {
   constexpr int kBlk = ln_block<kV, kSplit>();
   // gamma then beta, each 512 kV kSplit floats, zero-padded; 16-byte aligned for the
-  // b128 reads
+  // b128 reads.  Each is stored as two planes, columns 8u..8u+3 of every unit u, then
+  // columns 8u+4..8u+7, so that a wavefront's reads of one plane (lane l: unit base + l)
+  // are 64 consecutive 16-byte pieces, free of bank conflicts (unit-major order puts
+  // lanes 32 bytes apart: 2-way conflicts).
   extern __shared__ __attribute__((aligned(16))) float lds[];
   __shared__ uint32_t block_amax;
   __shared__ float xch_all[kSplit > 1 ? 3 * kSplit * ln_rows_per_block<kV, kSplit>() : 1];
@@ -380,15 +461,17 @@ void ln_quantize_kernel(const LnArgs a) {
     for (int it = 0; it < kIt; ++it) {
       const int i4 = threadIdx.x + it * kBlk;
       if (4 * i4 < kPad) {
-        ((float4*)lg)[i4] = gs[it];
-        ((float4*)lb)[i4] = bs[it];
+        const int p4 = (i4 & 1) * (kPad / 8) + (i4 >> 1);  // plane, unit
+        ((float4*)lg)[p4] = gs[it];
+        ((float4*)lb)[p4] = bs[it];
       }
     }
   } else {
     for (int i = threadIdx.x; i < kPad; i += kBlk) {
       const bool in = i < a.H;
-      lg[i] = in ? (a.gamma ? a.gamma[i] : 1.0f) : 0.0f;
-      lb[i] = in ? (a.beta ? a.beta[i] : 0.0f) : 0.0f;
+      const int p = ((i >> 2) & 1) * (kPad / 2) + (i >> 3) * 4 + (i & 3);  // plane, unit, column
+      lg[p] = in ? (a.gamma ? a.gamma[i] : 1.0f) : 0.0f;
+      lb[p] = in ? (a.beta ? a.beta[i] : 0.0f) : 0.0f;
     }
   }
   if (threadIdx.x == 0) block_amax = 0;
@@ -403,11 +486,24 @@ void ln_quantize_kernel(const LnArgs a) {
 
   uint32_t acc = 0;
   if constexpr (kSplit == 1) {
-    // one row at a time: latency is hidden by the other resident wavefronts
-    for (; row < a.rows; row += nwaves) {
-      uint4 w[kV];
-      ln_load_row<kV>(w, ln_rsrc(a.x + row * a.H, row_bytes), lane);
-      ln_row<kFmt, kV, kMasked, 1>(w, a, row, true, lane, 0, nullptr, lg, lb, q, acc);
+    uint4 w[kV];
+    if constexpr (ln_keep<kV, kSplit>() && FP8Q_LN_PREFETCH) {
+      // the next row is loaded inside ln_row, after the current row's first pass (a
+      // row past the end has an empty resource and reads zeros)
+      if (row < a.rows) ln_load_row<kV>(w, ln_rsrc(a.x + row * a.H, row_bytes), lane);
+      for (; row < a.rows; row += nwaves) {
+        const int64_t nx = row + nwaves;
+        const __amdgpu_buffer_rsrc_t nrs =
+            nx < a.rows ? ln_rsrc(a.x + nx * a.H, row_bytes) : ln_rsrc(a.x, 0u);
+        ln_row<kFmt, kV, kMasked, 1>(w, a, row, true, lane, 0, nullptr, lg, lb, q, acc, nrs);
+      }
+    } else {
+      // one row at a time: latency is hidden by the other resident wavefronts
+      for (; row < a.rows; row += nwaves) {
+        ln_load_row<kV>(w, ln_rsrc(a.x + row * a.H, row_bytes), lane);
+        ln_row<kFmt, kV, kMasked, 1>(w, a, row, true, lane, 0, nullptr, lg, lb, q, acc,
+                                     ln_rsrc(a.x, 0u));
+      }
     }
   } else {
     // wavefronts kSplit r .. kSplit r + kSplit - 1 hold the parts of row slot r; every
@@ -427,7 +523,8 @@ void ln_quantize_kernel(const LnArgs a) {
                        row_bytes > 1024u * kV * half ? row_bytes - 1024u * kV * half : 0u)
              : ln_rsrc(a.x, 0u);
       ln_load_row<kV>(w, rs, lane);
-      ln_row<kFmt, kV, kMasked, kSplit>(w, a, r, ok, lane, half, xch, lg, lb, q, acc);
+      ln_row<kFmt, kV, kMasked, kSplit>(w, a, r, ok, lane, half, xch, lg, lb, q, acc,
+                                        ln_rsrc(a.x, 0u));
     }
   }
   // block amax: packed halves -> wavefront -> LDS -> one global atomic
