@@ -50,8 +50,11 @@ constexpr int kLMaxH = 16384;      // 64 lanes x 32 units x 8 elements
 #ifndef FP8Q_LN_BLOCKS_PER_CU
 #define FP8Q_LN_BLOCKS_PER_CU 4
 #endif
+// A scheduling barrier after each unit of the last pass (below): measured slower once
+// the next unit's gamma/beta are read during the current unit (8192 x 12288 75.2 vs 74.1
+// us, 4096 x 16384 54.6 vs 52.6), so off.
 #ifndef FP8Q_LN_UNIT_BARRIER
-#define FP8Q_LN_UNIT_BARRIER 1
+#define FP8Q_LN_UNIT_BARRIER 0
 #endif
 constexpr int kLBlocksPerCU = FP8Q_LN_BLOCKS_PER_CU;
 // Wavefronts per row for 24 and 32 units per lane (hidden 8200-12288, 12296-16384).
@@ -257,6 +260,12 @@ constexpr bool ln_keep() { return kSplit == 1 && kV <= 8; }
 #endif
 // the next row's load inside ln_row (below); FP8Q_LN_KEEP8_WAVES: wavefronts per SIMD
 // the 8-unit instance is compiled for
+// The next unit's gamma/beta read from LDS during the current unit of the last pass:
+// with FP8Q_LN_UNIT_BARRIER off, 8192 x 4096 26.0 -> 25.4 us, 8192 x 12288 78.4 -> 74.1,
+// 4096 x 16384 55.6 -> 52.6 (one box, one run).
+#ifndef FP8Q_LN_GB_PREFETCH
+#define FP8Q_LN_GB_PREFETCH 1
+#endif
 #ifndef FP8Q_LN_PREFETCH
 #define FP8Q_LN_PREFETCH 1
 #endif
@@ -351,15 +360,41 @@ __device__ __forceinline__ void ln_row(uint4 (&w)[kV], const LnArgs& a, int64_t 
   if constexpr (!kKeep) rebind(w);
   const __amdgpu_buffer_rsrc_t out =
       ln_rsrc(a.dst + (row_ok ? row * (int64_t)a.H : 0), row_ok ? (uint32_t)a.H : 0u);
+  // gamma/beta of a unit's first 4 and last 4 columns (two planes: consecutive lanes
+  // read consecutive 16 bytes)
+  constexpr int kPlane = 64 * kV * kSplit;  // units, i.e. float4s per plane
+  const float4* g4 = (const float4*)lg;
+  const float4* b4 = (const float4*)lb;
+  float4 gb_next[4];
+  if constexpr (FP8Q_LN_GB_PREFETCH) {
+    const int u0 = ubase + lane;
+    gb_next[0] = g4[u0];
+    gb_next[1] = g4[kPlane + u0];
+    gb_next[2] = b4[u0];
+    gb_next[3] = b4[kPlane + u0];
+  }
 #pragma unroll
   for (int k = 0; k < kV; ++k) {
     const int unit = ubase + lane + 64 * k;
-    // gamma/beta of the unit's first 4 and last 4 columns (two planes: consecutive lanes
-    // read consecutive 16 bytes)
-    constexpr int kPlane = 64 * kV * kSplit;  // units, i.e. float4s per plane
-    const float4* g4 = (const float4*)lg;
-    const float4* b4 = (const float4*)lb;
-    const float4 g0 = g4[unit], g1 = g4[kPlane + unit], b0 = b4[unit], b1 = b4[kPlane + unit];
+    float4 g0, g1, b0, b1;
+    if constexpr (FP8Q_LN_GB_PREFETCH) {
+      // this unit's values were read during the previous unit; read the next unit's now
+      g0 = gb_next[0];
+      g1 = gb_next[1];
+      b0 = gb_next[2];
+      b1 = gb_next[3];
+      if (k + 1 < kV) {
+        gb_next[0] = g4[unit + 64];
+        gb_next[1] = g4[kPlane + unit + 64];
+        gb_next[2] = b4[unit + 64];
+        gb_next[3] = b4[kPlane + unit + 64];
+      }
+    } else {
+      g0 = g4[unit];
+      g1 = g4[kPlane + unit];
+      b0 = b4[unit];
+      b1 = b4[kPlane + unit];
+    }
     const float gv[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
     const float bv[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
     float y[8];
