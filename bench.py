@@ -282,7 +282,17 @@ class StepBench:
              "value_gbps": (qb + ub) / (ms * 1e-3) / 1e9,
              "q_avg_us": q_avg, "q_median_us": 1e3 * float(np.median(q_ms)),
              "q_gbps": qb / (q_avg * 1e-6) / 1e9, "u_gap_avg_us": 1e3 * float(np.mean(u_ms))}
-        one_ms, one_dev, one_enq = region(lambda k: self.one_launch_step())
+        # the two forms compared in alternating regions (one-launch first), so that a
+        # drift of the clock over the run does not favour either; medians of 3 each
+        pairs = []
+        for _ in range(3):
+            pairs.append((region(lambda k: self.one_launch_step()),
+                          region(lambda k: self.step())))
+        one_ms = float(np.median([p[0][0] for p in pairs]))
+        one_dev = float(np.median([p[0][1] for p in pairs]))
+        one_enq = float(np.median([p[0][2] for p in pairs]))
+        two_ms = float(np.median([p[1][0] for p in pairs]))
+        two_dev = float(np.median([p[1][1] for p in pairs]))
         ev1 = make_events()
         region(lambda k: self.one_launch_step(ev1[k]))
         s_ms = [ev1[k][0].elapsed_time(ev1[k][1]) for k in range(K)]
@@ -291,6 +301,9 @@ class StepBench:
             "entry": "fp8_quantize_amax_and_update (quantize + amax + update, one launch)",
             "ms_per_step": round(one_ms, 5), "device_ms_per_step": round(one_dev, 5),
             "host_enqueue_us_per_step": round(one_enq, 2),
+            "two_launch_ms_per_step": round(two_ms, 5),
+            "two_launch_device_ms_per_step": round(two_dev, 5),
+            "timing": "medians of 3 regions of K steps per form, the forms alternating",
             "value_gbps": round((qb + ub) / (one_ms * 1e-3) / 1e9, 2),
             "kernel_avg_us": round(s_avg, 3),
             "kernel_median_us": round(1e3 * float(np.median(s_ms)), 3),
@@ -299,9 +312,10 @@ class StepBench:
             "avg %.2f us (median %.2f) = %.1f GB/s; update + gaps avg %.2f us" % (
                 self.w.name, ms, dev_ms, enq, r["value_gbps"], q_avg, r["q_median_us"],
                 r["q_gbps"], r["u_gap_avg_us"]))
-        log("%s: one-launch step %.4f ms (device %.4f ms) = %.1f GB/s; kernel avg %.2f us "
-            "(median %.2f)" % (self.w.name, one_ms, one_dev, r["one_launch"]["value_gbps"],
-                               s_avg, r["one_launch"]["kernel_median_us"]))
+        log("%s: one-launch step %.4f ms (device %.4f ms) = %.1f GB/s vs two launches %.4f ms "
+            "(device %.4f ms) in alternating regions; kernel avg %.2f us (median %.2f)" % (
+                self.w.name, one_ms, one_dev, r["one_launch"]["value_gbps"], two_ms, two_dev,
+                s_avg, r["one_launch"]["kernel_median_us"]))
         return r
 
 

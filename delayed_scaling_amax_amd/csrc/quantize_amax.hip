@@ -333,6 +333,55 @@ __device__ __forceinline__ uint4 gelu8_bf16(uint4 w) {
   return y;
 }
 
+// ---------------------------------------------------------------- gelu table
+// A bf16 input has 65536 bit patterns, so the full-chunk passes of the gelu instance
+// look its output up instead of evaluating it: gelu_bf16 of every pattern, built on each
+// device by gelu_table_kernel (the same arithmetic as above, run once per device before
+// its first gelu launch), copied into each block's LDS at kernel start (128 KB: the
+// instance runs one block per CU) and read with 16-bit gathers -- one LDS read and about
+// one address instruction per element instead of ten instructions, two of them
+// transcendental.  The remainders (phase 2) still evaluate per element, with the same
+// gelu_bf16.  FP8Q_Q_GELU_TABLE 0 keeps the evaluated form everywhere.
+#ifndef FP8Q_Q_GELU_TABLE
+#define FP8Q_Q_GELU_TABLE 1
+#endif
+constexpr bool kQGeluTable = FP8Q_Q_GELU_TABLE != 0;
+constexpr int kQGeluTableBytes = 65536 * 2;
+static __device__ __attribute__((aligned(16))) uint16_t g_gelu_table[65536];
+
+__global__ __launch_bounds__(256) void gelu_table_kernel() {
+  const uint32_t h = blockIdx.x * 256u + threadIdx.x;  // grid of 256 blocks: every pattern
+  g_gelu_table[h] = (uint16_t)gelu_bf16(h);
+}
+
+// the gelu instance's dynamic LDS: the table
+extern __shared__ __attribute__((aligned(16))) uint16_t q_gelu_lds[];
+
+// Copy the table into this block's LDS by LDS DMA (16 bytes per lane, 1 KB per
+// wavefront instruction, no registers), then wait for it and publish it to the block.
+__device__ __forceinline__ void gelu_table_to_lds() {
+  typedef __attribute__((address_space(3))) uint8_t lds_u8;
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)g_gelu_table, (short)0, kQGeluTableBytes, 0x00020000);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const uint32_t lane = threadIdx.x & 63;
+  constexpr int kPieces = kQGeluTableBytes / 1024 / (kQBlock / 64);  // 1 KB pieces per wave
+#pragma unroll
+  for (int j = 0; j < kPieces; ++j) {
+    const uint32_t piece = (uint32_t)(wave * kPieces + j);  // wave-uniform
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rs, (__attribute__((address_space(3))) void*)((lds_u8*)q_gelu_lds + 1024 * piece), 16,
+        piece * 1024u + lane * 16u, 0, 0, 0);
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+}
+
+// gelu of the two bf16 values of w, from the LDS table
+__device__ __forceinline__ uint32_t gelu2_lds(uint32_t w) {
+  return (uint32_t)q_gelu_lds[w & 0xFFFFu] | ((uint32_t)q_gelu_lds[w >> 16] << 16);
+}
+
 // ---------------------------------------------------------------- per-tensor constants
 // Filled once per block at kernel start (one thread per tensor) so that switching to
 // the next tensor costs an LDS read, not a dependent global load.
@@ -662,7 +711,22 @@ __device__ __forceinline__ void run_full_chunks(const Tab& tab, Sh& sh, int t_be
       uint2 o[kU] = {};
       if (real) {
         uint32_t pm = 0;  // pass magnitude max
-        if constexpr (kGelu) {
+        if constexpr (kGelu && kQGeluTable) {
+          // table lookups; the table holds the patched outputs of non-finite inputs
+#pragma unroll
+          for (int u = 0; u < kU; ++u) {
+            const uint4 x = cur.w[u][0];
+            cur.w[u][0] = make_uint4(gelu2_lds(x.x), gelu2_lds(x.y), gelu2_lds(x.z),
+                                     gelu2_lds(x.w));
+            pm = pk_max_u16(pm, mag8_bf16(cur.w[u][0]));
+          }
+          // no saturation needed when no |y| of the pass exceeds clim (<= FP8_MAX * s)
+          const bool nosat = __builtin_amdgcn_ballot_w64(max_halves(pm) > clim) == 0;
+#pragma unroll
+          for (int u = 0; u < kU; ++u)
+            o[u] = nosat ? codes8_bf16_unsaturated<kFmt>(cur.w[u][0], s, r)
+                         : codes8_bf16<kFmt>(cur.w[u][0], s, r);
+        } else if constexpr (kGelu) {
           // the direct gelu form unless some input of the pass is <= -9 (wave-uniform)
           uint32_t raw = 0;
 #pragma unroll
@@ -998,6 +1062,7 @@ __device__ __forceinline__ void quantize_body(const Tab& tab, Sh& sh) {
 template <int kSrc, bool kUpd>
 __global__ __launch_bounds__(kQBlock) void quantize_amax_kernel(const QTable tab) {
   __shared__ QShared sh;
+  if constexpr (kSrc == 4 && kQGeluTable) gelu_table_to_lds();
   quantize_body<kSrc>(tab, sh);
   if constexpr (kUpd) {
     __shared__ uint32_t colmax[kQUpdMaxCols];
@@ -1058,6 +1123,24 @@ static void plan_entry(const fp8q_tensor& t, bool gelu, QEntry* e) {
   e->nfull = e->n_vec / kQChunk;
 }
 
+// Build the gelu table on the current device before its first gelu launch: one small
+// kernel on `stream`, then a synchronisation of `stream` (once per device and process),
+// so that launches on any stream find it complete.
+static int ensure_gelu_table(hipStream_t stream) {
+  static std::atomic<bool> ready[64];
+  static std::mutex lock;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return FP8Q_EHIP;
+  if (ready[dev].load(std::memory_order_acquire)) return FP8Q_OK;
+  std::lock_guard<std::mutex> g(lock);
+  if (ready[dev].load(std::memory_order_relaxed)) return FP8Q_OK;
+  hipLaunchKernelGGL(gelu_table_kernel, dim3(256), dim3(256), 0, stream);
+  if (hipGetLastError() != hipSuccess) return FP8Q_EHIP;
+  if (hipStreamSynchronize(stream) != hipSuccess) return FP8Q_EHIP;
+  ready[dev].store(true, std::memory_order_release);
+  return FP8Q_OK;
+}
+
 // Launch one table.  `start`/`stop` (may be null): events that take the start and stop
 // time of this kernel's own dispatch (hipExtLaunchKernel), for profiling.  *launched
 // tells whether a kernel was enqueued (a table of empty tensors enqueues nothing).
@@ -1087,14 +1170,24 @@ static int launch_table(QTable* tab, bool upd, hipStream_t stream, hipEvent_t st
          : src_kinds == 3 ? (const void*)quantize_amax_kernel<3, true>
                           : nullptr;
   if (fn == nullptr) return FP8Q_EINVAL;
+  // the gelu instance reads its table from dynamic LDS
+  const bool table = src_kinds == 4 && kQGeluTable;
+  const size_t smem = table ? (size_t)kQGeluTableBytes : 0;
+  if (table) {
+    st = ensure_gelu_table(stream);
+    if (st != FP8Q_OK) return st;
+  }
   // The grid-stride schedule needs every block resident at once: cap the blocks per
-  // CU at what the instance's register use allows.
+  // CU at what the instance's register and LDS use allow.
   static std::atomic<int> fit[16];
   const int inst = src_kinds + (upd ? 8 : 0);
   int per_cu = fit[inst].load(std::memory_order_relaxed);
   if (per_cu <= 0) {
+    if (table && hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                     (int)smem) != hipSuccess)
+      return FP8Q_EHIP;
     int occ = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, fn, kQBlock, 0) != hipSuccess)
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, fn, kQBlock, smem) != hipSuccess)
       return FP8Q_EHIP;
     const int want = src_kinds == 4 ? kQGeluBlocksPerCU : kQBlocksPerCU;
     per_cu = occ < want ? (occ > 0 ? occ : 1) : want;
@@ -1108,9 +1201,9 @@ static int launch_table(QTable* tab, bool upd, hipStream_t stream, hipEvent_t st
   *launched = true;
   if (start == nullptr && stop == nullptr)
     return launch_status(
-        hipLaunchKernel(fn, dim3((unsigned)blocks), dim3(kQBlock), args, 0, stream));
-  return launch_status(hipExtLaunchKernel(fn, dim3((unsigned)blocks), dim3(kQBlock), args, 0,
-                                          stream, start, stop, 0));
+        hipLaunchKernel(fn, dim3((unsigned)blocks), dim3(kQBlock), args, smem, stream));
+  return launch_status(hipExtLaunchKernel(fn, dim3((unsigned)blocks), dim3(kQBlock), args,
+                                          smem, stream, start, stop, 0));
 }
 
 // Quantize n tensors (with the gelu prologue on every one if `gelu`), at most

@@ -223,6 +223,12 @@ int fp8_multi_quantize_amax_timed(const fp8q_tensor* tensors, int n, void* strea
  * gelu, so it is the correctly rounded bf16 of gelu(x) except where that lies within
  * this distance of a bf16 rounding midpoint (then it may be the other neighbour).
  * gelu(+inf) = +inf, gelu(-inf) = -0, gelu(NaN) = NaN with the sign of x.
+ * The bulk of the tensor reads y from a table of these values for all 65536 bf16
+ * inputs, which the library builds on each device, with the same binary32 arithmetic,
+ * before the first call on that device runs: that first call launches one extra small
+ * kernel on `stream` and synchronizes `stream` once (so it must not be captured into a
+ * graph); every later call is one launch.  The table is device memory of the library
+ * (128 KB per device, kept until the process ends).
  *   src_dtype  FP8Q_BF16 (FP8Q_F32 returns FP8Q_EUNSUPPORTED).   format  as above.
  *   numel, pointers, alignment, amax accumulation and errors as fp8_quantize_amax.
  * Returns FP8Q_OK, FP8Q_EINVAL, FP8Q_EUNSUPPORTED or FP8Q_EHIP.
