@@ -148,6 +148,19 @@ def test_history_shapes_at_the_fused_limits(orc, H, n_upd):
         st.run(orc)
 
 
+@pytest.mark.parametrize("H,n_upd", [(1, 1), (16, 1), (1024, 3), (2, 256)])
+def test_one_block_grid(orc, H, n_upd):
+    """A step small enough for a one-block grid: the block that rolls the history (the
+    first to finish) is also the last, so it counts twice and then finishes the update."""
+    g = np.random.Generator(np.random.PCG64(9350 + H + n_upd))
+    xs = [bf16(g, 100, 3.0)]
+    hist = np.exp(g.normal(0, 2, (H, n_upd))).astype(np.float32)
+    note("fused step, one-block grid: H %d n %d" % (H, n_upd))
+    st = Step(xs, [E4M3], H, n_upd=n_upd, hist=hist)
+    for _ in range(3):
+        st.run(orc)
+
+
 @pytest.mark.parametrize("case", ["40 tensors", "H n > 65536", "257 columns", "all empty"])
 def test_two_launch_forms(orc, case):
     """Calls the single launch does not take give the same results through two launches."""
