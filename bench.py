@@ -408,7 +408,7 @@ def main():
     if args.steps < 1 or args.warmup < 0 or args.rotate < 1 or args.update_calls < 1:
         ap.error("--steps, --rotate and --update-calls must be >= 1, --warmup >= 0")
     if args.gpus != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (the amax "
+        print("bench.py measures one GPU: this library has no multi-GPU path (the amax "
               "all-reduce across replicas is described in the design notes, not built); "
               "run with --gpus 1", file=sys.stderr)
         sys.exit(2)

@@ -71,7 +71,7 @@ enum { FP8Q_AMAX_MAX = 0, FP8Q_AMAX_MOST_RECENT = 1 };
 enum {
   FP8Q_OK = 0,
   FP8Q_EINVAL = -1,       /* invalid argument; nothing was enqueued            */
-  FP8Q_EUNSUPPORTED = -2, /* valid request this build cannot serve              */
+  FP8Q_EUNSUPPORTED = -2, /* valid request this library cannot serve            */
   FP8Q_EHIP = -3          /* a HIP runtime call or kernel launch failed          */
 };
 
