@@ -178,6 +178,8 @@ struct LnQuant {
   uint32_t xlim;
   uint32_t clim;  // sat_limit_bf16(s): units whose |y| stay within need no saturation
   bool win;
+  float gmax;     // max |gamma| of the block's staged gamma
+  bool gb_fin;    // every staged gamma and beta is finite
 };
 
 // Make the packed row opaque to the compiler between passes (an empty asm that
@@ -258,13 +260,19 @@ constexpr bool ln_keep() { return kSplit == 1 && kV <= 8; }
 #ifndef FP8Q_LN_SQ_CHAIN
 #define FP8Q_LN_SQ_CHAIN 1
 #endif
-// the next row's load inside ln_row (below); FP8Q_LN_KEEP8_WAVES: wavefronts per SIMD
-// the 8-unit instance is compiled for
+// the next row's load inside ln_row (below), after the first pass (issued before it, so
+// that the registers of both rows are live through the first pass, the 8-unit instance
+// spills: 67 us on 8192 x 4096); FP8Q_LN_KEEP8_WAVES: wavefronts per SIMD the 8-unit
+// instance is compiled for
 // The next unit's gamma/beta read from LDS during the current unit of the last pass:
 // with FP8Q_LN_UNIT_BARRIER off, 8192 x 4096 26.0 -> 25.4 us, 8192 x 12288 78.4 -> 74.1,
 // 4096 x 16384 55.6 -> 52.6 (one box, one run).
 #ifndef FP8Q_LN_GB_PREFETCH
 #define FP8Q_LN_GB_PREFETCH 1
+#endif
+// Rows known to give no NaN skip the per-unit NaN test (below): 0.8 % on 8192 x 4096.
+#ifndef FP8Q_LN_ROWFIN
+#define FP8Q_LN_ROWFIN 1
 #endif
 #ifndef FP8Q_LN_PREFETCH
 #define FP8Q_LN_PREFETCH 1
@@ -352,6 +360,12 @@ __device__ __forceinline__ void ln_row(uint4 (&w)[kV], const LnArgs& a, int64_t 
   // hardware reciprocal square root (1 ulp) where its input is normal; the IEEE
   // square root and divide for a subnormal (or zero) V + eps
   const float rstd = ve >= 0x1p-126f ? __builtin_amdgcn_rsqf(ve) : 1.0f / __builtin_sqrtf(ve);
+  // A row whose mean is finite (every x finite), whose rstd is finite and positive (every
+  // d' and e' finite) and whose gamma rstd products stay finite, with finite gamma and
+  // beta, gives no NaN y (an fma of finite operands is finite or overflows to an
+  // infinity): its units skip the NaN test.  Wave-uniform (mu, rstd are).
+  const bool row_fin = FP8Q_LN_ROWFIN && q.gb_fin && (as_uint(mu) & 0x7FFFFFFFu) < 0x7F800000u &&
+                       rstd > 0.0f && q.gmax * rstd < __builtin_inff();
   if (lane == 0 && half == 0 && row_ok) {
     if (a.mean_out) a.mean_out[row] = mu + e;
     if (a.rstd_out) a.rstd_out[row] = rstd;
@@ -410,7 +424,7 @@ __device__ __forceinline__ void ln_row(uint4 (&w)[kV], const LnArgs& a, int64_t 
     uint4 yw = make_uint4(pack_bf16_rne(y[0], y[1]), pack_bf16_rne(y[2], y[3]),
                           pack_bf16_rne(y[4], y[5]), pack_bf16_rne(y[6], y[7]));
     uint32_t mg = mag8_bf16(yw);
-    if (__builtin_amdgcn_ballot_w64(halves_nan(mg) != 0) != 0) {  // rare: NaN rows
+    if (!row_fin && __builtin_amdgcn_ballot_w64(halves_nan(mg) != 0) != 0) {  // rare: NaN rows
       uint32_t o[4] = {yw.x, yw.y, yw.z, yw.w};
 #pragma unroll
       for (int h = 0; h < 4; ++h) {
@@ -510,6 +524,8 @@ void ln_quantize_kernel(const LnArgs a) {
     }
   }
   if (threadIdx.x == 0) block_amax = 0;
+  __shared__ uint32_t gb_gmax, gb_bmax;  // max |gamma|, max |beta| bits
+  if (threadIdx.x == 0) gb_gmax = gb_bmax = 0;
 
   LnQuant q;
   q.s = uniform(*a.scale);
@@ -518,6 +534,28 @@ void ln_quantize_kernel(const LnArgs a) {
   q.xlim = min(as_uint(q.s * 0x1p126f) >> 16, 0x7F80u);
   q.clim = sat_limit_bf16<kFmt>(q.s);
   __syncthreads();
+  // the staged gamma's largest magnitude and whether gamma and beta are all finite
+  // (magnitude bits: unsigned order is magnitude order; inf and NaN lie at or above
+  // 0x7F800000)
+  {
+    uint32_t gm = 0, bm = 0;
+    for (int i = threadIdx.x; i < kPad / 4; i += kBlk) {
+      const uint4 g4 = ((const uint4*)lg)[i], b4 = ((const uint4*)lb)[i];
+      gm = max(max(max(gm, g4.x & 0x7FFFFFFFu), max(g4.y & 0x7FFFFFFFu, g4.z & 0x7FFFFFFFu)),
+               g4.w & 0x7FFFFFFFu);
+      bm = max(max(max(bm, b4.x & 0x7FFFFFFFu), max(b4.y & 0x7FFFFFFFu, b4.z & 0x7FFFFFFFu)),
+               b4.w & 0x7FFFFFFFu);
+    }
+    gm = wave_max_u32(gm);
+    bm = wave_max_u32(bm);
+    if ((threadIdx.x & 63) == 0) {
+      atomicMax(&gb_gmax, gm);
+      atomicMax(&gb_bmax, bm);
+    }
+    __syncthreads();
+    q.gmax = as_float(gb_gmax);
+    q.gb_fin = gb_gmax < 0x7F800000u && gb_bmax < 0x7F800000u;
+  }
 
   uint32_t acc = 0;
   if constexpr (kSplit == 1) {

@@ -150,6 +150,24 @@ def test_ln_special_rows(orc):
     check_ln(orc, x, E4M3, 0.02, gamma, beta, eps=1e-6)
 
 
+@pytest.mark.parametrize("H", [1024, 4096])
+def test_ln_nonfinite_beta_and_huge_gamma(orc, H):
+    """beta with a NaN and an inf column (every row's y there is NaN / inf: the kernel's
+    per-unit NaN handling stays on for the whole launch), and gamma of 1e38 in a few
+    columns with finite beta (y overflows to +-inf there, never to NaN, in rows the kernel
+    treats as giving no NaN)."""
+    x = ln_input(740 + H, 8, H, offset=0.25)
+    gamma, beta = affine(741, H)
+    b2 = beta.copy()
+    b2[3], b2[H - 2] = np.float32(np.nan), np.float32(np.inf)
+    note("ln H=%d beta with NaN and inf" % H)
+    check_ln(orc, x, E4M3, 0.02, gamma, b2)
+    g2 = gamma.copy()
+    g2[[1, 100, H - 1]] = np.float32(1e38)
+    note("ln H=%d gamma 1e38 in 3 columns" % H)
+    check_ln(orc, x, E5M2, 1.0, g2, beta)
+
+
 @pytest.mark.parametrize("scale", [2.0 ** -100, 0.0, float("inf"), float("nan"), -0.5, 3e38])
 def test_ln_odd_scales(orc, scale):
     x = ln_input(730, 24, 768)
