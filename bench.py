@@ -326,7 +326,34 @@ def probe_lib():
     lib.probe_stream.restype = i32
     lib.probe_update_floor.argtypes = [vp, i64, i64, i32, vp]
     lib.probe_update_floor.restype = i32
+    lib.probe_mfma.argtypes = [i32, i32, vp, vp, vp, vp]
+    lib.probe_mfma.restype = i32
     return lib
+
+
+def mfma_ceiling(plib, dev, cus, iters=2000, reps=5):
+    """The FP8 matrix cores' sustained rate with register operands only (probe_mfma: one
+    block of 4 wavefronts per CU, each wavefront iters x 16 independent 32x32x64 MFMAs),
+    the best of `reps` launches timed with events taken by the kernel's own dispatch."""
+    torch = __import__("torch")
+    sink = torch.empty(cus * 256, dtype=torch.float32, device=dev)
+    flops = float(cus) * 4 * iters * 16 * 2 * 32 * 32 * 64
+    cs = torch.cuda.current_stream().cuda_stream
+    best = None
+    for _ in range(reps + 1):  # the first launch loads the kernel
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        b.record()
+        torch.cuda.synchronize()
+        st = plib.probe_mfma(cus, iters, ctypes.c_void_p(sink.data_ptr()), ctypes.c_void_p(cs),
+                             ctypes.c_void_p(a.cuda_event), ctypes.c_void_p(b.cuda_event))
+        if st != 0:
+            raise RuntimeError("probe_mfma failed: %d" % st)
+        torch.cuda.synchronize()
+        us = a.elapsed_time(b) * 1e3
+        best = us if best is None or us < best else best
+    return {"pflops": round(flops / best / 1e9, 3), "best_us": round(best, 2),
+            "launch": "%d blocks x 4 wavefronts, %d x 16 MFMA 32x32x64 FP8 each" % (cus, iters)}
 
 
 def stream_ceiling(plib, dev, units, sets, reps, cus):
@@ -805,6 +832,11 @@ def main():
                 if "torch_scaled_mm_us" in rec else ""))
             del gc
         del h_codes
+        if not args.no_probes:
+            # the ceiling the GEMM is measured against: the same MFMA with register operands
+            gemm_out["mfma_ceiling"] = mfma_ceiling(probe_lib(), dev, cus)
+            log("mfma ceiling (register operands, 32x32x64 FP8): %.2f PFLOP/s" % (
+                gemm_out["mfma_ceiling"]["pflops"]))
     del codes4096, scale4096
 
     # ------------------------------------------------------------ copy context

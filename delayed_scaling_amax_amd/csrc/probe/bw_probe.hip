@@ -15,6 +15,11 @@
 //    trip of exactly the history locations the update loads, stored back unchanged.
 //    These are the floors under the update kernel: launch and dispatch alone, and the
 //    one memory round trip its in-place roll cannot avoid.
+//  * probe_mfma: the matrix cores' sustained rate on the FP8 GEMM's instruction
+//    (v_mfma_scale_f32_32x32x64_f8f6f4) with register operands only: each wavefront
+//    issues `iters` rounds of 16 independent MFMAs into 16 accumulator tiles (the GEMM's
+//    4 x 4 tile grid per wavefront), then stores one checksum per lane.  The ceiling the
+//    GEMM's data path and epilogue are measured against.
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -132,9 +137,46 @@ __global__ __launch_bounds__(kUBlock) void update_roundtrip_kernel(float* hist, 
   for (int k = 0; k < kURows; ++k) __builtin_amdgcn_raw_buffer_store_b128(v[k], r, off[k], 0, 0);
 }
 
+typedef int mfma_v8i __attribute__((ext_vector_type(8)));
+typedef float mfma_v16f __attribute__((ext_vector_type(16)));
+
+__global__ __launch_bounds__(256) void mfma_kernel(int iters, float* sink) {
+  // operands: E4M3 1.0 (0x38) in every byte, chosen at run time so that nothing folds
+  const uint32_t one = iters > 0 ? 0x38383838u : 0u;
+  const mfma_v8i a = {(int)one, (int)one, (int)one, (int)one, (int)one, (int)one, (int)one, (int)one};
+  mfma_v16f acc[16];
+#pragma unroll
+  for (int t = 0; t < 16; ++t) acc[t] = mfma_v16f{};
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int t = 0; t < 16; ++t)
+      acc[t] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, a, acc[t], 0, 0, 0, 127, 0,
+                                                               127);
+  }
+  float sum = 0.0f;
+#pragma unroll
+  for (int t = 0; t < 16; ++t) sum += acc[t][0];
+  sink[(size_t)blockIdx.x * blockDim.x + threadIdx.x] = sum;
+}
+
 }  // namespace
 
 extern "C" {
+
+// `blocks` blocks of 256 threads, each wavefront `iters` x 16 MFMAs of 32 x 32 x 64 (FP8):
+// blocks * 4 * iters * 16 * 131072 flops.  sink: device float[blocks * 256].  start/stop as
+// probe_stream.  Returns 0, -1 for an invalid argument, -3 for a launch failure.
+int probe_mfma(int blocks, int iters, float* sink, void* stream, void* start, void* stop) {
+  if (blocks <= 0 || iters <= 0 || !sink) return -1;
+  void* args[] = {&iters, &sink};
+  const void* fn = (const void*)mfma_kernel;
+  const hipError_t e =
+      start || stop
+          ? hipExtLaunchKernel(fn, dim3((unsigned)blocks), dim3(256), args, 0,
+                               (hipStream_t)stream, (hipEvent_t)start, (hipEvent_t)stop, 0)
+          : hipLaunchKernel(fn, dim3((unsigned)blocks), dim3(256), args, 0, (hipStream_t)stream);
+  return e == hipSuccess ? 0 : -3;
+}
 
 // Stream `units` 16-byte units: mode 0 reads src and writes dst (8 bytes per unit),
 // 1 reads src only, 2 writes dst only.  u in {2, 4, 8, 16} loads in flight per thread,
