@@ -348,9 +348,11 @@ int fp8_amax_and_scale_update(float* amax, float* amax_history, float* scale,
  *                             history_len, algo, margin, reset_amax, stream);
  * (same results, bit for bit) in ONE kernel launch when it fits: the quantize pass of
  * "Fusion of Fp8 quantization and amax reduction kernels" and the fused update of
- * "Implement fused kernel for FP8 scale update" share the launch, the update running in
- * the block that finishes the quantize last, after every block's amax is accumulated.
- * This removes the kernel boundary and the second launch between the two passes.
+ * "Implement fused kernel for FP8 scale update" share the launch: the history roll runs
+ * in the block that finishes its quantize work first (it needs no amax of this step),
+ * the rest of the update in the block that finishes last, after every block's amax is
+ * accumulated.  This removes the kernel boundary and the second launch between the two
+ * passes.
  * The single launch is used when 1 <= n_tensors <= 32, some tensor is non-empty,
  * 1 <= n <= 256 and history_len * n <= 65536; otherwise the call enqueues the two
  * launches above (same results).  The quantize reads each tensor's scale before the

@@ -1,11 +1,13 @@
-"""Host check of the in-place history walk the one-launch step's update uses (one block
-of 256 threads; thread t owns column t mod n and rows g, g + G, ... of each chunk with
-G = 256 // n row groups; chunks of G * 32 destination rows from the top; every load of a
-chunk before any of its stores; row 0 written last).  Replays that schedule on a numpy
-array for many (n, H) and checks that the result is the roll (row h-1 moves to row h,
-the new amax enters row 0), that no element is read after it was overwritten, and that
-the per-column maxima taken from the loaded values are the maxima over the old rows
-0 .. H-2.  No GPU and no oracle: this checks the schedule's indexing only."""
+"""Host check of the in-place history walk the one-launch step's update uses.  The roll
+runs in one block of 256 threads (thread t owns column t mod n and rows g, g + G, ... of
+each chunk with G = 256 // n row groups; chunks of G * 32 destination rows from the top;
+every load of a chunk before any of its stores) and leaves the column maxima in row 0;
+the block that finishes last then selects from row 0 and the new amax and writes the
+amax into row 0.  Replays that schedule on a numpy array for many (n, H) and checks that
+the result is the roll (row h-1 moves to row h, the new amax enters row 0), that no
+element is read after it was overwritten, and that row 0 held the maxima over the old
+rows 0 .. H-2 in between.  No GPU and no oracle: this checks the schedule's indexing
+only."""
 import numpy as np
 import pytest
 
@@ -38,8 +40,10 @@ def walk(hist: np.ndarray, amax: np.ndarray):
             hist[d, c] = v
             written[d, c] = True
         d_hi -= span
-    hist[0, :] = amax
-    return hist, colmax
+    hist[0, :] = colmax  # the rolling block's last stores
+    row0 = hist[0].copy()  # what the finishing block reads
+    hist[0, :] = amax  # the finishing block
+    return hist, row0
 
 
 @pytest.mark.parametrize("n", [1, 2, 3, 5, 7, 8, 64, 100, 255, 256])
