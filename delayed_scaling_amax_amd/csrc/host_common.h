@@ -14,6 +14,14 @@ namespace fp8q {
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // Compute units of the current device, cached per device ordinal.
+// The current device's index, for per-device caches of launch shapes: 0..63, or -1 (and
+// FP8Q_EHIP from the caller) when it cannot be read or is out of range.
+inline int current_device_index() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return -1;
+  return dev;
+}
+
 inline int current_device_cus(int* cus) {
   static std::atomic<int> cache[64];
   int dev = 0;

@@ -614,8 +614,10 @@ static int ln_launch(const LnArgs& a, hipStream_t stream) {
   constexpr int kBlk = ln_block<kV, kSplit>();
   const void* fn = (const void*)ln_quantize_kernel<kFmt, kV, kMasked, kSplit>;
   const size_t smem = (size_t)2 * 512 * kV * kSplit * sizeof(float);
-  static std::atomic<int> fit{0};
-  int per_cu = fit.load(std::memory_order_relaxed);
+  static std::atomic<int> fit[64];  // per device (the LDS attribute is set on each one)
+  const int dev = current_device_index();
+  if (dev < 0) return FP8Q_EHIP;
+  int per_cu = fit[dev].load(std::memory_order_relaxed);
   if (per_cu <= 0) {
     // gamma/beta staging beyond 64 KB (24 and 32 units per lane: 96 and 128 KB)
     if (smem > 65536 &&
@@ -626,7 +628,7 @@ static int ln_launch(const LnArgs& a, hipStream_t stream) {
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, fn, kBlk, smem) != hipSuccess)
       return FP8Q_EHIP;
     per_cu = occ < kLBlocksPerCU ? (occ > 0 ? occ : 1) : kLBlocksPerCU;
-    fit.store(per_cu, std::memory_order_relaxed);
+    fit[dev].store(per_cu, std::memory_order_relaxed);
   }
   int cus = 0;
   const int st = current_device_cus(&cus);

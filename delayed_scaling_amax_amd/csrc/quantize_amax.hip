@@ -1178,10 +1178,13 @@ static int launch_table(QTable* tab, bool upd, hipStream_t stream, hipEvent_t st
     if (st != FP8Q_OK) return st;
   }
   // The grid-stride schedule needs every block resident at once: cap the blocks per
-  // CU at what the instance's register and LDS use allow.
-  static std::atomic<int> fit[16];
+  // CU at what the instance's register and LDS use allow.  Per device: the dynamic-LDS
+  // attribute is set on each device the instance runs on.
+  static std::atomic<int> fit[64][16];
+  const int dev = current_device_index();
+  if (dev < 0) return FP8Q_EHIP;
   const int inst = src_kinds + (upd ? 8 : 0);
-  int per_cu = fit[inst].load(std::memory_order_relaxed);
+  int per_cu = fit[dev][inst].load(std::memory_order_relaxed);
   if (per_cu <= 0) {
     if (table && hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize,
                                      (int)smem) != hipSuccess)
@@ -1191,7 +1194,7 @@ static int launch_table(QTable* tab, bool upd, hipStream_t stream, hipEvent_t st
       return FP8Q_EHIP;
     const int want = src_kinds == 4 ? kQGeluBlocksPerCU : kQBlocksPerCU;
     per_cu = occ < want ? (occ > 0 ? occ : 1) : want;
-    fit[inst].store(per_cu, std::memory_order_relaxed);
+    fit[dev][inst].store(per_cu, std::memory_order_relaxed);
   }
   const int64_t max_blocks = (int64_t)cus * per_cu;
   int64_t blocks = tab->total_full > tab->n ? tab->total_full : tab->n;
@@ -1372,14 +1375,16 @@ static int launch_planned(const PlanRec& rec, hipStream_t stream) {
   const void* fn = rec.src_kinds == 1   ? (const void*)quantize_amax_planned_kernel<1>
                    : rec.src_kinds == 2 ? (const void*)quantize_amax_planned_kernel<2>
                                         : (const void*)quantize_amax_planned_kernel<3>;
-  static std::atomic<int> fit[4];
-  int per_cu = fit[rec.src_kinds & 3].load(std::memory_order_relaxed);
+  static std::atomic<int> fit[64][4];
+  const int dev = current_device_index();
+  if (dev < 0) return FP8Q_EHIP;
+  int per_cu = fit[dev][rec.src_kinds & 3].load(std::memory_order_relaxed);
   if (per_cu <= 0) {
     int occ = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, fn, kQBlock, 0) != hipSuccess)
       return FP8Q_EHIP;
     per_cu = occ < kQPlanBlocksPerCU ? (occ > 0 ? occ : 1) : kQPlanBlocksPerCU;
-    fit[rec.src_kinds & 3].store(per_cu, std::memory_order_relaxed);
+    fit[dev][rec.src_kinds & 3].store(per_cu, std::memory_order_relaxed);
   }
   const int64_t max_blocks = (int64_t)cus * per_cu;
   int64_t blocks = rec.total_full > rec.n ? rec.total_full : rec.n;
