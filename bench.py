@@ -331,10 +331,11 @@ def probe_lib():
     return lib
 
 
-def mfma_ceiling(plib, dev, cus, iters=2000, reps=5):
+def mfma_ceiling(plib, dev, cus, iters=2000, reps=12):
     """The FP8 matrix cores' sustained rate with register operands only (probe_mfma: one
     block of 4 wavefronts per CU, each wavefront iters x 16 independent 32x32x64 MFMAs),
-    the best of `reps` launches timed with events taken by the kernel's own dispatch."""
+    the best of `reps` launches (~0.9 ms each, back to back: the clock settles over the
+    first few) timed with events taken by the kernel's own dispatch."""
     torch = __import__("torch")
     sink = torch.empty(cus * 256, dtype=torch.float32, device=dev)
     flops = float(cus) * 4 * iters * 16 * 2 * 32 * 32 * 64
