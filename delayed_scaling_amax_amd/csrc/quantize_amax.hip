@@ -71,9 +71,11 @@ constexpr int kQBlocksPerCU = FP8Q_Q_BLOCKS_PER_CU;  // persistent grid size per
 #ifndef FP8Q_Q_GELU_BLOCKS_PER_CU
 #define FP8Q_Q_GELU_BLOCKS_PER_CU 6
 #endif
-// the gelu instance is arithmetic-bound: more resident waves hide exp/rcp latency (on
-// 8192 x 16384 bf16 with the direct form: 6 blocks per CU 75-80 us, 5 76-80, 4 79-86, 3
-// 79-89; its 79 registers leave room for six)
+// the evaluated gelu instance (FP8Q_Q_GELU_TABLE 0) is arithmetic-bound: more resident
+// waves hide exp/rcp latency (on 8192 x 16384 bf16 with the direct form: 6 blocks per CU
+// 75-80 us, 5 76-80, 4 79-86, 3 79-89; its 79 registers leave room for six).  With the
+// table its 128 KB of LDS leave room for one block per CU, which the occupancy query at
+// launch applies.
 constexpr int kQGeluBlocksPerCU = FP8Q_Q_GELU_BLOCKS_PER_CU;
 constexpr int kQChunk = kQBlock * kQUnroll;       // units (8-element groups) per chunk
 #ifndef FP8Q_Q_DEPTH
