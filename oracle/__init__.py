@@ -112,22 +112,26 @@ class Oracle:
         dst = np.empty(n, np.uint8) if out is None else out.reshape(-1)
         threads = max(1, min(int(threads), max(1, n // (1 << 16))))
         bounds = [n * k // threads for k in range(threads + 1)]
-        amaxes = np.zeros(threads, np.float32)
+        # amax travels as its bit pattern: a float32 -> Python float conversion would
+        # quiet a signaling NaN and so raise its magnitude bits above the true maximum.
+        a_in = np.asarray(amax_in, np.float32).reshape(1).view(np.uint32)
+        amaxes = np.zeros(threads, np.uint32)
 
         def run(k):
             lo, hi = bounds[k], bounds[k + 1]
-            a = ctypes.c_float(amax_in)      # every chunk max-accumulates into amax_in
+            a = a_in.copy()                  # every chunk max-accumulates into amax_in
             self.lib.oracle_quantize_amax(flat[lo:].ctypes.data if hi > lo else None, dt,
                                           dst[lo:].ctypes.data if hi > lo else None,
-                                          hi - lo, fmt, float(scale), ctypes.byref(a))
-            amaxes[k] = a.value
+                                          hi - lo, fmt, float(scale),
+                                          a.ctypes.data_as(ctypes.POINTER(ctypes.c_float)))
+            amaxes[k] = a[0]
 
         if threads == 1:
             run(0)
         else:
             with ThreadPoolExecutor(threads) as ex:
                 list(ex.map(run, range(threads)))
-        return dst.reshape(x.shape), np.uint32(amaxes.view(np.uint32).max()).view(np.float32)
+        return dst.reshape(x.shape), amaxes.max().view(np.float32)
 
     def amax_and_scale_update(self, amax, hist, scale, formats, algo=AMAX_MAX, margin=0,
                               reset_amax=False):

@@ -358,8 +358,8 @@ def pin_amax(o):
     _, a = o.quantize_amax(y, E4M3, 1.0)
     assert np.isnan(a)
     # the NaN payload (R5: the largest sign-cleared bit pattern): among NaNs of both signs
-    # the largest payload wins, and any NaN beats inf; quiet NaNs, so no conversion on
-    # the way can change them; bf16 sources count by their binary32 upcast
+    # the largest payload wins, and any NaN beats inf; bf16 sources count by their
+    # binary32 upcast
     zb = np.concatenate([np.array([1.0, -np.inf, 3.0, 0.0], np.float32).view(np.uint32),
                          np.array([0xFFE12345, 0x7FC00001, 0xFFC00100], np.uint32)])
     _, a = o.quantize_amax(zb.view(np.float32), E4M3, 1.0)
@@ -367,6 +367,19 @@ def pin_amax(o):
     hb = np.array([0x3F80, 0xFFE1, 0x7FC3, 0xFF80], np.uint16)  # 1, -NaN, +NaN, -inf
     _, a = o.quantize_amax(hb, E5M2, 1.0)
     assert np.float32(a).view(np.uint32) == 0x7FE10000
+    # signaling NaNs count by their own bits, never quieted: a quieted 0x7F81F558 would
+    # read 0x7FC1F558 and beat the quiet 0x7FC1EA99 that is the true bit maximum; the
+    # incoming amax keeps its bits the same way
+    sn = np.array([0x3F800000, 0xFF81F558, 0x7FC1EA99], np.uint32)
+    _, a = o.quantize_amax(sn.view(np.float32), E4M3, 1.0, threads=1)
+    assert np.float32(a).view(np.uint32) == 0x7FC1EA99
+    _, a = o.quantize_amax(sn[:2].view(np.float32), E4M3, 1.0)
+    assert np.float32(a).view(np.uint32) == 0x7F81F558
+    _, a = o.quantize_amax(sn[:1].view(np.float32), E4M3, 1.0,
+                           amax_in=np.uint32(0x7F80ABCD).view(np.float32))
+    assert np.float32(a).view(np.uint32) == 0x7F80ABCD
+    _, a = o.quantize_amax(np.array([0x3F80, 0xFF81, 0x7F80], np.uint16), E5M2, 1.0)
+    assert np.float32(a).view(np.uint32) == 0x7F810000
 
 
 def pin_saturation_count(o):

@@ -62,7 +62,7 @@ def _oracle(orc, items, scales, slot_of):
     amax = np.zeros(n_slots, np.float32)
     codes = []
     for i, (x, off, fmt) in enumerate(items):
-        c, a = orc.quantize_amax(x, fmt, float(scales[i]), amax_in=float(amax[slot_of[i]]),
+        c, a = orc.quantize_amax(x, fmt, float(scales[i]), amax_in=amax[slot_of[i]],
                                  threads=8)
         amax[slot_of[i]] = a
         codes.append(c.reshape(-1))

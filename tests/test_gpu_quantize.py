@@ -144,7 +144,7 @@ def test_multi_tensor_mixed_and_shared_amax(orc):
     sc = scales.cpu().numpy()
     want_amax = np.zeros(20, np.float32)
     for i, (x, fmt, slot, dst) in enumerate(host):
-        want, wa = orc.quantize_amax(x, fmt, float(sc[i]), amax_in=float(want_amax[slot]))
+        want, wa = orc.quantize_amax(x, fmt, float(sc[i]), amax_in=want_amax[slot])
         want_amax[slot] = wa
         assert dst.cpu().numpy().tobytes() == want.tobytes(), i
     assert (bits(amax.cpu().numpy()) == bits(want_amax)).all()
@@ -197,7 +197,7 @@ def test_amax_max_accumulates_and_is_deterministic(orc):
         torch.cuda.synchronize()
         outs.append((o1.cpu().numpy(), o2.cpu().numpy(), a.cpu().numpy()[0]))
     _, a1 = orc.quantize_amax(x1, E4M3, 0.01)
-    _, a12 = orc.quantize_amax(x2, E4M3, 0.01, amax_in=float(a1))
+    _, a12 = orc.quantize_amax(x2, E4M3, 0.01, amax_in=a1)
     assert bits(outs[0][2]) == bits(a12)
     for k in range(3):
         assert np.array_equal(np.atleast_1d(outs[0][k]).view(np.uint8),

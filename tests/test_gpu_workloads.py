@@ -143,9 +143,9 @@ def test_microbatch_accumulation_once_per_step(orc):
                                        (srcs[m][1], qg, scale[1:2], amax[1:2], 1)])
             torch.cuda.synchronize()
             wa, o_amax[0] = orc.quantize_amax(acts[m], 0, float(o_scale[0]),
-                                              amax_in=float(o_amax[0]))
+                                              amax_in=o_amax[0])
             wg, o_amax[1] = orc.quantize_amax(grads[m], 1, float(o_scale[1]),
-                                              amax_in=float(o_amax[1]))
+                                              amax_in=o_amax[1])
             assert qa.cpu().numpy().tobytes() == wa.tobytes()
             assert qg.cpu().numpy().tobytes() == wg.tobytes()
         assert (bits(amax.cpu().numpy()) == bits(o_amax)).all()
