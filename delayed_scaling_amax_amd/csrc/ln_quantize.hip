@@ -182,6 +182,45 @@ struct LnQuant {
   bool gb_fin;    // every staged gamma and beta is finite
 };
 
+// y rounded to bf16 (nearest even), returned as the binary32 of the same value: the
+// packed convert puts RN_bf16(y) in the high half and RN_bf16(0) = 0 in the low one.
+__device__ __forceinline__ float round_bf16(float y) {
+  return as_float(pack_bf16_rne(0.0f, y));
+}
+
+// max(|v0|, ..., |v7|) of non-NaN values: four max3 with |.| source modifiers.
+__device__ __forceinline__ float max3_abs(float a, float b, float c) {
+  float m;
+  __asm__("v_max3_f32 %0, |%1|, |%2|, |%3|" : "=v"(m) : "v"(a), "v"(b), "v"(c));
+  return m;
+}
+__device__ __forceinline__ float max8_abs(const float (&v)[8]) {
+  float m = max3_abs(v[0], v[1], v[2]);
+  m = max3_abs(m, v[3], v[4]);
+  m = max3_abs(m, v[5], v[6]);
+  return max3_abs(m, v[7], v[7]);
+}
+
+// The codes of 8 bf16-valued binary32 y (the corrected division, saturated or, where
+// the caller has checked that no quotient can exceed FP8_MAX, not), as codes8_bf16 and
+// codes8_bf16_unsaturated give them for the packed values.
+template <int kFmt, bool kSat>
+__device__ __forceinline__ uint2 codes8_vals(const float (&x)[8], float s, float r) {
+  float c[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const float qk = div_corrected1(x[k], s, r);
+    c[k] = kSat ? saturate<kFmt>(qk) : qk;
+  }
+  return make_uint2(pack4<kFmt>(c[0], c[1], c[2], c[3]), pack4<kFmt>(c[4], c[5], c[6], c[7]));
+}
+
+// 8 bf16-valued binary32 back to packed bf16 (exact).
+__device__ __forceinline__ uint4 pack8_bf16(const float (&v)[8]) {
+  return make_uint4(pack_bf16_rne(v[0], v[1]), pack_bf16_rne(v[2], v[3]),
+                    pack_bf16_rne(v[4], v[5]), pack_bf16_rne(v[6], v[7]));
+}
+
 // Make the packed row opaque to the compiler between passes (an empty asm that
 // rebinds the registers, emitting nothing): values derived from it are recomputed
 // rather than merged with, and kept live from, an earlier pass.
@@ -379,89 +418,125 @@ __device__ __forceinline__ void ln_row(uint4 (&w)[kV], const LnArgs& a, int64_t 
   constexpr int kPlane = 64 * kV * kSplit;  // units, i.e. float4s per plane
   const float4* g4 = (const float4*)lg;
   const float4* b4 = (const float4*)lb;
-  float4 gb_next[4];
-  if constexpr (FP8Q_LN_GB_PREFETCH) {
-    const int u0 = ubase + lane;
-    gb_next[0] = g4[u0];
-    gb_next[1] = g4[kPlane + u0];
-    gb_next[2] = b4[u0];
-    gb_next[3] = b4[kPlane + u0];
-  }
-#pragma unroll
-  for (int k = 0; k < kV; ++k) {
-    const int unit = ubase + lane + 64 * k;
-    float4 g0, g1, b0, b1;
+  // Two forms of a unit's rounding, amax and codes, chosen per row by a scalar branch:
+  // rows that give no NaN (row_fin) with the scale inside the division window round each
+  // y to a bf16-valued binary32 in one instruction and take the magnitude max as a float
+  // max3 with |.| modifiers, which for non-NaN values orders exactly as the bit patterns
+  // do; other rows keep y packed, canonicalize NaNs and take the packed 16-bit magnitude
+  // max.  Both give the same codes and amax.  The branch is per unit, after y: with a
+  // whole unit loop per form the compiler hoists the y arithmetic the two loops share
+  // above the branch, and the 8-unit instances spill.  Measured against the packed form
+  // alone (us, medians of 5 x 20 launches, one box): 8192 x 4096 25.7 -> 25.0,
+  // 8192 x 4000 25.4 -> 24.6, 16384 x 2048 24.8 -> 23.9, 8192 x 8192 54.6 -> 52.2,
+  // 4096 x 16384 53.7 -> 54.1; 8 fewer VALU instructions per unit of 8 elements.
+  uint32_t fast = uniform((uint32_t)(row_fin && q.win));
+  // held in an SGPR (otherwise the compiler re-derives it, through a VGPR and a
+  // readfirstlane, at every unit's branch)
+  __asm__ volatile("" : "+s"(fast));
+  {
+    uint32_t acc32 = 0;  // fast rows: max |y| as binary32 bits (low 16 bits zero)
+    float4 gb_next[4];
     if constexpr (FP8Q_LN_GB_PREFETCH) {
-      // this unit's values were read during the previous unit; read the next unit's now
-      g0 = gb_next[0];
-      g1 = gb_next[1];
-      b0 = gb_next[2];
-      b1 = gb_next[3];
-      if (k + 1 < kV) {
-        gb_next[0] = g4[unit + 64];
-        gb_next[1] = g4[kPlane + unit + 64];
-        gb_next[2] = b4[unit + 64];
-        gb_next[3] = b4[kPlane + unit + 64];
+      const int u0 = ubase + lane;
+      gb_next[0] = g4[u0];
+      gb_next[1] = g4[kPlane + u0];
+      gb_next[2] = b4[u0];
+      gb_next[3] = b4[kPlane + u0];
+    }
+#pragma unroll
+    for (int k = 0; k < kV; ++k) {
+      const int unit = ubase + lane + 64 * k;
+      float4 g0, g1, b0, b1;
+      if constexpr (FP8Q_LN_GB_PREFETCH) {
+        // this unit's values were read during the previous unit; read the next unit's now
+        g0 = gb_next[0];
+        g1 = gb_next[1];
+        b0 = gb_next[2];
+        b1 = gb_next[3];
+        if (k + 1 < kV) {
+          gb_next[0] = g4[unit + 64];
+          gb_next[1] = g4[kPlane + unit + 64];
+          gb_next[2] = b4[unit + 64];
+          gb_next[3] = b4[kPlane + unit + 64];
+        }
+      } else {
+        g0 = g4[unit];
+        g1 = g4[kPlane + unit];
+        b0 = b4[unit];
+        b1 = b4[kPlane + unit];
       }
-    } else {
-      g0 = g4[unit];
-      g1 = g4[kPlane + unit];
-      b0 = b4[unit];
-      b1 = b4[kPlane + unit];
-    }
-    const float gv[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
-    const float bv[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
-    float y[8];
-    if constexpr (kKeep) {
+      const float gv[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+      const float bv[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+      float y[8];
+      if constexpr (kKeep) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) y[j] = __builtin_fmaf(xs[k][j] - e, gv[j] * rstd, bv[j]);
-    } else {
-      float x[8];
-      unpack8(w[k], x);
+        for (int j = 0; j < 8; ++j) y[j] = __builtin_fmaf(xs[k][j] - e, gv[j] * rstd, bv[j]);
+      } else {
+        float x[8];
+        unpack8(w[k], x);
 #pragma unroll
-      for (int j = 0; j < 8; ++j) y[j] = __builtin_fmaf((x[j] - mu) - e, gv[j] * rstd, bv[j]);
-    }
-    uint4 yw = make_uint4(pack_bf16_rne(y[0], y[1]), pack_bf16_rne(y[2], y[3]),
-                          pack_bf16_rne(y[4], y[5]), pack_bf16_rne(y[6], y[7]));
-    uint32_t mg = mag8_bf16(yw);
-    if (!row_fin && __builtin_amdgcn_ballot_w64(halves_nan(mg) != 0) != 0) {  // rare: NaN rows
-      uint32_t o[4] = {yw.x, yw.y, yw.z, yw.w};
-#pragma unroll
-      for (int h = 0; h < 4; ++h) {
-        const uint32_t l = (o[h] & 0x7FFFu) > 0x7F80u ? 0x7FC0u : (o[h] & 0xFFFFu);
-        const uint32_t u = ((o[h] >> 16) & 0x7FFFu) > 0x7F80u ? 0x7FC0u : (o[h] >> 16);
-        o[h] = l | (u << 16);
+        for (int j = 0; j < 8; ++j) y[j] = __builtin_fmaf((x[j] - mu) - e, gv[j] * rstd, bv[j]);
       }
-      yw = make_uint4(o[0], o[1], o[2], o[3]);
-      mg = mag8_bf16(yw);
-    }
-    const bool valid = row_ok && (!kMasked || unit < a.nunits);
-    acc = pk_max_u16(acc, valid ? mg : 0u);
-    uint2 c;
-    if (q.win) {
-      // no saturation step where no quotient of the unit (across the wavefront) can
-      // exceed FP8_MAX
-      if (__builtin_amdgcn_ballot_w64(max_halves(mg) > q.clim) == 0)
-        c = codes8_bf16_unsaturated<kFmt>(yw, q.s, q.r);
-      else
-        c = codes8_bf16<kFmt>(yw, q.s, q.r);
-      if (max_halves(mg) >= q.xlim) c = patch8_bf16<kFmt>(c, yw, q.xlim);
-    } else {  // scale outside the corrected-division window: IEEE divide per element
-      const uint32_t u[4] = {yw.x, yw.y, yw.z, yw.w};
-      uint32_t cw[2] = {0, 0};
+      const bool valid = row_ok && (!kMasked || unit < a.nunits);
+      uint2 c;
+      // a fresh scalar compare per unit: a compare shared by all units crosses blocks as
+      // a lane mask, rebuilt with two VALU instructions at each branch
+      uint32_t fast_u = fast;
+      __asm__ volatile("" : "+s"(fast_u));
+      if (fast_u) {
+        float yb[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const float v = (j & 1) ? hi_f32(u[j >> 1]) : lo_f32(u[j >> 1]);
-        cw[j >> 2] |= code_ieee<kFmt>(v, q.s) << (8 * (j & 3));
+        for (int j = 0; j < 8; ++j) yb[j] = round_bf16(y[j]);
+        const uint32_t mb = as_uint(max8_abs(yb));
+        acc32 = max(acc32, valid ? mb : 0u);
+        // no saturation step where no quotient of the unit (across the wavefront) can
+        // exceed FP8_MAX
+        if (__builtin_amdgcn_ballot_w64(mb > q.clim << 16) == 0)
+          c = codes8_vals<kFmt, false>(yb, q.s, q.r);
+        else
+          c = codes8_vals<kFmt, true>(yb, q.s, q.r);
+        if (mb >= q.xlim << 16) c = patch8_bf16<kFmt>(c, pack8_bf16(yb), q.xlim);
+      } else {
+        uint4 yw = make_uint4(pack_bf16_rne(y[0], y[1]), pack_bf16_rne(y[2], y[3]),
+                              pack_bf16_rne(y[4], y[5]), pack_bf16_rne(y[6], y[7]));
+        uint32_t mg = mag8_bf16(yw);
+        if (__builtin_amdgcn_ballot_w64(halves_nan(mg) != 0) != 0) {  // NaNs in the unit
+          uint32_t o[4] = {yw.x, yw.y, yw.z, yw.w};
+#pragma unroll
+          for (int h = 0; h < 4; ++h) {
+            const uint32_t l = (o[h] & 0x7FFFu) > 0x7F80u ? 0x7FC0u : (o[h] & 0xFFFFu);
+            const uint32_t u = ((o[h] >> 16) & 0x7FFFu) > 0x7F80u ? 0x7FC0u : (o[h] >> 16);
+            o[h] = l | (u << 16);
+          }
+          yw = make_uint4(o[0], o[1], o[2], o[3]);
+          mg = mag8_bf16(yw);
+        }
+        acc = pk_max_u16(acc, valid ? mg : 0u);
+        if (q.win) {
+          if (__builtin_amdgcn_ballot_w64(max_halves(mg) > q.clim) == 0)
+            c = codes8_bf16_unsaturated<kFmt>(yw, q.s, q.r);
+          else
+            c = codes8_bf16<kFmt>(yw, q.s, q.r);
+          if (max_halves(mg) >= q.xlim) c = patch8_bf16<kFmt>(c, yw, q.xlim);
+        } else {
+          const uint32_t u[4] = {yw.x, yw.y, yw.z, yw.w};
+          uint32_t cw[2] = {0, 0};
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const float v = (j & 1) ? hi_f32(u[j >> 1]) : lo_f32(u[j >> 1]);
+            cw[j >> 2] |= code_ieee<kFmt>(v, q.s) << (8 * (j & 3));
+          }
+          c = make_uint2(cw[0], cw[1]);
+        }
       }
-      c = make_uint2(cw[0], cw[1]);
-    }
-    __builtin_amdgcn_raw_buffer_store_b64(ln_u32x2{c.x, c.y}, out, (uint32_t)unit * 8u, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b64(ln_u32x2{c.x, c.y}, out, (uint32_t)unit * 8u, 0, 0);
 #if FP8Q_LN_UNIT_BARRIER
-    // keep each unit's work (LDS reads, arithmetic) from being hoisted into the
-    // previous one's, which would hold every unit's temporaries at once
-    __builtin_amdgcn_sched_barrier(0);
+      // keep each unit's work (LDS reads, arithmetic) from being hoisted into the
+      // previous one's, which would hold every unit's temporaries at once
+      __builtin_amdgcn_sched_barrier(0);
 #endif
+    }
+    acc = pk_max_u16(acc, acc32 >> 16);
   }
 }
 

@@ -168,6 +168,22 @@ def test_ln_nonfinite_beta_and_huge_gamma(orc, H):
     check_ln(orc, x, E5M2, 1.0, g2, beta)
 
 
+@pytest.mark.parametrize("H", [1000, 4096, 8192])
+def test_ln_saturating_scales(orc, H):
+    """Scales inside the division window at which most units hold quotients beyond
+    FP8_MAX (the saturating form of the codes) in rows that give no NaN, and a column of
+    gamma 3e38 whose y overflows to +-inf there (the fixed-code patch in the same rows)."""
+    x = ln_input(760 + H, 12, H, offset=0.1)
+    gamma, beta = affine(761 + H, H)
+    for fmt, scale in ((E4M3, 1 / 512), (E5M2, 2.0 ** -15)):
+        note("ln H=%d saturating scale %r fmt %d" % (H, scale, fmt))
+        check_ln(orc, x, fmt, scale, gamma, beta)
+    g2 = gamma.copy()
+    g2[H // 2] = np.float32(3e38)
+    note("ln H=%d saturating scale with an overflowing column" % H)
+    check_ln(orc, x, E4M3, 1 / 512, g2, beta)
+
+
 @pytest.mark.parametrize("scale", [2.0 ** -100, 0.0, float("inf"), float("nan"), -0.5, 3e38])
 def test_ln_odd_scales(orc, scale):
     x = ln_input(730, 24, 768)
