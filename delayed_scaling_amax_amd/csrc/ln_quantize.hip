@@ -316,6 +316,14 @@ constexpr bool ln_keep() { return kSplit == 1 && kV <= 8; }
 #ifndef FP8Q_LN_PREFETCH
 #define FP8Q_LN_PREFETCH 1
 #endif
+// The wavefront's first row loaded during the gamma/beta staging: 1 for the kept-row
+// instances, 2 for all, 0 for none.  Measured (us, medians; none / kept / all): 8192 x
+// 4096 24.6 / 24.5 / 24.4, 16384 x 2048 24.0 / 23.4 / 23.4, 8192 x 8192 50.9 / 50.9 /
+// 53.2, 4096 x 16384 54.3 / 54.1 / 55.8 (the instances that hold a row per wavefront
+// without keeping it lose when its registers are live through the staging).
+#ifndef FP8Q_LN_EARLY_ROW
+#define FP8Q_LN_EARLY_ROW 1
+#endif
 #ifndef FP8Q_LN_KEEP8_WAVES
 #define FP8Q_LN_KEEP8_WAVES 3
 #endif
@@ -540,6 +548,17 @@ __device__ __forceinline__ void ln_row(uint4 (&w)[kV], const LnArgs& a, int64_t 
   }
 }
 
+// The resource of row r's part `half` (units from 64 kV half on) in split blocks: the
+// part's bytes of the row, empty for a padding row past the end.
+template <int kV, int kSplit>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t ln_split_rsrc(const LnArgs& a, int64_t r,
+                                                               int half, uint32_t row_bytes) {
+  // this half's units start 64 kV units (1024 kV bytes) into the row
+  return r < a.rows ? ln_rsrc(a.x + r * a.H + 512 * kV * half,
+                              row_bytes > 1024u * kV * half ? row_bytes - 1024u * kV * half : 0u)
+                    : ln_rsrc(a.x, 0u);
+}
+
 // Rows kept unpacked (ln_keep) are held to the register count at which kLBlocksPerCU
 // blocks of 4 wavefronts fit each CU (one wavefront of each block per SIMD).
 template <int kV, int kSplit>
@@ -568,29 +587,54 @@ void ln_quantize_kernel(const LnArgs a) {
   const int64_t nwaves = (int64_t)gridDim.x * (kBlk / 64);
   int64_t row = (int64_t)blockIdx.x * (kBlk / 64) + wave;  // (kSplit == 1)
   const uint32_t row_bytes = (uint32_t)a.H * 2u;
-  // stage gamma/beta: 16-byte loads, all issued before any is used
+  // The wavefront's first row (or row part) is loaded while gamma/beta are staged:
+  // issued after the gamma/beta loads, so the staging waits for those alone.
+  uint4 w[kV];
+  constexpr bool kEarly = FP8Q_LN_EARLY_ROW == 2 || (FP8Q_LN_EARLY_ROW == 1 && ln_keep<kV, kSplit>());
+  const auto load_first = [&]() {
+    if constexpr (!kEarly) {
+    } else if constexpr (kSplit == 1) {
+      ln_load_row<kV>(w, row < a.rows ? ln_rsrc(a.x + row * a.H, row_bytes) : ln_rsrc(a.x, 0u),
+                      lane);
+    } else {
+      const int64_t r = (int64_t)blockIdx.x * ln_rows_per_block<kV, kSplit>() + wave / kSplit;
+      ln_load_row<kV>(w, ln_split_rsrc<kV, kSplit>(a, r, wave % kSplit, row_bytes), lane);
+    }
+  };
+  // stage gamma/beta: 16-byte loads, all issued before any is used.  Unconditional
+  // buffer loads whose resources cover exactly gamma and beta (none for an absent one):
+  // the pieces past H, and a missing gamma or beta, read zeros (a load under a branch
+  // whose other side fills the same registers waits for the load before the next is
+  // issued, one round trip per piece).
   if (a.vec_affine) {
     float4 gs[kPad / 4 / kBlk > 0 ? kPad / 4 / kBlk : 1];
     float4 bs[kPad / 4 / kBlk > 0 ? kPad / 4 / kBlk : 1];
     constexpr int kIt = (kPad / 4 + kBlk - 1) / kBlk;
+    const __amdgpu_buffer_rsrc_t rg = ln_rsrc(a.gamma, a.gamma ? (uint32_t)a.H * 4u : 0u);
+    const __amdgpu_buffer_rsrc_t rb = ln_rsrc(a.beta, a.beta ? (uint32_t)a.H * 4u : 0u);
 #pragma unroll
     for (int it = 0; it < kIt; ++it) {
-      const int i4 = threadIdx.x + it * kBlk;  // float4 index
-      const bool in = 4 * i4 < a.H;
-      gs[it] = in && a.gamma ? ((const float4*)a.gamma)[i4] : make_float4(1.f, 1.f, 1.f, 1.f);
-      bs[it] = in && a.beta ? ((const float4*)a.beta)[i4] : make_float4(0.f, 0.f, 0.f, 0.f);
-      if (!in) gs[it] = make_float4(0.f, 0.f, 0.f, 0.f);
+      const uint32_t off = (uint32_t)(threadIdx.x + it * kBlk) * 16u;  // float4 index * 16
+      gs[it] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rg, off, 0, 0));
+      bs[it] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rb, off, 0, 0));
     }
+    load_first();
 #pragma unroll
     for (int it = 0; it < kIt; ++it) {
       const int i4 = threadIdx.x + it * kBlk;
       if (4 * i4 < kPad) {
         const int p4 = (i4 & 1) * (kPad / 8) + (i4 >> 1);  // plane, unit
-        ((float4*)lg)[p4] = gs[it];
+        float4 g = gs[it];
+        if (!a.gamma) {  // gamma 1 inside the row, 0 in the padding
+          const float one = 4 * i4 < a.H ? 1.0f : 0.0f;
+          g = make_float4(one, one, one, one);
+        }
+        ((float4*)lg)[p4] = g;
         ((float4*)lb)[p4] = bs[it];
       }
     }
   } else {
+    load_first();
     for (int i = threadIdx.x; i < kPad; i += kBlk) {
       const bool in = i < a.H;
       const int p = ((i >> 2) & 1) * (kPad / 2) + (i >> 3) * 4 + (i & 3);  // plane, unit, column
@@ -634,11 +678,12 @@ void ln_quantize_kernel(const LnArgs a) {
 
   uint32_t acc = 0;
   if constexpr (kSplit == 1) {
-    uint4 w[kV];
     if constexpr (ln_keep<kV, kSplit>() && FP8Q_LN_PREFETCH) {
       // the next row is loaded inside ln_row, after the current row's first pass (a
       // row past the end has an empty resource and reads zeros)
-      if (row < a.rows) ln_load_row<kV>(w, ln_rsrc(a.x + row * a.H, row_bytes), lane);
+      if constexpr (!kEarly) {
+        if (row < a.rows) ln_load_row<kV>(w, ln_rsrc(a.x + row * a.H, row_bytes), lane);
+      }
       for (; row < a.rows; row += nwaves) {
         const int64_t nx = row + nwaves;
         const __amdgpu_buffer_rsrc_t nrs =
@@ -647,8 +692,8 @@ void ln_quantize_kernel(const LnArgs a) {
       }
     } else {
       // one row at a time: latency is hidden by the other resident wavefronts
-      for (; row < a.rows; row += nwaves) {
-        ln_load_row<kV>(w, ln_rsrc(a.x + row * a.H, row_bytes), lane);
+      for (bool first = true; row < a.rows; row += nwaves, first = false) {
+        if (!first || !kEarly) ln_load_row<kV>(w, ln_rsrc(a.x + row * a.H, row_bytes), lane);
         ln_row<kFmt, kV, kMasked, 1>(w, a, row, true, lane, 0, nullptr, lg, lb, q, acc,
                                      ln_rsrc(a.x, 0u));
       }
@@ -660,17 +705,12 @@ void ln_quantize_kernel(const LnArgs a) {
     constexpr int kRows = ln_rows_per_block<kV, kSplit>();
     const int slot = wave / kSplit, half = wave % kSplit;
     float* xch = xch_all + 3 * kSplit * slot;
+    bool first = true;
     for (int64_t base = (int64_t)blockIdx.x * kRows; base < a.rows;
-         base += (int64_t)gridDim.x * kRows) {
+         base += (int64_t)gridDim.x * kRows, first = false) {
       const int64_t r = base + slot;
       const bool ok = r < a.rows;
-      uint4 w[kV];
-      // this half's units start 64 kV units (1024 kV bytes) into the row
-      const __amdgpu_buffer_rsrc_t rs =
-          ok ? ln_rsrc(a.x + r * a.H + 512 * kV * half,
-                       row_bytes > 1024u * kV * half ? row_bytes - 1024u * kV * half : 0u)
-             : ln_rsrc(a.x, 0u);
-      ln_load_row<kV>(w, rs, lane);
+      if (!first || !kEarly) ln_load_row<kV>(w, ln_split_rsrc<kV, kSplit>(a, r, half, row_bytes), lane);
       ln_row<kFmt, kV, kMasked, kSplit>(w, a, r, ok, lane, half, xch, lg, lb, q, acc,
                                         ln_rsrc(a.x, 0u));
     }
