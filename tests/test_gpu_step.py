@@ -53,7 +53,7 @@ class Step:
         codes = []
         for i, x in enumerate(self.xs):
             c, a = orc.quantize_amax(x, self.fmts[i], float(self.o_scale[i]),
-                                     float(self.o_amax[i]), threads=8)
+                                     self.o_amax[i], threads=8)
             codes.append(c)
             self.o_amax[i] = a
         r = orc.amax_and_scale_update(self.o_amax, self.o_hist, self.o_scale, self.o_fmt,
