@@ -124,6 +124,14 @@ constexpr int kQPlanDepth = FP8Q_Q_PLAN_DEPTH;
 #endif
 constexpr int kQPlanBlocksPerCU = FP8Q_Q_PLAN_BLOCKS_PER_CU;
 constexpr int kQPass = FP8Q_Q_PASS;    // bf16 groups per pass (fp32: half)
+// The gelu instance (table in LDS, one block per CU) converts whole chunks as one pass of
+// 8 groups: more bytes in flight per wavefront against the LDS gathers' latency.  On the
+// (2048,4,16384) pre-activation (us, best of 3 x 20 launches, 4 rounds): passes of 2
+// groups 83.8-85.2, 4 69.2-72.8, 8 65.0-68.3, 8 with two passes ahead 65.7-68.9.
+#ifndef FP8Q_Q_GELU_PASS
+#define FP8Q_Q_GELU_PASS 8
+#endif
+constexpr int kQGeluPass = FP8Q_Q_GELU_PASS;  // groups per pass, gelu instance
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -539,7 +547,7 @@ __device__ __forceinline__ void run_full_chunks(const Tab& tab, Sh& sh, int t_be
                                                 int t_end, bool setup) {
   constexpr int kD = Tab::kPlanned ? kQPlanDepth : kQDepth;  // passes in flight ahead
   constexpr int kL = kBF16 ? 1 : 2;                // 16-byte loads per group
-  constexpr int kU = kBF16 ? kQPass : kQPass / 2;  // groups per pass
+  constexpr int kU = kGelu ? kQGeluPass : kBF16 ? kQPass : kQPass / 2;  // groups per pass
   constexpr int kP = kQUnroll / kU;                // passes per chunk
   static_assert(kQUnroll % kU == 0, "a chunk is a whole number of passes");
   constexpr int esz = kBF16 ? 2 : 4;
