@@ -28,8 +28,10 @@
 //  * Rows with inf/NaN inputs (or V + eps = 0) produce NaN, written as the positive
 //    default NaN 0x7FC0; its code is 0x7F.
 //  * The quantize of y' is the shared element math (corrected division by the scale,
-//    saturate, native OCP convert, fixed codes for huge quotients); the amax is the
-//    packed bf16 magnitude max -> wavefront -> LDS -> one global atomic per block.
+//    saturate, native OCP convert, fixed codes for huge quotients).  The amax goes
+//    lane max -> wavefront -> LDS -> one global atomic per block.  Rows that give no
+//    NaN take the lane max as a float max3 of |y|; other rows take the packed bf16
+//    magnitude max.
 #include "device_common.h"
 #include "host_common.h"
 #include "quant_math.h"
