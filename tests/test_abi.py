@@ -294,3 +294,18 @@ def test_noalloc_refuses_before_enqueue():
     big[0].format = 5
     assert N(big, 2, None) == d.EINVAL
     assert N(None, 3, None) == d.EINVAL
+
+
+def test_import_fails_loudly_without_the_library(tmp_path):
+    """The package has no fallback: a copy of it without libfp8q.so refuses to import."""
+    import shutil
+    import sys
+    import delayed_scaling_amax_amd as d
+    pkg = tmp_path / "delayed_scaling_amax_amd"
+    pkg.mkdir()
+    shutil.copy(os.path.join(os.path.dirname(d.__file__), "__init__.py"), pkg / "__init__.py")
+    out = subprocess.run([sys.executable, "-c", "import delayed_scaling_amax_amd"],
+                         capture_output=True, text=True, cwd=str(tmp_path),
+                         env=dict(os.environ, PYTHONPATH=str(tmp_path)))
+    assert out.returncode != 0
+    assert "ImportError" in out.stderr and "libfp8q.so is not built" in out.stderr, out.stderr
