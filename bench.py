@@ -40,7 +40,14 @@ import numpy as np  # noqa: E402
 PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E, published
 PEAK_FP8_TFLOPS = 5000.0  # MI355X dense FP8 matrix throughput, published
 METRIC = "fused quantize+amax GB/s & % HBM peak; µs per batched scale update"
-ROOFLINE_KERNEL = "quantize_amax_kernel<1, false>"  # the multi-tensor quantize, bf16 sources
+# The multi-tensor quantize with bf16 sources; launches of at least 256 MiB of codes take
+# its instance with non-temporal stores.
+STREAM_CODE_BYTES = 256 << 20
+
+
+def roofline_kernel(w) -> str:
+    big = sum(int(t.data.size) for t in w.tensors) >= STREAM_CODE_BYTES
+    return "quantize_amax_kernel<1, false, %s>" % ("true" if big else "false")
 PROBE_LIB = os.path.join(ROOT, "delayed_scaling_amax_amd", "libfp8q_probe.so")
 OTHER_WORKLOADS = ("mlp_4096", "grad_8192x16384")
 
@@ -61,7 +68,7 @@ def traffic_file(workload: str) -> str:
     return os.path.join(ROOT, "profiles", "quantize_amax_%s_traffic.txt" % workload)
 
 
-def measured_traffic(workload: str):
+def measured_traffic(workload: str, kernel: str):
     """HBM bytes per quantize launch from the committed rocprofv3 counter summary, or
     None if absent, for another workload or kernel, or taken on a different kernel
     source."""
@@ -73,7 +80,7 @@ def measured_traffic(workload: str):
                     k, v = line.split("=", 1)
                     kv[k.strip()] = v.strip()
         if (kv.get("kernel_source_sha256_16") != kernel_hash() or kv.get("workload") != workload
-                or kv.get("kernel") != ROOFLINE_KERNEL):
+                or kv.get("kernel") != kernel):
             return None
         return float(kv["hbm_bytes_per_launch"])
     except (OSError, KeyError, ValueError):
@@ -361,8 +368,11 @@ def stream_ceiling(plib, dev, units, sets, reps, cus):
     """The quantize pass's traffic without its arithmetic (16 B read + 8 B written per 8
     bf16 elements), timed like the quantize kernel (events attached to each launch, `sets`
     rotating buffers): the fastest of a sweep of loads in flight per thread and blocks per
-    CU, with the quantize kernel's cache policies, and with default ones; plus read-only
-    and write-only rates of the same sizes (best of the same sweep)."""
+    CU, with each of the quantize kernel's two cache-policy sets (non-temporal loads with
+    device-scope stores, or with non-temporal device-scope stores: the kernel's choice
+    for launches whose codes exceed the Infinity Cache), and with default ones; plus
+    read-only and write-only rates of the same sizes (best of the same sweep).  rw_2to1
+    is the faster of the kernel's two sets."""
     import torch
     srcs = [torch.empty(units * 16, dtype=torch.uint8, device=dev) for _ in range(sets)]
     for s in srcs:
@@ -398,8 +408,12 @@ def stream_ceiling(plib, dev, units, sets, reps, cus):
                            "blocks_per_cu": bpc}
         return out
 
+    sc1, nt = best(0, 1), best(0, 2)
+    sc1["stores"], nt["stores"] = "sc1", "nt sc1"
     res = {"bytes_2to1": 24 * units, "rotating_sets": sets,
-           "rw_2to1": best(0, 1), "rw_2to1_default_policy": best(0, 0),
+           "rw_2to1": dict(nt if nt["gbps"] > sc1["gbps"] else sc1),
+           "rw_2to1_sc1_stores": sc1, "rw_2to1_nt_stores": nt,
+           "rw_2to1_default_policy": best(0, 0),
            "read_only": best(1, 1), "write_only": best(2, 1)}
     del srcs, dsts
     return res
@@ -694,9 +708,11 @@ def main():
         for label, elems, sets in (("0.5GB", 167772160, 3), ("4GB", 1358954496, 1)):
             ceilings[label] = stream_ceiling(plib, dev, elems // 8, sets, 10, cus)
             torch.cuda.empty_cache()
-            log("stream %s: 2:1 read:write %.1f GB/s (default policies %.1f), read-only "
-                "%.1f, write-only %.1f" % (
+            log("stream %s: 2:1 read:write %.1f GB/s (sc1 stores %.1f, nt stores %.1f, "
+                "default policies %.1f), read-only %.1f, write-only %.1f" % (
                     label, ceilings[label]["rw_2to1"]["gbps"],
+                    ceilings[label]["rw_2to1_sc1_stores"]["gbps"],
+                    ceilings[label]["rw_2to1_nt_stores"]["gbps"],
                     ceilings[label]["rw_2to1_default_policy"]["gbps"],
                     ceilings[label]["read_only"]["gbps"], ceilings[label]["write_only"]["gbps"]))
 
@@ -854,7 +870,7 @@ def main():
     copy_gbps = 2 * cbuf.numel() * 4 * 10 / (a.elapsed_time(b) * 1e-3) / 1e9
     del cbuf, cdst
 
-    traffic = measured_traffic(w.name)
+    traffic = measured_traffic(w.name, roofline_kernel(w))
     q_gbps = head["q_gbps"]
     upd_roof = None
     if graph_us:
@@ -904,7 +920,7 @@ def main():
         "layernorm_quantize": ln_out,
         "fp8_gemm": gemm_out,
         "copy_d2d_gbps": round(copy_gbps, 1),
-        "roofline": {"bound": "hbm", "kernel": ROOFLINE_KERNEL + " (fp8_multi_quantize_amax)",
+        "roofline": {"bound": "hbm", "kernel": roofline_kernel(w) + " (fp8_multi_quantize_amax)",
                      "achieved": round(q_gbps, 1), "peak": PEAK_HBM_GBPS,
                      "unit": "GB/s", "frac": round(q_gbps / PEAK_HBM_GBPS, 4),
                      "traffic": traffic},

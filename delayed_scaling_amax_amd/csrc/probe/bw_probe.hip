@@ -6,7 +6,8 @@
 //  * probe_stream: the quantize pass's traffic without its arithmetic.  Each 16-byte
 //    unit of the source (8 bf16) is read and 8 bytes are written (the high byte of each
 //    element), i.e. 2 bytes read per byte written, with the same cache policies as the
-//    quantize kernel (non-temporal loads, device-scope stores) or the default ones; also
+//    quantize kernel (non-temporal loads, device-scope stores, non-temporal as well for
+//    launches whose codes exceed the Infinity Cache) or the default ones; also
 //    read-only and write-only forms.  Plain persistent grid-stride loop: each thread
 //    issues U 16-byte loads, then U 8-byte stores, per iteration; the benchmark sweeps U
 //    and the blocks per CU and reports the fastest.
@@ -37,13 +38,14 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_
 }
 
 // kMode: 0 = read 16 B + write 8 B per unit, 1 = read only, 2 = write only.
-// kPolicy: 1 = non-temporal loads and device-scope (sc1) stores, 0 = default policies.
+// kPolicy: 1 = non-temporal loads and device-scope (sc1) stores, 2 = non-temporal loads
+// and non-temporal device-scope (nt | sc1) stores, 0 = default policies.
 template <int kMode, int kU, int kPolicy>
 __global__ __launch_bounds__(256) void stream_kernel(const uint4* __restrict__ src,
                                                      uint2* __restrict__ dst, int64_t units,
                                                      uint32_t* __restrict__ sink) {
   constexpr int kLd = kPolicy ? 2 : 0;
-  constexpr int kSt = kPolicy ? 16 : 0;
+  constexpr int kSt = kPolicy == 2 ? 18 : kPolicy ? 16 : 0;
   const int64_t step = (int64_t)gridDim.x * 256 * kU;
   uint32_t acc = 0;
   for (int64_t base = (int64_t)blockIdx.x * 256 * kU; base < units; base += step) {
@@ -191,9 +193,12 @@ int probe_stream(const void* src, void* dst, int64_t units, int mode, int u, int
       (mode != 1 && !dst) || (mode == 1 && !sink))
     return -1;
   const void* fn = nullptr;
-  if (mode == 0) fn = policy ? stream_fn_u<0, 1>(u) : stream_fn_u<0, 0>(u);
+  if (policy < 0 || policy > 2) return -1;
+  if (mode == 0)
+    fn = policy == 2 ? stream_fn_u<0, 2>(u) : policy ? stream_fn_u<0, 1>(u) : stream_fn_u<0, 0>(u);
   if (mode == 1) fn = policy ? stream_fn_u<1, 1>(u) : stream_fn_u<1, 0>(u);
-  if (mode == 2) fn = policy ? stream_fn_u<2, 1>(u) : stream_fn_u<2, 0>(u);
+  if (mode == 2)
+    fn = policy == 2 ? stream_fn_u<2, 2>(u) : policy ? stream_fn_u<2, 1>(u) : stream_fn_u<2, 0>(u);
   if (fn == nullptr) return -1;
   void* args[] = {(void*)&src, &dst, &units, &sink};
   const hipError_t e =

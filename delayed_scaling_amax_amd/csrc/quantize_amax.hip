@@ -63,6 +63,19 @@ namespace fp8q {
 #ifndef FP8Q_Q_ST_AUX
 #define FP8Q_Q_ST_AUX 16
 #endif
+// Launches whose codes are larger than the 256 MB Infinity Cache in front of HBM store
+// them non-temporally as well (nt | sc1): they could not stay in the cache for the
+// consumer, and on the 4.08 GB hidden-12288 step (1.36 GB of codes) this is 1.4-2 %
+// faster (685 against 695-699 us, interleaved in one process).  Smaller launches keep
+// sc1 stores, which leave the codes in the cache for the GEMM that reads them next (on
+// a 0.5 GB step quantized repeatedly, nt stores were 8 % slower: 83.6 against 76.9 us).
+#ifndef FP8Q_Q_ST_STREAM_AUX
+#define FP8Q_Q_ST_STREAM_AUX 18
+#endif
+#ifndef FP8Q_Q_STREAM_BYTES
+#define FP8Q_Q_STREAM_BYTES (256LL << 20)
+#endif
+constexpr int64_t kQStreamBytes = FP8Q_Q_STREAM_BYTES;
 constexpr int kQBlock = FP8Q_Q_BLOCK;             // threads per block
 constexpr int kQUnroll = FP8Q_Q_UNROLL;           // 8-element groups per thread per chunk
 constexpr int kQMaxEntries = 32;                  // tensors per launch (kernel-argument table)
@@ -154,15 +167,16 @@ __device__ __forceinline__ uint4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_
   return make_uint4(v[0], v[1], v[2], v[3]);
 }
 
+template <int kAux = FP8Q_Q_ST_AUX>
 __device__ __forceinline__ void buffer_store8(__amdgpu_buffer_rsrc_t r, uint32_t voff,
                                               uint32_t soff, uint2 o) {
-  __builtin_amdgcn_raw_buffer_store_b64(u32x2{o.x, o.y}, r, voff, soff, FP8Q_Q_ST_AUX);
+  __builtin_amdgcn_raw_buffer_store_b64(u32x2{o.x, o.y}, r, voff, soff, kAux);
 }
 
+template <int kAux = FP8Q_Q_ST_AUX>
 __device__ __forceinline__ void buffer_store16(__amdgpu_buffer_rsrc_t r, uint32_t voff,
                                                uint32_t soff, uint2 a, uint2 b) {
-  __builtin_amdgcn_raw_buffer_store_b128(u32x4{a.x, a.y, b.x, b.y}, r, voff, soff,
-                                         FP8Q_Q_ST_AUX);
+  __builtin_amdgcn_raw_buffer_store_b128(u32x4{a.x, a.y, b.x, b.y}, r, voff, soff, kAux);
 }
 
 __device__ __forceinline__ uint4 load16(const uint4* p) {
@@ -542,7 +556,7 @@ __device__ __forceinline__ void elementwise_units(const void* __restrict__ src,
 // speculatively (assuming that tensor's scale is in the window) before the per-tensor
 // constants are set up, so the block's first HBM requests do not wait for the scale
 // loads, the reciprocals and the barrier.
-template <bool kBF16, int kFmt, bool kGelu, class Tab, class Sh>
+template <bool kBF16, int kFmt, bool kGelu, int kStAux, class Tab, class Sh>
 __device__ __forceinline__ void run_full_chunks(const Tab& tab, Sh& sh, int t_begin,
                                                 int t_end, bool setup) {
   constexpr int kD = Tab::kPlanned ? kQPlanDepth : kQDepth;  // passes in flight ahead
@@ -652,9 +666,9 @@ __device__ __forceinline__ void run_full_chunks(const Tab& tab, Sh& sh, int t_be
 #pragma unroll
     for (int q = 0; q < kS; ++q) {
       if constexpr (kQPair)
-        buffer_store16(rnull, tid * 16, q * kQBlock * 16, make_uint2(0, 0), make_uint2(0, 0));
+        buffer_store16<kStAux>(rnull, tid * 16, q * kQBlock * 16, make_uint2(0, 0), make_uint2(0, 0));
       else
-        buffer_store8(rnull, tid * 8, q * kQBlock * 8, make_uint2(0, 0));
+        buffer_store8<kStAux>(rnull, tid * 8, q * kQBlock * 8, make_uint2(0, 0));
     }
   };
   Pass buf[kR];
@@ -800,10 +814,10 @@ __device__ __forceinline__ void run_full_chunks(const Tab& tab, Sh& sh, int t_be
         static_assert(kU % 2 == 0, "units pair up within a pass");
 #pragma unroll
         for (int q = 0; q < kU / 2; ++q)
-          buffer_store16(rout, tid * 16, q * kQBlock * 16, o[2 * q], o[2 * q + 1]);
+          buffer_store16<kStAux>(rout, tid * 16, q * kQBlock * 16, o[2 * q], o[2 * q + 1]);
       } else {
 #pragma unroll
-        for (int u = 0; u < kU; ++u) buffer_store8(rout, tid * 8, u * kQBlock * 8, o[u]);
+        for (int u = 0; u < kU; ++u) buffer_store8<kStAux>(rout, tid * 8, u * kQBlock * 8, o[u]);
       }
       const Slot& nx = pos[(k + 1) % kR];
       more = nx.t < t_end;  // uniform
@@ -892,13 +906,13 @@ struct KindTraits {
 };
 
 // Phase 1 for the run of kind kKind, if the instance handles that kind.
-template <int kSrc, int kKind, class Tab, class Sh>
+template <int kSrc, int kKind, int kStAux, class Tab, class Sh>
 __device__ __forceinline__ void phase1_run(const Tab& tab, Sh& sh, int& tb, bool& ready) {
   using T = KindTraits<kKind>;
   const int te = tab.run_end[kKind];
   if constexpr ((kSrc & T::kSrcBit) != 0) {
     if (te > tb) {
-      run_full_chunks<T::kBF16, T::kFmt, T::kGelu>(tab, sh, tb, te, !ready);
+      run_full_chunks<T::kBF16, T::kFmt, T::kGelu, kStAux>(tab, sh, tb, te, !ready);
       ready = true;
     }
   }
@@ -1034,7 +1048,7 @@ __device__ void finish_in_block(const QUpdate& u) {
 }
 
 // Phases 1 and 2 of a launch and the block's amax atomics.
-template <int kSrc, class Tab, class Sh>
+template <int kSrc, int kStAux, class Tab, class Sh>
 __device__ __forceinline__ void quantize_body(const Tab& tab, Sh& sh) {
   const int n = tab.n;
   const int tid = threadIdx.x;
@@ -1042,12 +1056,12 @@ __device__ __forceinline__ void quantize_body(const Tab& tab, Sh& sh) {
   // phase 1, one run of same-kind tensors at a time; the first run also sets up sh
   bool ready = false;
   int tb = 0;
-  phase1_run<kSrc, 0>(tab, sh, tb, ready);
-  phase1_run<kSrc, 1>(tab, sh, tb, ready);
-  phase1_run<kSrc, 2>(tab, sh, tb, ready);
-  phase1_run<kSrc, 3>(tab, sh, tb, ready);
-  phase1_run<kSrc, 4>(tab, sh, tb, ready);
-  phase1_run<kSrc, 5>(tab, sh, tb, ready);
+  phase1_run<kSrc, 0, kStAux>(tab, sh, tb, ready);
+  phase1_run<kSrc, 1, kStAux>(tab, sh, tb, ready);
+  phase1_run<kSrc, 2, kStAux>(tab, sh, tb, ready);
+  phase1_run<kSrc, 3, kStAux>(tab, sh, tb, ready);
+  phase1_run<kSrc, 4, kStAux>(tab, sh, tb, ready);
+  phase1_run<kSrc, 5, kStAux>(tab, sh, tb, ready);
   if (!ready) setup_shared(tab, sh);
   // phase 2
   if constexpr (Tab::kPlanned) {
@@ -1069,11 +1083,11 @@ __device__ __forceinline__ void quantize_body(const Tab& tab, Sh& sh) {
   }
 }
 
-template <int kSrc, bool kUpd>
+template <int kSrc, bool kUpd, bool kStream = false>
 __global__ __launch_bounds__(kQBlock) void quantize_amax_kernel(const QTable tab) {
   __shared__ QShared sh;
   if constexpr (kSrc == 4 && kQGeluTable) gelu_table_to_lds();
-  quantize_body<kSrc>(tab, sh);
+  quantize_body<kSrc, kStream ? FP8Q_Q_ST_STREAM_AUX : FP8Q_Q_ST_AUX>(tab, sh);
   if constexpr (kUpd) {
     __shared__ uint32_t colmax[kQUpdMaxCols];
     // every block counts once, the one that rolls the history (the first) twice
@@ -1090,7 +1104,7 @@ __global__ __launch_bounds__(kQBlock) void quantize_amax_kernel(const QTable tab
 template <int kSrc>
 __global__ __launch_bounds__(kQBlock) void quantize_amax_planned_kernel(const QPlanTable tab) {
   __shared__ QSharedT<kQPlanMaxEntries> sh;
-  quantize_body<kSrc>(tab, sh);
+  quantize_body<kSrc, FP8Q_Q_ST_AUX>(tab, sh);
 }
 
 // ---------------------------------------------------------------- host side
@@ -1167,17 +1181,29 @@ static int launch_table(QTable* tab, bool upd, hipStream_t stream, hipEvent_t st
   for (int i = 0; i < tab->n; ++i)
     src_kinds |= tab->e[i].gelu ? 4 : tab->e[i].dtype == FP8Q_BF16 ? 1 : 2;
   // tables hold either plain entries (any mix of bf16 and fp32) or gelu entries only
+  // codes beyond the Infinity Cache's size are stored non-temporally (plain entries)
+  const bool nt = src_kinds != 4 && units * 8 >= kQStreamBytes;
   const void* fn = nullptr;
-  if (!upd)
+  if (!upd && !nt)
     fn = src_kinds == 1   ? (const void*)quantize_amax_kernel<1, false>
          : src_kinds == 2 ? (const void*)quantize_amax_kernel<2, false>
          : src_kinds == 3 ? (const void*)quantize_amax_kernel<3, false>
          : src_kinds == 4 ? (const void*)quantize_amax_kernel<4, false>
                           : nullptr;
-  else
+  else if (!upd)
+    fn = src_kinds == 1   ? (const void*)quantize_amax_kernel<1, false, true>
+         : src_kinds == 2 ? (const void*)quantize_amax_kernel<2, false, true>
+         : src_kinds == 3 ? (const void*)quantize_amax_kernel<3, false, true>
+                          : nullptr;
+  else if (!nt)
     fn = src_kinds == 1   ? (const void*)quantize_amax_kernel<1, true>
          : src_kinds == 2 ? (const void*)quantize_amax_kernel<2, true>
          : src_kinds == 3 ? (const void*)quantize_amax_kernel<3, true>
+                          : nullptr;
+  else
+    fn = src_kinds == 1   ? (const void*)quantize_amax_kernel<1, true, true>
+         : src_kinds == 2 ? (const void*)quantize_amax_kernel<2, true, true>
+         : src_kinds == 3 ? (const void*)quantize_amax_kernel<3, true, true>
                           : nullptr;
   if (fn == nullptr) return FP8Q_EINVAL;
   // the gelu instance reads its table from dynamic LDS
@@ -1190,10 +1216,10 @@ static int launch_table(QTable* tab, bool upd, hipStream_t stream, hipEvent_t st
   // The grid-stride schedule needs every block resident at once: cap the blocks per
   // CU at what the instance's register and LDS use allow.  Per device: the dynamic-LDS
   // attribute is set on each device the instance runs on.
-  static std::atomic<int> fit[64][16];
+  static std::atomic<int> fit[64][32];
   const int dev = current_device_index();
   if (dev < 0) return FP8Q_EHIP;
-  const int inst = src_kinds + (upd ? 8 : 0);
+  const int inst = src_kinds + (upd ? 8 : 0) + (nt ? 16 : 0);
   int per_cu = fit[dev][inst].load(std::memory_order_relaxed);
   if (per_cu <= 0) {
     if (table && hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize,
