@@ -78,3 +78,34 @@ def test_f32_past_4_gib(orc):
     got = dst.cpu().numpy()
     del dst, dbuf
     _compare(orc, x, E5M2, float(np.float32(0.37)), got, amax.cpu().numpy()[0])
+
+
+@pytest.mark.parametrize("numel", [(1 << 28) - 8, 1 << 28])
+def test_store_policy_threshold(orc, numel):
+    """Launches of at least 256 MiB of codes take the instance with non-temporal stores,
+    smaller ones the default instance: both sides of the threshold, one bf16 tensor
+    with a ragged view (offset 1) in the multi-tensor launch and through a plan, every
+    code byte and the amax against the oracle."""
+    import delayed_scaling_amax_amd as d
+    x = _big(workloads.random_bf16(1 << 20, 52, -6, 6, specials=True), numel)
+    note("large: store-policy threshold, %d elements" % numel)
+    buf = torch.empty(numel + 1, dtype=torch.bfloat16, device="cuda")
+    src = buf[1:]
+    src.copy_(dev_src(x))
+    dst = torch.empty(numel, dtype=torch.uint8, device="cuda")
+    scale = f32([0.05])
+    amax = torch.zeros(1, dtype=torch.float32, device="cuda")
+    d.fp8_multi_quantize_amax([(src, dst, scale, amax, E5M2)])
+    torch.cuda.synchronize()
+    got, got_amax = dst.cpu().numpy(), amax.cpu().numpy()[0]
+    want, wa = orc.quantize_amax(x, E5M2, float(np.float32(0.05)),
+                                 threads=workloads.default_threads())
+    assert np.array_equal(got, want)
+    assert bits(got_amax) == bits(wa)
+    note("large: store-policy threshold, %d elements, planned" % numel)
+    dst.fill_(0xAA)
+    amax.zero_()
+    d.fp8_multi_quantize_amax_planned(d.fp8_multi_quantize_plan([(src, dst, scale, amax, E5M2)]))
+    torch.cuda.synchronize()
+    assert np.array_equal(dst.cpu().numpy(), want)
+    assert bits(amax.cpu().numpy()[0]) == bits(wa)
